@@ -1,0 +1,317 @@
+/*
+ * decode_oracle.c -- plain, slow fp64 CPU reference for single-query (decode)
+ * attention over a KV cache.  TEST INFRASTRUCTURE ONLY: nothing on the product
+ * path may link or call this file; only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header or table with
+ * the HIP library.
+ *
+ * What it computes (per query row = (batch b, token t, query head h)):
+ *
+ *   out[d] = sum_j softmax_j( scale * <q, k_j> ) * v_j[d]      (visible keys j)
+ *
+ * as stated in the description of "mha_decoding_single_batch_pipelined"
+ * (FA2 decode: the decoding, single-query case of attention, Args `scale`
+ * "applied to Q.K^T") and in "mha_sm100_dispatch", Args `scale` (applied to the
+ * Q@K' product before softmax).  It is written out directly, two passes over
+ * the keys (max, then exp-sum and weighted sum), no online rescaling, no
+ * blocking, everything accumulated in double.
+ *
+ * Readings taken where the pages leave a step open (each also listed in the
+ * design notes):
+ *   - KV head of query head h is floor(h / group): `group` is the number of
+ *     query heads per KV head ("mha_sm100_dispatch", Parameters `group`).
+ *   - Keys visible to row (b, t): N_b = valid_length[b] if given, else
+ *     max_seq_len ("mha_sm100_dispatch", Args `valid_length`,
+ *     `max_cache_valid_length_arg`).  N_b counts the current tokens too.  With
+ *     the causal mask, token t of T sees keys j <= N_b - T + t (bottom-right
+ *     aligned; the MTP tokens are the last T positions).
+ *   - MLA ("flare_mla_decoding_dispatch", Args `k`): V is K[..., :depth_v];
+ *     the caller passes v == NULL for that case.
+ *   - Sink ("flare_mla_decoding_dispatch", Args `attn_sink_ptr`;
+ *     "mha_sm100_dispatch", Args `sink_weights`): one fp32 logit sigma_h per
+ *     query head that joins the softmax denominator only (a virtual key with
+ *     score sigma_h and a zero value row), not multiplied by `scale`.
+ *   - LSE = m + ln(l) of the full denominator, sink included.
+ *   - A row with no visible key and no sink: out = 0, LSE = -inf.
+ *   - Split-K ("mha_decoding_single_batch_pipelined", description: each block
+ *     takes a contiguous slice of the key dimension and records its exp-sum and
+ *     running max for a later "mha_splitk_reduce" pass): partition p covers
+ *     keys [p*C, (p+1)*C); its partial output is normalised by its own exp-sum;
+ *     the merge is by log-sum-exp.
+ *
+ * Element types: 0 = float32, 1 = bfloat16 given as its raw 16-bit pattern.
+ * bf16 -> double is exact (the 16 bits are the top half of a float32).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+static double elem(const void* base, size_t idx, int dtype) {
+  if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* Problem description shared by the entry points below. */
+typedef struct {
+  const void* q;              /* [B, T, H, D]                                   */
+  const void* k;              /* contiguous [B, S, KVH, D] or pool [pages, ps, KVH, D] */
+  const void* v;              /* same layout with Dv, or NULL => V = K[..., :Dv] */
+  int dtype;
+  const uint32_t* page_table; /* [B, max_pages] or NULL (contiguous)            */
+  int page_size, max_pages;
+  const uint32_t* valid_length; /* [B] or NULL                                  */
+  int B, T, H, KVH, D, Dv, S;
+  double scale;
+  const float* sink;          /* [H] or NULL                                    */
+  int causal;
+} problem_t;
+
+/* Flat element index of depth element d of key j (of sequence b, KV head g)
+ * in a cache whose rows hold `width` elements. */
+static size_t kv_index(const problem_t* p, int b, int j, int g, int d, int width) {
+  size_t row;
+  if (p->page_table) {
+    uint32_t phys = p->page_table[(size_t)b * p->max_pages + (size_t)(j / p->page_size)];
+    row = (size_t)phys * p->page_size + (size_t)(j % p->page_size);
+  } else {
+    row = (size_t)b * p->S + (size_t)j;
+  }
+  return (row * p->KVH + (size_t)g) * (size_t)width + (size_t)d;
+}
+
+static double key_elem(const problem_t* p, int b, int j, int g, int d) {
+  return elem(p->k, kv_index(p, b, j, g, d, p->D), p->dtype);
+}
+
+static double value_elem(const problem_t* p, int b, int j, int g, int d) {
+  if (p->v == NULL) return elem(p->k, kv_index(p, b, j, g, d, p->D), p->dtype);
+  return elem(p->v, kv_index(p, b, j, g, d, p->Dv), p->dtype);
+}
+
+/* Number of keys visible to row (b, t). */
+static int visible_keys(const problem_t* p, int b, int t) {
+  int n = p->valid_length ? (int)p->valid_length[b] : p->S;
+  if (p->causal) {
+    int lim = n - p->T + t + 1;
+    if (lim < n) n = lim;
+  }
+  return n < 0 ? 0 : n;
+}
+
+/* Scores s_j = scale * <q_row, k_j> for keys j in [lo, hi). */
+static void scores(const problem_t* p, int b, int t, int h, int lo, int hi, double* s) {
+  int g = h / (p->H / p->KVH);
+  size_t qbase = (((size_t)b * p->T + t) * p->H + h) * (size_t)p->D;
+  for (int j = lo; j < hi; ++j) {
+    double dot = 0.0;
+    for (int d = 0; d < p->D; ++d)
+      dot += elem(p->q, qbase + d, p->dtype) * key_elem(p, b, j, g, d);
+    s[j - lo] = p->scale * dot;
+  }
+}
+
+/* Softmax-weighted sum over keys [lo, hi) of row (b, t, h).
+ * with_sink: include the row's sink logit in max and denominator.
+ * Returns through out[Dv] the normalised output, *m the max, *l the exp-sum
+ * (l = 0 and m = -inf when nothing contributes). */
+static void attend(const problem_t* p, int b, int t, int h, int lo, int hi, int with_sink,
+                   double* s, double* out, double* m_out, double* l_out) {
+  int g = h / (p->H / p->KVH);
+  int n = hi > lo ? hi - lo : 0;
+  if (n > 0) scores(p, b, t, h, lo, hi, s);
+
+  double m = -INFINITY;
+  for (int j = 0; j < n; ++j)
+    if (s[j] > m) m = s[j];
+  double sigma = (with_sink && p->sink) ? (double)p->sink[h] : -INFINITY;
+  if (sigma > m) m = sigma;
+
+  for (int d = 0; d < p->Dv; ++d) out[d] = 0.0;
+  if (m == -INFINITY) { /* no key and no sink */
+    *m_out = -INFINITY;
+    *l_out = 0.0;
+    return;
+  }
+  double l = 0.0;
+  for (int j = 0; j < n; ++j) {
+    double w = exp(s[j] - m);
+    l += w;
+    for (int d = 0; d < p->Dv; ++d) out[d] += w * value_elem(p, b, lo + j, g, d);
+  }
+  if (sigma != -INFINITY) l += exp(sigma - m);
+  for (int d = 0; d < p->Dv; ++d) out[d] /= l;
+  *m_out = m;
+  *l_out = l;
+}
+
+static problem_t make_problem(const void* q, const void* k, const void* v, int dtype,
+                              const uint32_t* page_table, int page_size, int max_pages,
+                              const uint32_t* valid_length, int B, int T, int H, int KVH,
+                              int D, int Dv, int S, float scale, const float* sink, int causal) {
+  problem_t p;
+  p.q = q; p.k = k; p.v = v; p.dtype = dtype;
+  p.page_table = page_table; p.page_size = page_size; p.max_pages = max_pages;
+  p.valid_length = valid_length;
+  p.B = B; p.T = T; p.H = H; p.KVH = KVH; p.D = D; p.Dv = Dv; p.S = S;
+  p.scale = (double)scale; p.sink = sink; p.causal = causal;
+  return p;
+}
+
+static int check_problem(const problem_t* p) {
+  if (p->B < 0 || p->T < 1 || p->H < 1 || p->KVH < 1 || p->D < 1 || p->Dv < 1 || p->S < 0)
+    return -1;
+  if (p->H % p->KVH != 0) return -1;
+  if (p->v == NULL && p->Dv > p->D) return -1;
+  if (p->page_table && (p->page_size < 1 || p->max_pages < 1)) return -1;
+  return 0;
+}
+
+static int longest_cache(const problem_t* p) {
+  int s = p->S;
+  if (p->valid_length)
+    for (int b = 0; b < p->B; ++b)
+      if ((int)p->valid_length[b] > s) s = (int)p->valid_length[b];
+  return s;
+}
+
+/*
+ * Full attention for the listed rows (row id = (b*T + t)*H + h), or for all
+ * B*T*H rows when rows == NULL.  out: [num_rows, Dv]; lse: [num_rows].
+ */
+int oracle_decode_attention(const void* q, const void* k, const void* v, int dtype,
+                            const uint32_t* page_table, int page_size, int max_pages,
+                            const uint32_t* valid_length, int B, int T, int H, int KVH, int D,
+                            int Dv, int S, float scale, const float* sink, int causal,
+                            const int64_t* rows, int64_t num_rows, double* out, double* lse,
+                            int num_threads) {
+  problem_t p = make_problem(q, k, v, dtype, page_table, page_size, max_pages, valid_length,
+                             B, T, H, KVH, D, Dv, S, scale, sink, causal);
+  if (check_problem(&p)) return -1;
+  int64_t n_rows = rows ? num_rows : (int64_t)B * T * H;
+  int smax = longest_cache(&p);
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#endif
+  int err = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(smax > 0 ? smax : 1));
+    if (!s) {
+#pragma omp atomic write
+      err = -2;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_rows; ++i) {
+      if (!s) continue;
+      int64_t r = rows ? rows[i] : i;
+      int h = (int)(r % H);
+      int t = (int)((r / H) % T);
+      int b = (int)(r / ((int64_t)H * T));
+      double m, l;
+      attend(&p, b, t, h, 0, visible_keys(&p, b, t), 1, s, out + (size_t)i * Dv, &m, &l);
+      lse[i] = (l > 0.0) ? m + log(l) : -INFINITY;
+    }
+    free(s);
+  }
+  return err;
+}
+
+/*
+ * Split-K partials: partition part covers keys [part*C, (part+1)*C) of each
+ * row's visible keys.  No sink here (it joins the merge once).
+ * part_o: [P, B*T*H, Dv] (normalised by its own exp-sum, zero if empty);
+ * part_m: [P, B*T*H] natural-log max (-inf if empty); part_l: exp-sum (0 if empty).
+ */
+int oracle_decode_partials(const void* q, const void* k, const void* v, int dtype,
+                           const uint32_t* page_table, int page_size, int max_pages,
+                           const uint32_t* valid_length, int B, int T, int H, int KVH, int D,
+                           int Dv, int S, float scale, int causal, int num_partitions,
+                           int keys_per_partition, double* part_o, double* part_m,
+                           double* part_l, int num_threads) {
+  problem_t p = make_problem(q, k, v, dtype, page_table, page_size, max_pages, valid_length,
+                             B, T, H, KVH, D, Dv, S, scale, NULL, causal);
+  if (check_problem(&p) || num_partitions < 1 || keys_per_partition < 1) return -1;
+  int64_t n_rows = (int64_t)B * T * H;
+  int64_t n_items = n_rows * num_partitions;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#endif
+  int err = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)keys_per_partition);
+    if (!s) {
+#pragma omp atomic write
+      err = -2;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_items; ++i) {
+      if (!s) continue;
+      int part = (int)(i / n_rows);
+      int64_t r = i % n_rows;
+      int h = (int)(r % H);
+      int t = (int)((r / H) % T);
+      int b = (int)(r / ((int64_t)H * T));
+      int n = visible_keys(&p, b, t);
+      int64_t lo64 = (int64_t)part * keys_per_partition;
+      int lo = lo64 < n ? (int)lo64 : n;
+      int hi = lo64 + keys_per_partition < n ? (int)(lo64 + keys_per_partition) : n;
+      attend(&p, b, t, h, lo, hi, 0, s, part_o + (size_t)i * Dv, &part_m[i], &part_l[i]);
+    }
+    free(s);
+  }
+  return err;
+}
+
+/*
+ * Log-sum-exp merge of split-K partials (the "mha_splitk_reduce" pass).
+ * Row r uses sink[r % H] when sink != NULL.  out: [rows, Dv]; lse: [rows].
+ */
+int oracle_splitk_merge(const double* part_o, const double* part_m, const double* part_l,
+                        int num_partitions, int64_t rows, int H, int Dv, const float* sink,
+                        double* out, double* lse) {
+  if (num_partitions < 1 || rows < 0 || H < 1 || Dv < 1) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    double sigma = sink ? (double)sink[r % H] : -INFINITY;
+    double M = sigma;
+    for (int p = 0; p < num_partitions; ++p) {
+      size_t i = (size_t)p * rows + r;
+      if (part_l[i] > 0.0 && part_m[i] > M) M = part_m[i];
+    }
+    double* o = out + (size_t)r * Dv;
+    for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+    if (M == -INFINITY) {
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double L = (sigma != -INFINITY) ? exp(sigma - M) : 0.0;
+    for (int p = 0; p < num_partitions; ++p) {
+      size_t i = (size_t)p * rows + r;
+      if (!(part_l[i] > 0.0)) continue;
+      double w = part_l[i] * exp(part_m[i] - M);
+      L += w;
+      for (int d = 0; d < Dv; ++d) o[d] += w * part_o[i * Dv + d];
+    }
+    for (int d = 0; d < Dv; ++d) o[d] /= L;
+    lse[r] = M + log(L);
+  }
+  return 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is one full decode-attention pass (every kernel of the call: the
+partition pass and, when the keys are split, the log-sum-exp merge) over one
+batch of synthetic inputs already resident in HBM.  The default workload is the
+GQA decode problem (batch 32, 32 query / 8 KV heads, depth 128, 4096 keys per
+sequence, bf16).  Prints one JSON line.
+
+  value      = algorithmic KV bytes per step / time per step  (GB/s)
+  roofline   = the partition-pass kernel alone: the same bytes / its average
+               HIP-event duration, against the 8 TB/s HBM peak
+  cpu_baseline = the fp64 CPU oracle on this host, on a bounded sample
+
+Input sets are rotated so that consecutive steps never find their KV cache in
+the 256 MB last-level cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "decode-attention μs/step + achieved KV-read HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 2 << 30  # >= 8x the last-level cache
+
+WORKLOADS = {"tiny": W.TINY_MHA, "gqa": W.GQA, "paged": W.PAGED, "mla": W.MLA,
+             "mla_mtp": W.MLA_MTP, "long": W.LONG}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gqa")
+    ap.add_argument("--partitions", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="rough budget of the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def sample_inputs(inp: W.Inputs, nb: int) -> W.Inputs:
+    """The first nb sequences of an instance (same cache pool when paged)."""
+    wl = inp.wl.with_(batch=nb)
+    k = inp.k if inp.page_table is not None else inp.k[:nb]
+    v = None if inp.v is None else (inp.v if inp.page_table is not None else inp.v[:nb])
+    return W.Inputs(wl, inp.q[:nb], k, v,
+                    None if inp.valid_length is None else inp.valid_length[:nb],
+                    None if inp.page_table is None else inp.page_table[:nb], inp.sink)
+
+
+def cpu_baseline(inp: W.Inputs, budget_s: float):
+    """Time the oracle as it stands on a bounded sample of the workload."""
+    from oracle import oracle as O
+    wl = inp.wl
+    threads = O.num_threads()
+    # Size the sample from one short probe run on one sequence.
+    probe = sample_inputs(inp, 1)
+    t0 = time.perf_counter()
+    O.attention(probe.q, probe.k, probe.v, scale=wl.softmax_scale, page_table=probe.page_table,
+                valid_length=probe.valid_length, sink=probe.sink, causal=wl.causal,
+                depth_v=wl.dv, max_seq_len=wl.max_seq_len)
+    per_seq = max(time.perf_counter() - t0, 1e-4)
+    nb = int(max(1, min(wl.batch, budget_s / 3 / per_seq)))
+    smp = sample_inputs(inp, nb)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (len(times) < 5 and time.perf_counter() - t_start < budget_s / 2):
+        t0 = time.perf_counter()
+        O.attention(smp.q, smp.k, smp.v, scale=wl.softmax_scale, page_table=smp.page_table,
+                    valid_length=smp.valid_length, sink=smp.sink, causal=wl.causal,
+                    depth_v=wl.dv, max_seq_len=wl.max_seq_len)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    gbs = smp.kv_bytes() / t / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {nb} of {wl.batch} sequences (all heads, all keys), median of "
+                      f"{len(times)} runs of {t * 1e3:.1f} ms; full-step equivalent "
+                      f"{t * inp.kv_bytes() / smp.kv_bytes() * 1e6:.0f} us",
+            "us_per_step_equiv": round(t * inp.kv_bytes() / smp.kv_bytes() * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from decode_attention_07_amd import binding as DA
+
+    wl = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    log(f"workload {wl.name}")
+    first = W.make_inputs(wl)
+    footprint = first.kv_bytes()
+    R = args.rotate or max(1, min(4, math.ceil(ROTATE_BYTES / max(footprint, 1))))
+    if wl.ragged is not None:
+        R = 1  # ragged draws differ per set; keep the one instance whose bytes we report
+    host_sets = [first] + [W.make_inputs(wl, variant=r) for r in range(1, R)]
+    log(f"{R} input set(s) of {footprint / 2**20:.1f} MiB KV each")
+    dev_sets = []
+    for inp in host_sets:
+        dev_sets.append(dict(q=DA.to_device(inp.q), k=DA.to_device(inp.k),
+                             v=DA.to_device(inp.v), table=DA.to_device(inp.page_table),
+                             valid=DA.to_device(inp.valid_length), sink=DA.to_device(inp.sink)))
+    kv_bytes = footprint
+    S = wl.max_seq_len
+    B, T, H = wl.batch, wl.q_len, wl.num_heads
+    P = args.partitions or DA.num_partitions(B, T, H, wl.kv_heads, wl.depth, wl.dv, S)
+    split = P > 1
+    ws = torch.empty(DA.decode_workspace_size(P, B, T, H, wl.dv), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((B, T, H, wl.dv), dtype=dev_sets[0]["q"].dtype, device="cuda")
+    lse = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+    po, pm, ps = DA.workspace_views(ws, P, B, T, H, wl.dv)
+
+    def partition_pass(d):
+        if wl.mla:
+            DA.mla_decode_partials(d["q"], d["k"], scale=wl.softmax_scale, num_partitions=P,
+                                   page_table=d["table"], valid_length=d["valid"],
+                                   max_seq_len=S, causal=wl.causal, workspace=ws)
+        else:
+            DA.decode_attention_partials(d["q"], d["k"], d["v"], group=wl.group,
+                                         scale=wl.softmax_scale, num_partitions=P,
+                                         page_table=d["table"], valid_length=d["valid"],
+                                         max_seq_len=S, causal=wl.causal, workspace=ws)
+
+    def reduce_pass(d):
+        DA.splitk_reduce(po, pm, ps, num_q_heads=H, sink_weights=d["sink"], out=out.view(-1, wl.dv),
+                         lse=lse.view(-1))
+
+    def full_call(d):
+        kw = dict(scale=wl.softmax_scale, page_table=d["table"], valid_length=d["valid"],
+                  max_seq_len=S, num_partitions=P, sink_weights=d["sink"], causal=wl.causal,
+                  out=out, lse=lse, workspace=ws)
+        if wl.mla:
+            DA.mla_decode(d["q"], d["k"], **kw)
+        else:
+            DA.decode_attention(d["q"], d["k"], d["v"], group=wl.group, **kw)
+
+    def step(i, ev_a=None, ev_b=None):
+        d = dev_sets[i % R]
+        if ev_a is not None:
+            ev_a.record()
+        if split:
+            partition_pass(d)
+            if ev_b is not None:
+                ev_b.record()
+            reduce_pass(d)
+        else:
+            full_call(d)
+            if ev_b is not None:
+                ev_b.record()
+
+    log(f"P={P} split={split}; warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, *evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (kern_avg_ms * 1e-3) / 1e9
+    log(f"{ms_per_step * 1e3:.1f} us/step, kernel {kern_avg_ms * 1e3:.1f} us")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1), shapes of the problem statement)",
+        "config": {"workload": wl.name, "batch": B, "q_len": T, "num_q_heads": H,
+                   "num_kv_heads": wl.kv_heads, "depth": wl.depth, "depth_v": wl.dv,
+                   "max_seq_len": S, "page_size": wl.page_size, "partitions": P,
+                   "kv_bytes_per_step": kv_bytes, "input_sets": R},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "partition pass" if split else "decode (single partition)",
+                     "kernel_avg_us": round(kern_avg_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(first, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,401 @@
+// api.cpp -- the C ABI (include/decode_attention.h): argument checks, the
+// partition-count heuristic, workspace layout and kernel dispatch.
+//
+// Host dispatch follows the role of "mha_sm100_dispatch" / "flare_mla_decoding_dispatch"
+// (descriptions): choose the kernel configuration and the split count, thread
+// the optional valid-length / page-table / sink arguments through, enqueue on
+// the caller's stream.  Nothing here reads device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+#include "../../include/decode_attention.h"
+#include "da_params.h"
+
+namespace da {
+hipError_t launch_decode_valu(const DecodeParams& p, bool bf16, hipStream_t s);
+int valu_step_keys(int rows_per_block);
+int valu_rows_per_block(int fold);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s);
+int mfma_step_keys();
+int mfma_rows_per_block();
+hipError_t launch_mla(const DecodeParams& p, hipStream_t s);
+int mla_step_keys(int q_len);
+int mla_rows_per_block(int q_len, int num_q_heads);
+bool splitk_reduce_supported(int depth_v, int P);
+hipError_t launch_splitk_reduce(const float* po, const float* pm, const float* pl, int P,
+                                int rows, int H, int depth_v, const float* sink, void* out,
+                                bool bf16, float* lse, hipStream_t s);
+}  // namespace da
+
+namespace {
+
+constexpr int kMlaDepth = 576;
+constexpr int kMlaDepthV = 512;
+constexpr size_t kAlign = 256;
+constexpr bool kMfmaReady = false;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("DECODE_ATTN_LOG");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
+// Compute-unit count of the current device, cached per device.
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    cache[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+                     ? prop.multiProcessorCount
+                     : 256;
+  }
+  return cache[dev];
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+// Which partition kernel runs, and its tiling.
+enum Variant { kValu = 0, kMfma = 1, kMla = 2 };
+
+struct Plan {
+  Variant variant;
+  int rows_per_block;
+  int row_blocks;
+  int step;  // keys per block iteration; partitions are multiples of it
+};
+
+Plan plan_mha(int q_len, int group, bool bf16) {
+  const int fold = q_len * group;
+  Plan pl;
+  if (kMfmaReady && bf16 && fold >= 8) {
+    pl.variant = kMfma;
+    pl.rows_per_block = da::mfma_rows_per_block();
+    pl.step = da::mfma_step_keys();
+  } else {
+    pl.variant = kValu;
+    pl.rows_per_block = da::valu_rows_per_block(fold < 8 ? fold : 8);
+    pl.step = da::valu_step_keys(pl.rows_per_block);
+  }
+  pl.row_blocks = (fold + pl.rows_per_block - 1) / pl.rows_per_block;
+  return pl;
+}
+
+Plan plan_mla(int q_len, int num_q_heads) {
+  Plan pl;
+  pl.variant = kMla;
+  pl.rows_per_block = da::mla_rows_per_block(q_len, num_q_heads);
+  pl.row_blocks = (q_len * num_q_heads + pl.rows_per_block - 1) / pl.rows_per_block;
+  pl.step = da::mla_step_keys(q_len);
+  return pl;
+}
+
+int heuristic_partitions(int base_blocks, int max_seq_len, int num_cus, int blocks_per_cu,
+                         int min_keys) {
+  if (base_blocks < 1) base_blocks = 1;
+  const long target = (long)num_cus * blocks_per_cu;
+  long P = (target + base_blocks - 1) / base_blocks;
+  const long by_len = (max_seq_len + min_keys - 1) / min_keys;
+  if (P > by_len) P = by_len;
+  if (P < 1) P = 1;
+  if (P > DA_MAX_PARTITIONS) P = DA_MAX_PARTITIONS;
+  return (int)P;
+}
+
+int keys_per_partition(int max_seq_len, int P, int step) {
+  long c = ((long)max_seq_len + P - 1) / P;
+  c = (c + step - 1) / step * step;
+  if (c < step) c = step;
+  return (int)c;
+}
+
+struct Common {
+  const uint32_t* page_table;
+  int page_size, max_pages;
+  const uint32_t* valid_length;
+  int batch, q_len, num_q_heads, max_seq_len, mask;
+  float scale;
+};
+
+int check_common(const Common& c) {
+  if (c.batch < 0 || c.q_len < 1 || c.num_q_heads < 1 || c.max_seq_len < 0)
+    return DA_ERR_INVALID_ARG;
+  if (c.mask != DA_MASK_NONE && c.mask != DA_MASK_CAUSAL) return DA_ERR_INVALID_ARG;
+  if (!std::isfinite(c.scale)) return DA_ERR_INVALID_ARG;
+  if (c.page_table) {
+    if (c.page_size < 1 || c.max_pages < 1) return DA_ERR_INVALID_ARG;
+    if (!is_pow2(c.page_size) || c.page_size < 32) return DA_ERR_UNSUPPORTED;
+    if ((long)c.max_pages * c.page_size < (long)c.max_seq_len) return DA_ERR_INVALID_ARG;
+  }
+  return DA_OK;
+}
+
+da::DecodeParams base_params(const Common& c, const void* q, const void* k, const void* v,
+                             int kv_heads, int group, int depth, int depth_v) {
+  da::DecodeParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.page_table = c.page_table;
+  p.valid_length = c.valid_length;
+  p.batch = c.batch;
+  p.q_len = c.q_len;
+  p.num_q_heads = c.num_q_heads;
+  p.num_kv_heads = kv_heads;
+  p.group = group;
+  p.depth = depth;
+  p.depth_v = depth_v;
+  p.max_seq_len = c.max_seq_len;
+  p.page_shift = c.page_table ? log2i(c.page_size) : 0;
+  p.max_pages = c.page_table ? c.max_pages : 0;
+  p.causal = c.mask == DA_MASK_CAUSAL;
+  p.scale_log2 = c.scale * 1.4426950408889634f;
+  return p;
+}
+
+void ws_sections(void* ws, int P, size_t rows, int depth_v, float** po, float** pm, float** pl) {
+  char* base = (char*)ws;
+  const size_t o_bytes = align_up((size_t)P * rows * depth_v * sizeof(float));
+  const size_t m_bytes = align_up((size_t)P * rows * sizeof(float));
+  *po = (float*)base;
+  *pm = (float*)(base + o_bytes);
+  *pl = (float*)(base + o_bytes + m_bytes);
+}
+
+hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16,
+                                 hipStream_t s) {
+  switch (v) {
+    case kValu: return da::launch_decode_valu(p, bf16, s);
+    case kMfma: return da::launch_decode_mfma(p, s);
+    default: return da::launch_mla(p, s);
+  }
+}
+
+const char* variant_name(Variant v) {
+  return v == kValu ? "valu" : (v == kMfma ? "mfma" : "mla");
+}
+
+// Shared driver of decode_attention / mla_decode (and their partial passes).
+int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int num_partitions,
+        bool partials_only, const float* sink, void* out, float* lse, void* workspace,
+        size_t workspace_bytes, void* stream) {
+  const size_t rows = (size_t)c.batch * c.q_len * c.num_q_heads;
+  if (rows == 0) return DA_OK;  // empty batch: nothing to enqueue
+  int P = num_partitions;
+  if (P == 0) {
+    P = decode_num_partitions(c.batch, c.q_len, c.num_q_heads, p.num_kv_heads, p.depth,
+                              p.depth_v, c.max_seq_len, 0);
+    if (P < 1) return P;
+  }
+  if (P < 1 || P > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  if (P > 1 && !da::splitk_reduce_supported(p.depth_v, P)) return DA_ERR_UNSUPPORTED;
+  const bool split = partials_only || P > 1;
+  if (split) {
+    const size_t need = decode_workspace_size(P, c.batch, c.q_len, c.num_q_heads, p.depth_v);
+    if (!workspace || workspace_bytes < need) return DA_ERR_WORKSPACE;
+  }
+
+  p.num_partitions = P;
+  p.keys_per_partition = keys_per_partition(c.max_seq_len, P, plan.step);
+  p.row_blocks = plan.row_blocks;
+  p.sink = sink;
+  p.out = out;
+  p.lse = lse;
+  p.write_partials = split ? 1 : 0;
+  float *po = nullptr, *pm = nullptr, *pl = nullptr;
+  if (split) ws_sections(workspace, P, rows, p.depth_v, &po, &pm, &pl);
+  p.part_o = po;
+  p.part_m = pm;
+  p.part_l = pl;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (log_enabled())
+    std::fprintf(stderr,
+                 "[decode_attention] variant=%s B=%d T=%d H=%d KVH=%d D=%d Dv=%d S=%d P=%d C=%d "
+                 "rows/block=%d row_blocks=%d grid=%d paged=%d reduce=%d\n",
+                 variant_name(plan.variant), c.batch, c.q_len, c.num_q_heads, p.num_kv_heads,
+                 p.depth, p.depth_v, c.max_seq_len, P, p.keys_per_partition,
+                 plan.rows_per_block, plan.row_blocks,
+                 P * c.batch * p.num_kv_heads * plan.row_blocks, c.page_table != nullptr,
+                 (!partials_only && P > 1) ? 1 : 0);
+  if (launch_partition_pass(p, plan.variant, bf16, s) != hipSuccess) return DA_ERR_HIP;
+  if (!partials_only && P > 1) {
+    if (da::launch_splitk_reduce(po, pm, pl, P, (int)rows, c.num_q_heads, p.depth_v, sink, out,
+                                 bf16, lse, s) != hipSuccess)
+      return DA_ERR_HIP;
+  }
+  return DA_OK;
+}
+
+int check_mha(const Common& c, const void* q, const void* k, const void* v, int group,
+              int depth, int dtype) {
+  if (!q || !k || !v) return DA_ERR_INVALID_ARG;
+  int rc = check_common(c);
+  if (rc) return rc;
+  if (group < 1 || c.num_q_heads % group != 0) return DA_ERR_INVALID_ARG;
+  if (dtype != DA_F32 && dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
+  if (depth != 64 && depth != 128) return DA_ERR_UNSUPPORTED;
+  return DA_OK;
+}
+
+int check_mla(const Common& c, const void* q, const void* kv) {
+  if (!q || !kv) return DA_ERR_INVALID_ARG;
+  return check_common(c);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* decode_attention_status_string(int status) {
+  switch (status) {
+    case DA_OK: return "ok";
+    case DA_ERR_INVALID_ARG: return "invalid argument";
+    case DA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_heads, int depth,
+                          int depth_v, int max_seq_len, int num_cus) {
+  if (batch < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || depth < 1 ||
+      depth_v < 1 || max_seq_len < 0 || num_q_heads % num_kv_heads != 0)
+    return DA_ERR_INVALID_ARG;
+  if (num_cus <= 0) num_cus = device_cus();
+  if (depth == kMlaDepth && num_kv_heads == 1) {
+    const Plan pl = plan_mla(q_len, num_q_heads);
+    // MLA partials are 512 wide per row: keep partitions long so the partial
+    // write-back stays a small fraction of the cache read.
+    return heuristic_partitions(batch * pl.row_blocks, max_seq_len, num_cus, 1, 1024);
+  }
+  const Plan pl = plan_mha(q_len, num_q_heads / num_kv_heads, true);
+  return heuristic_partitions(batch * num_kv_heads * pl.row_blocks, max_seq_len, num_cus, 4,
+                              256);
+}
+
+size_t decode_workspace_size(int num_partitions, int batch, int q_len, int num_q_heads,
+                             int depth_v) {
+  if (num_partitions < 1 || batch < 0 || q_len < 1 || num_q_heads < 1 || depth_v < 1) return 0;
+  const size_t rows = (size_t)batch * q_len * num_q_heads;
+  return align_up((size_t)num_partitions * rows * depth_v * sizeof(float)) +
+         2 * align_up((size_t)num_partitions * rows * sizeof(float));
+}
+
+size_t decode_workspace_max_offset(int num_partitions, int batch, int q_len, int num_q_heads,
+                                   int depth_v) {
+  const size_t rows = (size_t)batch * q_len * num_q_heads;
+  return align_up((size_t)num_partitions * rows * depth_v * sizeof(float));
+}
+
+size_t decode_workspace_sum_offset(int num_partitions, int batch, int q_len, int num_q_heads,
+                                   int depth_v) {
+  const size_t rows = (size_t)batch * q_len * num_q_heads;
+  return decode_workspace_max_offset(num_partitions, batch, q_len, num_q_heads, depth_v) +
+         align_up((size_t)num_partitions * rows * sizeof(float));
+}
+
+int decode_attention(const void* q, const void* k, const void* v, const uint32_t* page_table,
+                     int page_size, int max_pages_per_seq, const uint32_t* valid_length,
+                     int batch, int q_len, int num_q_heads, int group, int depth,
+                     int max_seq_len, float scale, int num_partitions,
+                     const float* sink_weights, int mask, int dtype, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+                 q_len,      num_q_heads, max_seq_len, mask, scale};
+  int rc = check_mha(c, q, k, v, group, depth, dtype);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  const bool bf16 = dtype == DA_BF16;
+  const int kv_heads = num_q_heads / group;
+  const da::DecodeParams p = base_params(c, q, k, v, kv_heads, group, depth, depth);
+  return run(c, p, plan_mha(q_len, group, bf16), bf16, num_partitions, false, sink_weights, out,
+             lse, workspace, workspace_bytes, stream);
+}
+
+int decode_attention_partials(const void* q, const void* k, const void* v,
+                              const uint32_t* page_table, int page_size, int max_pages_per_seq,
+                              const uint32_t* valid_length, int batch, int q_len,
+                              int num_q_heads, int group, int depth, int max_seq_len,
+                              float scale, int num_partitions, int mask, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+                 q_len,      num_q_heads, max_seq_len, mask, scale};
+  int rc = check_mha(c, q, k, v, group, depth, dtype);
+  if (rc) return rc;
+  if (num_partitions < 1 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  const bool bf16 = dtype == DA_BF16;
+  const int kv_heads = num_q_heads / group;
+  const da::DecodeParams p = base_params(c, q, k, v, kv_heads, group, depth, depth);
+  return run(c, p, plan_mha(q_len, group, bf16), bf16, num_partitions, true, nullptr, nullptr,
+             nullptr, workspace, workspace_bytes, stream);
+}
+
+int mla_decode(const void* q, const void* kv, const uint32_t* page_table, int page_size,
+               int max_pages_per_seq, const uint32_t* valid_length, int batch, int q_len,
+               int num_q_heads, int max_seq_len, float scale, int num_partitions,
+               const float* sink_weights, int mask, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+                 q_len,      num_q_heads, max_seq_len, mask, scale};
+  int rc = check_mla(c, q, kv);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  const da::DecodeParams p =
+      base_params(c, q, kv, kv, 1, num_q_heads, kMlaDepth, kMlaDepthV);
+  return run(c, p, plan_mla(q_len, num_q_heads), true, num_partitions, false, sink_weights, out,
+             lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_partials(const void* q, const void* kv, const uint32_t* page_table,
+                        int page_size, int max_pages_per_seq, const uint32_t* valid_length,
+                        int batch, int q_len, int num_q_heads, int max_seq_len, float scale,
+                        int num_partitions, int mask, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+                 q_len,      num_q_heads, max_seq_len, mask, scale};
+  int rc = check_mla(c, q, kv);
+  if (rc) return rc;
+  if (num_partitions < 1 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  const da::DecodeParams p =
+      base_params(c, q, kv, kv, 1, num_q_heads, kMlaDepth, kMlaDepthV);
+  return run(c, p, plan_mla(q_len, num_q_heads), true, num_partitions, true, nullptr, nullptr,
+             nullptr, workspace, workspace_bytes, stream);
+}
+
+int splitk_reduce(const float* part_o, const float* part_max, const float* part_sum,
+                  int num_partitions, int rows, int num_q_heads, int depth_v,
+                  const float* sink_weights, void* out, int out_dtype, float* lse,
+                  void* stream) {
+  if (!part_o || !part_max || !part_sum || !out) return DA_ERR_INVALID_ARG;
+  if (rows < 0 || num_q_heads < 1 || num_partitions < 1) return DA_ERR_INVALID_ARG;
+  if (out_dtype != DA_F32 && out_dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
+  if (!da::splitk_reduce_supported(depth_v, num_partitions)) return DA_ERR_UNSUPPORTED;
+  if (rows == 0) return DA_OK;
+  if (da::launch_splitk_reduce(part_o, part_max, part_sum, num_partitions, rows, num_q_heads,
+                               depth_v, sink_weights, out, out_dtype == DA_BF16, lse,
+                               (hipStream_t)stream) != hipSuccess)
+    return DA_ERR_HIP;
+  return DA_OK;
+}
+
+}  // extern "C"

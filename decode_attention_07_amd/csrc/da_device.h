@@ -1,0 +1,102 @@
+// da_device.h -- small device helpers for the gfx950 decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "da_params.h"
+
+namespace da {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---- bf16 <-> fp32 ------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c with bf16 pairs (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---- cross-lane (DPP within rows of 16 lanes) -----------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each half row
+constexpr int kDppRowRor8 = 0x128;    // lane i <- lane (i+8) mod 16 within each row
+
+// Sum over aligned groups of 8 lanes; every lane of the group gets the total.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+__device__ __forceinline__ int wave_id_uniform() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// ---- online-softmax state merge (log2 domain) ----------------------------------
+// Combines (mA, lA) with (mB, lB); returns the scale factors for A and B.
+__device__ __forceinline__ void merge_factors(float mA, float mB, float& m, float& fa,
+                                              float& fb) {
+  m = fmaxf(mA, mB);
+  float ms = (m == kNegInf) ? 0.f : m;
+  fa = fast_exp2(mA - ms);
+  fb = fast_exp2(mB - ms);
+}
+
+// ---- per-row key limits ----------------------------------------------------------
+// Keys of sequence b visible to query token t.
+__device__ __forceinline__ int visible_keys(const DecodeParams& p, int b, int t) {
+  int n = p.valid_length ? (int)p.valid_length[b] : p.max_seq_len;
+  if (n > p.max_seq_len) n = p.max_seq_len;
+  if (p.causal) {
+    int lim = n - p.q_len + t + 1;
+    n = lim < n ? lim : n;
+  }
+  return n < 0 ? 0 : n;
+}
+
+// Element offset of key j's row (row width `width` elements, KV head g).
+__device__ __forceinline__ size_t kv_row(const DecodeParams& p, int b, int j, int g, int width) {
+  size_t row;
+  if (p.page_table) {
+    uint32_t phys = p.page_table[(size_t)b * p.max_pages + (j >> p.page_shift)];
+    row = ((size_t)phys << p.page_shift) + (size_t)(j & ((1 << p.page_shift) - 1));
+  } else {
+    row = (size_t)b * p.max_seq_len + j;
+  }
+  return (row * p.num_kv_heads + g) * (size_t)width;
+}
+
+}  // namespace da

@@ -1,0 +1,37 @@
+// da_params.h -- launch parameters shared by the host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da {
+
+// Everything a partition-pass kernel needs.  Passed by value (kernarg segment).
+struct DecodeParams {
+  const void* q;                // [B, T, H, D]
+  const void* k;                // dense [B, S, KVH, D] or pool [pages, ps, KVH, D]
+  const void* v;                // same layout with Dv; unused by MLA (V = K[..., :Dv])
+  const uint32_t* page_table;   // [B, max_pages] or nullptr
+  const uint32_t* valid_length; // [B] or nullptr
+  const float* sink;            // [H] or nullptr (used only when P == 1)
+  void* out;                    // [B, T, H, Dv] (P == 1)
+  float* lse;                   // [B, T, H] or nullptr (P == 1)
+  float* part_o;                // [P, rows, Dv] (P > 1)
+  float* part_m;                // [P, rows]
+  float* part_l;                // [P, rows]
+  int batch, q_len, num_q_heads, num_kv_heads, group, depth, depth_v, max_seq_len;
+  int page_shift;               // log2(page_size) when paged
+  int max_pages;
+  int causal;
+  int num_partitions;
+  int keys_per_partition;       // C: partition p covers keys [p*C, (p+1)*C)
+  int row_blocks;               // row tiles per (batch, KV head)
+  int write_partials;           // 1: write part_*; 0: write out / lse directly
+  float scale_log2;             // scale * log2(e)
+};
+
+// Row-block geometry of a (batch, KV head): T*group rows (token-major:
+// row = t*group + i is query head kv*group + i of token t).
+__host__ __device__ inline int fold_rows(const DecodeParams& p) { return p.q_len * p.group; }
+
+}  // namespace da

@@ -1,0 +1,194 @@
+/*
+ * decode_attention.h -- C ABI of the MI355X (gfx950) split-K decode-attention
+ * library.
+ *
+ * The operation (description of "mha_decoding_single_batch_pipelined"; Args of
+ * "mha_sm100_dispatch" and "flare_mla_decoding_dispatch"): for every query row
+ * (batch b, query token t, query head h)
+ *
+ *     out[b,t,h,:] = softmax_j( scale * <q[b,t,h,:], k_j> + mask_j ) . V
+ *
+ * over the keys j of sequence b that the row may see, computed as FA2 online
+ * softmax per key partition ("split-K": each partition is a contiguous slice of
+ * the key axis that writes a partial output with its running max and exp-sum)
+ * followed by a log-sum-exp merge of the partials (the "mha_splitk_reduce" /
+ * "mla_splitk_reduce" pass).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises, and never reads device memory on
+ *    the host, so calls may be captured into a HIP graph.  All work is enqueued
+ *    on `stream` (a hipStream_t; NULL = the default stream) in order.
+ *  - Layouts are dense, row-major, with the last index fastest:
+ *      q            [batch, q_len, num_q_heads, depth]
+ *      k, v (dense) [batch, max_seq_len, num_kv_heads, depth]
+ *      k, v (paged) [num_pages, page_size, num_kv_heads, depth]  (page pools)
+ *      page_table   [batch, max_pages_per_seq] uint32: logical page i of
+ *                   sequence b lives in pool page page_table[b * max_pages_per_seq + i]
+ *      valid_length [batch] uint32: keys of sequence b (the current tokens
+ *                   included); NULL means every sequence has max_seq_len keys
+ *      out          [batch, q_len, num_q_heads, depth_v] in the input dtype
+ *      lse          [batch, q_len, num_q_heads] fp32, natural log of the
+ *                   softmax denominator (sink included); may be NULL
+ *      sink_weights [num_q_heads] fp32 logits or NULL
+ *  - Query head h reads KV head h / group (group = query heads per KV head).
+ *  - Causal mask (q_len > 1): token t of T sees key j iff j <= N_b - T + t
+ *    (the T query tokens are the last T positions of the sequence).
+ *  - Sink: sigma_h joins the softmax denominator once per row, as a virtual
+ *    key of score sigma_h (not multiplied by scale) whose value row is zero.
+ *  - A row with no visible key and no sink yields out = 0 and lse = -inf.
+ *  - Keys at or past a row's visible length are never read into the result,
+ *    whatever they hold (NaN included).
+ *  - Every argument check runs before anything is enqueued; on error nothing
+ *    is enqueued and a negative status is returned.  Launch failures map to
+ *    DA_ERR_HIP.  Calls are thread-safe.
+ */
+#ifndef DECODE_ATTENTION_H
+#define DECODE_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define DA_OK 0
+#define DA_ERR_INVALID_ARG (-1) /* null pointer, bad size, inconsistent shape   */
+#define DA_ERR_UNSUPPORTED (-2) /* valid but not built: depth, dtype, page size */
+#define DA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required   */
+#define DA_ERR_HIP (-4)         /* a HIP runtime call or launch failed          */
+
+/* Element types of q / k / v / out (the output dtype matches q:
+ * "flare_mla_decoding_dispatch", Args `output`). */
+#define DA_F32 0
+#define DA_BF16 1
+
+/* Masks applied to the scores ("mha_sm100_dispatch", Parameters `MaskType`). */
+#define DA_MASK_NONE 0
+#define DA_MASK_CAUSAL 1
+
+/* Largest partition count accepted (bounded by the workspace layout). */
+#define DA_MAX_PARTITIONS 1024
+
+/* Human-readable text for a status code (static storage). */
+const char* decode_attention_status_string(int status);
+
+/*
+ * Partition-count heuristic ("mha_sm100_dispatch", Args
+ * `num_partitions_override`: 0 selects the automatic ladder;
+ * "flare_mla_decoding_dispatch", Args `num_partitions`: None selects via
+ * heuristic).  Picks P >= 1 so that the grid of (batch x KV head x row block x
+ * partition) blocks fills `num_cus` compute units while each partition keeps
+ * enough keys to amortise its prologue and its partial write-back.
+ * num_cus <= 0 queries the current device.  MLA calls pass num_kv_heads = 1,
+ * depth = 576, depth_v = 512.  Returns P, or a negative status.
+ */
+int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_heads, int depth,
+                          int depth_v, int max_seq_len, int num_cus);
+
+/*
+ * Bytes of the split-K workspace for `num_partitions` partitions.  A
+ * decode_attention() / mla_decode() call that runs with one partition does not
+ * touch the workspace (it may be NULL); the *_partials() passes always write it.
+ * Workspace layout (each section 256-byte aligned):
+ *   part_o   fp32 [P, rows, depth_v]  partial outputs, each normalised by its exp-sum
+ *   part_max fp32 [P, rows]           partial max, natural-log units (-inf if empty)
+ *   part_sum fp32 [P, rows]           partial exp-sum relative to part_max (0 if empty)
+ * with rows = batch * q_len * num_q_heads.  Returns 0 for invalid arguments.
+ */
+size_t decode_workspace_size(int num_partitions, int batch, int q_len, int num_q_heads,
+                             int depth_v);
+
+/* Byte offsets of part_max and part_sum inside that workspace (part_o is at 0). */
+size_t decode_workspace_max_offset(int num_partitions, int batch, int q_len, int num_q_heads,
+                                   int depth_v);
+size_t decode_workspace_sum_offset(int num_partitions, int batch, int q_len, int num_q_heads,
+                                   int depth_v);
+
+/*
+ * Decode attention over a dense or paged KV cache (MHA / GQA).
+ *   q, k, v         see the layouts above; dtype DA_F32 or DA_BF16 for all of
+ *                   q, k, v and out.
+ *   page_table      NULL for a dense cache; otherwise page_size must be a power
+ *                   of two >= 32 and max_pages_per_seq >= ceil(max_seq_len / page_size).
+ *   valid_length    per-sequence key counts or NULL ("mha_sm100_dispatch", Args
+ *                   `valid_length`); values above max_seq_len count as max_seq_len.
+ *   group           query heads per KV head; num_q_heads % group == 0.
+ *   depth           64 or 128 (the value depth equals depth).
+ *   max_seq_len     host upper bound of the key count ("mha_sm100_dispatch",
+ *                   Args `max_cache_valid_length_arg`); also the dense cache's
+ *                   sequence stride.
+ *   scale           multiplies q.k before the softmax.
+ *   num_partitions  0 = decode_num_partitions(); > 0 is used verbatim.
+ *   mask            DA_MASK_NONE or DA_MASK_CAUSAL.
+ *   workspace       >= decode_workspace_size(P, ...) bytes when P > 1 (may be
+ *                   NULL when P == 1).
+ */
+int decode_attention(const void* q, const void* k, const void* v, const uint32_t* page_table,
+                     int page_size, int max_pages_per_seq, const uint32_t* valid_length,
+                     int batch, int q_len, int num_q_heads, int group, int depth,
+                     int max_seq_len, float scale, int num_partitions,
+                     const float* sink_weights, int mask, int dtype, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The partition pass of decode_attention() alone: writes the split-K partials
+ * of every row into `workspace` (layout above) for a later splitk_reduce()
+ * (e.g. after the partials of several devices have been gathered).  Takes the
+ * arguments of decode_attention() without sink / out / lse; num_partitions
+ * must be >= 1 (used verbatim; 1 gives a single partial per row).
+ */
+int decode_attention_partials(const void* q, const void* k, const void* v,
+                              const uint32_t* page_table, int page_size, int max_pages_per_seq,
+                              const uint32_t* valid_length, int batch, int q_len,
+                              int num_q_heads, int group, int depth, int max_seq_len,
+                              float scale, int num_partitions, int mask, int dtype,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * MLA decode ("flare_mla_decoding_dispatch"): one KV head ("kv_num_heads ...
+ * Must be 1 for MLA"), depth 576, and V = K[..., :512] read from the same cache
+ * rows ("V is derived as K[:, :, :depth_v], so V is not loaded separately").
+ *   q    bf16 [batch, q_len, num_q_heads, 576]; the q_len tokens of a sequence
+ *        are folded into one block of rows (the MTP token fold).
+ *   kv   bf16 dense [batch, max_seq_len, 1, 576] or pool [num_pages, page_size, 1, 576]
+ *   out  bf16 [batch, q_len, num_q_heads, 512]; lse fp32 [batch, q_len, num_q_heads] or NULL
+ * Other arguments as for decode_attention().
+ */
+int mla_decode(const void* q, const void* kv, const uint32_t* page_table, int page_size,
+               int max_pages_per_seq, const uint32_t* valid_length, int batch, int q_len,
+               int num_q_heads, int max_seq_len, float scale, int num_partitions,
+               const float* sink_weights, int mask, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* The partition pass of mla_decode() alone (see decode_attention_partials()). */
+int mla_decode_partials(const void* q, const void* kv, const uint32_t* page_table,
+                        int page_size, int max_pages_per_seq, const uint32_t* valid_length,
+                        int batch, int q_len, int num_q_heads, int max_seq_len, float scale,
+                        int num_partitions, int mask, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Log-sum-exp merge of split-K partials ("mha_splitk_reduce"; "mla_splitk_reduce").
+ *   part_o    fp32 [num_partitions, rows, depth_v]  normalised partial outputs
+ *   part_max  fp32 [num_partitions, rows]           natural-log partial max
+ *   part_sum  fp32 [num_partitions, rows]           partial exp-sum (0 = empty)
+ *   sink_weights  [num_q_heads] or NULL; row r uses head r % num_q_heads
+ *   out       [rows, depth_v] in out_dtype (DA_F32 or DA_BF16, rounded to nearest even)
+ *   lse       [rows] fp32 or NULL
+ * Per row: M = max(max_p part_max, sigma); w_p = part_sum_p * exp(part_max_p - M);
+ * L = sum_p w_p + exp(sigma - M); out = sum_p w_p * part_o_p / L; lse = M + ln L.
+ * depth_v must be one of 64, 128, 256, 512, 1024; 1 <= num_partitions <= DA_MAX_PARTITIONS.
+ */
+int splitk_reduce(const float* part_o, const float* part_max, const float* part_sum,
+                  int num_partitions, int rows, int num_q_heads, int depth_v,
+                  const float* sink_weights, void* out, int out_dtype, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTENTION_H */

@@ -36,7 +36,7 @@ namespace {
 constexpr int kMlaDepth = 576;
 constexpr int kMlaDepthV = 512;
 constexpr size_t kAlign = 256;
-constexpr bool kMfmaReady = false;
+constexpr bool kMfmaReady = true;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 

@@ -52,7 +52,7 @@ def test_small_shapes(shape, P):
 def test_ragged_lengths_with_zero_and_sink(P):
     wl = W.Workload("ragged_sink", 8201, batch=5, num_heads=8, kv_heads=2, depth=128,
                     max_seq_len=400, ragged=(0, 400, 1), sink=True)
-    inp = W.make_inputs(wl)
+    inp = W.make_inputs(wl, poison=False)  # lengths are edited below
     inp.valid_length[2] = 0          # an empty sequence
     inp.valid_length[3] = 400        # a full one
     check(wl, num_partitions=P, inp=inp)
@@ -145,3 +145,29 @@ def test_deterministic_and_guard_bands():
     assert bool((buf[:guard] == g).all()) and bool((buf[guard + n:] == g).all())
     assert bool((lbuf[:guard] == 777.0).all()) and bool((lbuf[guard + wl.batch * wl.num_heads:]
                                                           == 777.0).all())
+
+
+# ---- the matrix-core path (bf16, 8+ query rows per KV head) ------------------------
+
+def test_paged_ragged_full():
+    check(W.PAGED, num_partitions=0)
+
+
+MFMA = [
+    # (B, T, H, KVH, D, S, page, causal)
+    (2, 1, 16, 2, 128, 333, 0, False),     # group 8 (half-filled 16-row tile)
+    (2, 1, 32, 2, 128, 500, 0, False),     # group 16 (full tile)
+    (2, 1, 64, 2, 64, 257, 0, False),      # group 32 -> two row blocks, depth 64
+    (3, 2, 24, 2, 128, 300, 64, True),     # MTP fold: 2 tokens x group 12 = 24 rows
+    (2, 3, 8, 1, 64, 100, 32, True),       # 3 tokens x group 8, one KV head
+]
+
+
+@pytest.mark.parametrize("shape", MFMA, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("P", [1, 3])
+def test_mfma_shapes(shape, P):
+    B, T, H, KVH, D, S, page, causal = shape
+    wl = W.Workload(f"mfma_{'x'.join(map(str, shape))}", 8700 + S + T, batch=B, num_heads=H,
+                    kv_heads=KVH, depth=D, max_seq_len=S, q_len=T, causal=causal,
+                    page_size=page, ragged=(1, S, 1), sink=(P == 3))
+    check(wl, num_partitions=P)

@@ -42,7 +42,7 @@ struct MfmaCfg {
   static constexpr int KEYS_PER_VLOAD = 64 / CHUNKS;
   static constexpr int PITCH = D * 2 + 8;           // LDS bytes per V row (bank spread)
   static constexpr int VBUF = kTile * PITCH;        // LDS bytes per wave tile
-  static constexpr int MERGE = kWaves * 16 * (D + 2) * 4;
+  static constexpr int MERGE = kWaves * 16 * (D + 3) * 4;
   static constexpr int SMEM = (kWaves * VBUF > MERGE) ? kWaves * VBUF : MERGE;
 };
 
@@ -105,7 +105,8 @@ __device__ __forceinline__ void mfma_load(const DecodeParams& p, MfmaTile<D>& t,
 template <int D, bool MASKED>
 __device__ __forceinline__ void mfma_process(const MfmaTile<D>& t, const bf16x8_t (&qf)[MfmaCfg<D>::KS],
                                              f32x4_t (&acc)[MfmaCfg<D>::DT], float& m,
-                                             float& lsum, char* vl, int j0, int lane, int hi,
+                                             float& lsum, float& lsr, char* vl, int j0,
+                                             int lane, int hi,
                                              float scale_log2) {
   using C = MfmaCfg<D>;
   const int c16 = lane & 15, g16 = lane >> 4;
@@ -156,10 +157,14 @@ __device__ __forceinline__ void mfma_process(const MfmaTile<D>& t, const bf16x8_
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) acc[dt] *= alpha;
   // P^T operand: k-slot (g16, j) holds key j<4 ? 4*g16+j : 16+4*g16+(j-4).
+  // The weights enter the MFMA rounded to bf16; O is normalised by their rounded
+  // sum (lsr) so that the effective weights sum to one.
   const uint32_t pb0 = pack_bf16(pr[0][0], pr[0][1]);
   const uint32_t pb1 = pack_bf16(pr[0][2], pr[0][3]);
   const uint32_t pb2 = pack_bf16(pr[1][0], pr[1][1]);
   const uint32_t pb3 = pack_bf16(pr[1][2], pr[1][3]);
+  lsr = lsr * alpha + ((bf16lo(pb0) + bf16hi(pb0)) + (bf16lo(pb1) + bf16hi(pb1)) +
+                       (bf16lo(pb2) + bf16hi(pb2)) + (bf16lo(pb3) + bf16hi(pb3)));
   const uint4 pbu = make_uint4(pb0, pb1, pb2, pb3);
   const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbu);
   // O^T += V^T . P^T; V^T operand read from LDS by column (same k-slot order).
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
   f32x4_t acc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, lsum = 0.f;
+  float m = kNegInf, lsum = 0.f, lsr = 0.f;  // exact and bf16-rounded weight sums
   char* vl = smem + wave * C::VBUF;
 
   const int n_full = (hmin - k_lo) / kTile;
@@ -237,13 +242,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
     for (;;) {
       const bool more = t + kWaves < n_full;
       if (more) mfma_load<D, false>(p, tb, b, g, k_lo + (t + kWaves) * kTile, lane, 0);
-      mfma_process<D, false>(ta, qf, acc, m, lsum, vl, k_lo + t * kTile, lane, hi,
+      mfma_process<D, false>(ta, qf, acc, m, lsum, lsr, vl, k_lo + t * kTile, lane, hi,
                              p.scale_log2);
       t += kWaves;
       if (!more) break;
       const bool more2 = t + kWaves < n_full;
       if (more2) mfma_load<D, false>(p, ta, b, g, k_lo + (t + kWaves) * kTile, lane, 0);
-      mfma_process<D, false>(tb, qf, acc, m, lsum, vl, k_lo + t * kTile, lane, hi,
+      mfma_process<D, false>(tb, qf, acc, m, lsum, lsr, vl, k_lo + t * kTile, lane, hi,
                              p.scale_log2);
       t += kWaves;
       if (!more2) break;
@@ -252,18 +257,21 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
   for (; t < n_tot; t += kWaves) {
     MfmaTile<D> tt;
     mfma_load<D, true>(p, tt, b, g, k_lo + t * kTile, lane, hmax);
-    mfma_process<D, true>(tt, qf, acc, m, lsum, vl, k_lo + t * kTile, lane, hi, p.scale_log2);
+    mfma_process<D, true>(tt, qf, acc, m, lsum, lsr, vl, k_lo + t * kTile, lane, hi, p.scale_log2);
   }
 
   // Row exp-sum across the 4 lane groups.
   lsum += shfl_xor(lsum, 16);
   lsum += shfl_xor(lsum, 32);
+  lsr += shfl_xor(lsr, 16);
+  lsr += shfl_xor(lsr, 32);
 
   // Merge the 4 waves through LDS (reusing the V buffers).
   __syncthreads();
   float* so = (float*)smem;                       // [wave][row][D]
   float* sm = so + kWaves * 16 * D;               // [wave][row]
   float* sl = sm + kWaves * 16;                   // [wave][row]
+  float* sr = sl + kWaves * 16;                   // [wave][row]
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -271,6 +279,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
   if (g16 == 0) {
     sm[wave * 16 + c16] = m;
     sl[wave * 16 + c16] = lsum;
+    sr[wave * 16 + c16] = lsr;
   }
   __syncthreads();
 
@@ -285,18 +294,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * 16 + r]);
     const float Ms = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, O = 0.f;
+    float L = 0.f, Lr = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float f = fast_exp2(sm[w * 16 + r] - Ms);
       L += f * sl[w * 16 + r];
+      Lr += f * sr[w * 16 + r];
       O += f * so[(w * 16 + r) * D + d];
     }
     const size_t row = ((size_t)b * p.q_len + tt_) * p.num_q_heads + h;
     if (p.write_partials) {
       const size_t prow = (size_t)pidx * ((size_t)p.batch * p.q_len * p.num_q_heads) + row;
       const bool any = L > 0.f;
-      p.part_o[prow * D + d] = any ? O / L : 0.f;
+      p.part_o[prow * D + d] = any ? O / Lr : 0.f;
       if (d == 0) {
         p.part_m[prow] = any ? M * kLn2 : kNegInf;
         p.part_l[prow] = L;
@@ -306,12 +316,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
         const float sig = p.sink[h] * kLog2e;
         const float M2 = fmaxf(M, sig);
         const float c = fast_exp2(M - M2);
-        L = L * c + fast_exp2(sig - M2);
+        const float e = fast_exp2(sig - M2);
+        L = L * c + e;
+        Lr = Lr * c + e;
         O *= c;
         M = M2;
       }
       const bool any = L > 0.f;
-      ((uint16_t*)p.out)[row * D + d] = to_bf16(any ? O / L : 0.f);
+      ((uint16_t*)p.out)[row * D + d] = to_bf16(any ? O / Lr : 0.f);
       if (d == 0 && p.lse) p.lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
     }
   }

@@ -4,21 +4,31 @@
 // read from the same cache rows ("V is derived as K[:, :, :depth_v], so V is not
 // loaded separately").  The q_len tokens of a sequence and its num_q_heads heads
 // are folded into one set of T*H rows (the MTP token fold); a block owns 128 of
-// those rows (8 waves x 16 rows) and one partition of the keys, so every cache row
-// of the partition is read from HBM once per 128 rows.
+// those rows (4 waves x 32 rows, one wave per SIMD) and one partition of the
+// keys, so every cache row of the partition is read from HBM once per 128 rows.
 //
-// Per 32-key tile, shared by the block through LDS (double buffered, filled by
-// all 512 threads with 16-byte loads):
-//   S^T[32 keys x 16 rows] = K[32 x 576] . Q^T[576 x 16]     18 MFMAs per 16 keys
-//       A = K from LDS (16-byte reads, padded rows), B = this wave's Q^T kept
-//       in registers for the whole kernel.
-//   online softmax on the accumulator layout (lane l owns row l % 16); the
-//       running max is updated lazily: O and l are rescaled only when a row's
-//       tile max exceeds the reference max by more than 2^8, which keeps every
-//       exp2 argument <= 8 and the fp32 sums far from overflow.
-//   O^T[512 x 16 rows] += V^T[512 x 32 keys] . P^T[32 x 16]  32 MFMAs
-//       A = V^T read by column from the same LDS tile, B = P^T straight from the
-//       S^T accumulators (bf16).
+// Per 32-key tile, shared by the block through a 3-stage LDS ring filled by
+// direct global->LDS loads (no staging registers; two tiles in flight):
+//   S^T[32 keys x 32 rows] = K[32 x 576] . Q^T[576 x 32]    36 v_mfma_f32_32x32x16_bf16
+//       A = K from LDS, B = the wave's Q^T kept in registers for the whole
+//       kernel (144 VGPRs).
+//   softmax on the accumulator layout: lane l owns row l % 32 and 16 of the 32
+//       keys, lane l ^ 32 the other 16.  Each row keeps a fixed reference max,
+//       set by its first visible tile: p = 2^(s - m) may grow to 2^100 (fp32 and
+//       bf16 hold that, and the sums stay below 2^128), so O is never rescaled
+//       inside the loop.  If a row ever exceeds its reference by more than that,
+//       the block restarts its partition with the raised reference; each restart
+//       lifts the row's reference above every score seen so far, so restarts
+//       end, and for attention scores they do not occur in practice.
+//   O^T[512 x 32 rows] += V^T[512 x 32 keys] . P^T[32 x 32]  32 MFMAs
+//       A = V^T read by column from the same LDS tile, B = P^T taken straight
+//       from the S^T accumulators (bf16); O^T lives in the 256 accumulation
+//       registers.
+// LDS tile layout: column-major in 16-byte chunks with an XOR swizzle,
+//   chunk(key, col) = col * 32 + (key ^ (col & 3)),  col = 16-byte column 0..71,
+// so one 1 KB DMA instruction fills two columns of all 32 keys, the K-operand
+// reads of a half wave cover 512 contiguous bytes, and the V^T column reads of
+// a wave fall in 16 distinct bank groups.
 // With two tokens (256 rows) a sequence needs two blocks that read the same
 // tiles; their block ids differ by a multiple of 8 so that both land on the same
 // XCD and the second read of each tile is served by that XCD's L2.
@@ -31,31 +41,46 @@ namespace {
 constexpr int kD = 576;
 constexpr int kDv = 512;
 constexpr int kBN = 32;
-constexpr int kWaves = 8;
-constexpr int kRows = 16 * kWaves;           // rows per block
+constexpr int kWaves = 4;
+constexpr int kWaveRows = 32;
+constexpr int kRows = kWaveRows * kWaves;    // rows per block
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKS = kD / 32;                 // 18 depth steps
-constexpr int kDT = kDv / 16;                // 32 output depth tiles
+constexpr int kKS = kD / 16;                 // 36 depth steps of 16
+constexpr int kDT = kDv / 32;                // 16 output depth tiles of 32
 constexpr int kRowBytes = kD * 2;            // 1152
-constexpr int kPitch = kRowBytes + 16;       // LDS row pitch (bank spread)
-constexpr int kTileBytes = kBN * kPitch;
-constexpr int kChunksPerRow = kRowBytes / 16;   // 72
-constexpr int kChunks = kBN * kChunksPerRow;    // 2304
-constexpr int kLoads = (kChunks + kThreads - 1) / kThreads;  // 5
-constexpr float kLazy = 8.0f;                // rescale threshold (log2 units)
+constexpr int kCols = kRowBytes / 16;        // 72 columns of 16 bytes
+constexpr int kTileBytes = kCols * kBN * 16; // 36 KB
+constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // 9
+static_assert(kDmaPerWave * kWaves * 1024 == kTileBytes, "tile must split into 1 KB pieces");
+constexpr int kStages = 3;
+constexpr float kHeadroom = 100.0f;          // largest exp2 argument (log2 units)
 
-struct Stage {
-  uint4 v[kLoads];
-};
+// 16 bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane i of the wave writes lds_base + 16 * i.  Issued
+// through inline asm so that the compiler does not serialise later LDS reads of
+// other stages behind it; completion is tracked with explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
 
-__device__ __forceinline__ void mla_load(const DecodeParams& p, Stage& st, int b, int j0,
-                                         int kend) {
-  const int tid = threadIdx.x;
-  if (j0 >= kend) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) st.v[i] = make_uint4(0, 0, 0, 0);
-    return;
-  }
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt_hi[15:14]; expcnt left at its maximum).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
+// Requests the 32-key tile starting at key j0 into one LDS stage.  Instruction n
+// (n = wave + 4 i) fills columns 2n and 2n + 1; lane l of it takes column
+// 2n + (l >> 5) of key (l & 31) ^ (column & 3), which keeps the column-major
+// swizzled layout.  Keys at or past `kend` fetch row 0 of the tile instead
+// (finite data; those keys are masked out of the softmax), so every wave
+// issues exactly kDmaPerWave instructions.
+__device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage, int b, int j0,
+                                          int kend, int wave, int lane) {
   size_t row0;
   if (p.page_table) {
     const uint32_t phys = p.page_table[(size_t)b * p.max_pages + (j0 >> p.page_shift)];
@@ -63,106 +88,157 @@ __device__ __forceinline__ void mla_load(const DecodeParams& p, Stage& st, int b
   } else {
     row0 = (size_t)b * p.max_seq_len + j0;
   }
-  const char* base = (const char*)p.k + row0 * kRowBytes;
+  const int g = lane >> 5;
+  const int col0 = 2 * wave + g;               // column of instruction i is col0 + 8 i
+  const int key = (lane & 31) ^ (col0 & 3);    // (col0 + 8 i) & 3 == col0 & 3
+  const bool real = j0 + key < kend;
+  const char* src =
+      (const char*)p.k + row0 * kRowBytes + (real ? key * kRowBytes : 0) + col0 * 16;
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + wave * 1024);
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int c = tid + i * kThreads;
-    const int key = c / kChunksPerRow;
-    const int col = c % kChunksPerRow;
-    if (c < kChunks && j0 + key < kend)
-      st.v[i] = *(const uint4*)(base + (size_t)key * kRowBytes + col * 16);
-    else
-      st.v[i] = make_uint4(0, 0, 0, 0);
-  }
+  for (int i = 0; i < kDmaPerWave; ++i) dma16(src + i * 128, dst + i * kWaves * 1024);
 }
 
-__device__ __forceinline__ void mla_store(const Stage& st, char* buf) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int c = tid + i * kThreads;
-    if (c < kChunks) {
-      const int key = c / kChunksPerRow;
-      const int col = c % kChunksPerRow;
-      *(uint4*)(buf + key * kPitch + col * 16) = st.v[i];
-    }
-  }
+// The MFMAs are written as inline asm so that the register classes are fixed:
+// the O^T accumulator in the 256 accumulation registers, Q^T and the score
+// tiles in arch VGPRs (left to itself the compiler puts the score accumulators
+// in AGPRs and then spills Q^T).  The compiler does not see inside the asm, so
+// the hazards are covered here: a leading s_nop for a VALU write of A / B just
+// before the MFMA, and mfma_settle() before any VALU or accvgpr read of a
+// result.
+//
+// acc += A . B, acc in AGPRs.
+__device__ __forceinline__ void mfma_acc(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+a"(acc)
+               : "v"(a), "v"(b));
 }
 
-template <bool MASKED>
+// Score tile s (= / +=) A . B with s in arch VGPRs (the AGPRs hold O^T).  The
+// output is early-clobber: an MFMA destination may not overlap its A/B sources.
+__device__ __forceinline__ void mfma_v_first(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16_t& s, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+&v"(s) : "v"(a), "v"(b));
+}
+
+// Wait states between the last MFMA of a chain and a VALU / accvgpr read of its
+// result (24; the compiler itself uses 12 for this instruction).  The results
+// pass through the asm as operands, so that no read of them can be scheduled
+// above the s_nops.
+__device__ __forceinline__ void mfma_settle(f32x16_t& s0, f32x16_t& s1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+}
+__device__ __forceinline__ void mfma_settle(f32x16_t (&acc)[kDT]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) asm volatile("" : "+a"(acc[dt]));  // ordered after the nops
+}
+
+// acc = 0 without passing through arch VGPRs (0 * 0 + 0 in the matrix core).
+__device__ __forceinline__ void zero_acc(f32x16_t& acc, const bf16x8_t& zero) {
+  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
+}
+
+// Key of accumulator element j (0..15) of lane half g in a 32x32 C tile.
+__device__ __forceinline__ constexpr int c32_row(int j, int g) {
+  return (j / 4) * 8 + g * 4 + (j % 4);
+}
+
 __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[kKS],
-                                         f32x4_t (&acc)[kDT], float& m, float& lsum, int j0,
-                                         int hi, float scale_log2) {
+                                         f32x16_t (&acc)[kDT], float& m, float& lsum, float& lsr,
+                                         int j0,
+                                         bool masked, int hi, float scale_log2, int* restart) {
   const int lane = threadIdx.x & 63;
-  const int c16 = lane & 15, g16 = lane >> 4;
-  f32x4_t s[2];
+  const int c32 = lane & 31, g = lane >> 5;
+  // S^T = K . Q^T; the A operand of depth step st is column 2 st + g of key c32.
+  f32x16_t s0, s1;
+  const char* ka = buf + (g * 32 + (c32 ^ g)) * 16;        // even st: col & 3 = g
+  const char* kb = buf + (g * 32 + (c32 ^ (2 + g))) * 16;  // odd st:  col & 3 = 2 + g
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const char* krow = buf + (kt * 16 + c16) * kPitch + g16 * 16;
-#pragma unroll
-    for (int st = 0; st < kKS; ++st) {
-      const bf16x8_t a = *(const bf16x8_t*)(krow + st * 64);
-      s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], s[kt], 0, 0, 0);
+  for (int st = 0; st < kKS; st += 2) {
+    const bf16x8_t a0 = *(const bf16x8_t*)(ka + st * 1024);
+    const bf16x8_t a1 = *(const bf16x8_t*)(kb + (st + 1) * 1024);
+    if (st == 0) {
+      mfma_v_first(s0, a0, qf[st]);
+      mfma_v_first(s1, a1, qf[st + 1]);
+    } else {
+      mfma_v(s0, a0, qf[st]);
+      mfma_v(s1, a1, qf[st + 1]);
     }
   }
-  float x[2][4];
+  mfma_settle(s0, s1);
+  float x[16];
   float mx = kNegInf;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float v = s[kt][j] * scale_log2;
-      if (MASKED) v = (j0 + kt * 16 + g16 * 4 + j < hi) ? v : kNegInf;
-      x[kt][j] = v;
-      mx = fmaxf(mx, v);
-    }
-  mx = fmaxf(mx, shfl_xor(mx, 16));
+  for (int j = 0; j < 16; ++j) {
+    float v = (s0[j] + s1[j]) * scale_log2;
+    if (masked) v = (j0 + c32_row(j, g) < hi) ? v : kNegInf;
+    x[j] = v;
+    mx = fmaxf(mx, v);
+  }
   mx = fmaxf(mx, shfl_xor(mx, 32));
-  // Lazy rescale: move the reference max only when the tile exceeds it by > kLazy.
-  if (mx > m + kLazy) {
-    const float mn = mx;
-    const float alpha = fast_exp2(m - mn);  // m = -inf on the first tile -> 0
-    lsum *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) acc[dt] *= alpha;
-    m = mn;
+  // Fixed reference per row: exp2 arguments may reach kHeadroom; a row whose
+  // tile max exceeds it raises the block's restart flag (the partition is then
+  // recomputed from its first key with the larger reference).
+  const bool grow = mx > m + kHeadroom;
+  if (grow) {
+    if (m != kNegInf) *restart = 1;  // first visible tile of a row: acc is still 0, no restart
+    m = mx;
   }
   const float ms = (m == kNegInf) ? 0.f : m;
-  float pr[2][4];
   float ps = 0.f;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pr[kt][j] = fast_exp2(x[kt][j] - ms);
-      ps += pr[kt][j];
-    }
+  for (int j = 0; j < 16; ++j) {
+    x[j] = fast_exp2(x[j] - ms);
+    ps += x[j];
+  }
   lsum += ps;
-  const uint4 pbu = make_uint4(pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
-                               pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3]));
-  const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbu);
-  // V^T operand: k-slot (g16, j) <-> key j<4 ? 4*g16+j : 16+4*g16+(j-4); column d.
-  const char* r0 = buf + (4 * g16) * kPitch + c16 * 2;
-  const char* r1 = buf + (16 + 4 * g16) * kPitch + c16 * 2;
+  // P^T operands: the 16 keys of key-half kh are this lane's accumulators 8kh..8kh+7.
+  // The weights enter the MFMA rounded to bf16; their rounded sum (lsr) is what
+  // O is normalised by, so the effective weights still sum to one.
+  bf16x8_t pb[2];
+  float pr = 0.f;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[q] = pack_bf16(x[8 * kh + 2 * q], x[8 * kh + 2 * q + 1]);
+      pr += bf16lo(w[q]) + bf16hi(w[q]);
+    }
+    pb[kh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+  }
+  lsr += pr;
+  // O^T += V^T . P^T.  V^T operand of depth tile dt, k-slot (g, j) of key-half kh:
+  // V[key = c32_row(8 kh + j, g)][d = 32 dt + c32], stored in column 4 dt + (c32 >> 3),
+  // byte 2 (c32 & 7) of the chunk at swizzled key (key & ~3) | ((key & 3) ^ (c32 >> 3)).
+  const int xs = c32 >> 3;
+  const char* vbase = buf + (xs * 32) * 16 + (c32 & 7) * 2 + g * 4 * 16;
+  const char* vr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) vr[r] = vbase + ((r ^ xs) * 16);
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) {
-    uint16_t e[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      e[j] = *(const uint16_t*)(r0 + j * kPitch + dt * 32);
-      e[4 + j] = *(const uint16_t*)(r1 + j * kPitch + dt * 32);
+    for (int kh = 0; kh < 2; ++kh) {
+      uint32_t e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key_hi = (2 * kh + j / 4) * 8;  // key & ~3, without the 4 g part
+        e[j] = *(const uint16_t*)(vr[j % 4] + dt * 4 * 32 * 16 + key_hi * 16);
+      }
+      const uint4 au = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16),
+                                  e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+      mfma_acc(acc[dt], __builtin_bit_cast(bf16x8_t, au), pb[kh]);
     }
-    const uint4 au = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                                e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
-    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, au), pb,
-                                                      acc[dt], 0, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeParams p, int n_mblocks,
-                                                              int n_work) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
   // XCD-aware decode of the block id: blocks i and i + 8 share an XCD; the
   // n_mblocks row blocks of one (partition, sequence) get ids 8 apart.
   const int id = blockIdx.x;
@@ -175,12 +251,12 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeParams p, in
   const int pidx = work / p.batch;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int c16 = lane & 15, g16 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c32 = lane & 31, g = lane >> 5;
   const int H = p.num_q_heads;
   const int nrows = p.q_len * H;
 
-  const int rr = mb * kRows + wave * 16 + c16;
+  const int rr = mb * kRows + wave * kWaveRows + c32;
   const bool row_ok = rr < nrows;
   const int tok = row_ok ? rr / H : 0;
   const int head = row_ok ? rr % H : 0;
@@ -194,76 +270,113 @@ __global__ __launch_bounds__(kThreads) void mla_decode_kernel(DecodeParams p, in
   const int hmin = max(k_lo, min(k_end, visible_keys(p, b, t_first)));
   const int hmax = max(k_lo, min(k_end, visible_keys(p, b, t_last)));
 
+  // Q^T operand: k-slot (g, j) of depth step st <-> depth 16*st + 8*g + j.
   bf16x8_t qf[kKS];
   const uint16_t* qrow =
       (const uint16_t*)p.q + (((size_t)b * p.q_len + tok) * H + head) * (size_t)kD;
 #pragma unroll
   for (int s = 0; s < kKS; ++s)
-    qf[s] = row_ok ? *(const bf16x8_t*)(qrow + s * 32 + g16 * 8) : bf16x8_t{};
+    qf[s] = row_ok ? *(const bf16x8_t*)(qrow + s * 16 + g * 8) : bf16x8_t{};
 
-  f32x4_t acc[kDT];
+  f32x16_t acc[kDT];
 #pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, lsum = 0.f;
+  for (int dt = 0; dt < kDT; ++dt) acc[dt] = f32x16_t{};
+  float m = kNegInf, lsum = 0.f, lsr = 0.f;  // exact and bf16-rounded weight sums
 
   const int n_full = (hmin - k_lo) / kBN;
   const int n_tot = (hmax - k_lo + kBN - 1) / kBN;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  // 3-stage ring: tile i lives in stage i % 3; tile i + 2 is requested while
+  // tile i is consumed.  Before each barrier a wave waits until at most the
+  // kDmaPerWave requests of tile i + 2 are outstanding, i.e. tile i + 1 landed.
+  __shared__ int restart_flag;
+  if (threadIdx.x == 0) restart_flag = 0;
   if (n_tot > 0) {
-    Stage st;
-    mla_load(p, st, b, k_lo, hmax);
-    mla_store(st, smem);
-    if (n_tot > 1) mla_load(p, st, b, k_lo + kBN, hmax);
-    __syncthreads();
-    for (int i = 0; i < n_tot; ++i) {
-      const char* cur = smem + (i & 1) * kTileBytes;
-      const int j0 = k_lo + i * kBN;
-      if (i < n_full)
-        mla_tile<false>(cur, qf, acc, m, lsum, j0, hi, p.scale_log2);
-      else
-        mla_tile<true>(cur, qf, acc, m, lsum, j0, hi, p.scale_log2);
-      if (i + 1 < n_tot) {
-        mla_store(st, smem + ((i + 1) & 1) * kTileBytes);
-        if (i + 2 < n_tot) mla_load(p, st, b, k_lo + (i + 2) * kBN, hmax);
+    wait_vm_lgkm0<0>();  // Q loads done: only DMA requests are counted below
+    for (;;) {  // one pass over the partition; repeated only after a restart
+      mla_issue(p, lds0, b, k_lo, hmax, wave, lane);
+      if (n_tot > 1) {
+        mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, lane);
+        wait_vm_lgkm0<kDmaPerWave>();
+      } else {
+        wait_vm_lgkm0<0>();
       }
+      __syncthreads();
+      int cur = 0;
+      for (int i = 0; i < n_tot; ++i) {
+        const bool ahead = i + 2 < n_tot;
+        if (ahead) {
+          const int nxt = (cur + 2 >= kStages) ? cur + 2 - kStages : cur + 2;
+          mla_issue(p, lds0 + nxt * kTileBytes, b, k_lo + (i + 2) * kBN, hmax, wave, lane);
+        }
+        mla_tile(smem + cur * kTileBytes, qf, acc, m, lsum, lsr, k_lo + i * kBN, i >= n_full,
+                 hi, p.scale_log2, &restart_flag);
+        if (ahead)
+          wait_vm_lgkm0<kDmaPerWave>();
+        else
+          wait_vm_lgkm0<0>();
+        __syncthreads();
+        if (restart_flag) break;  // same value in every wave (read after the barrier)
+        cur = (cur + 1 == kStages) ? 0 : cur + 1;
+      }
+      if (!restart_flag) break;
+      // Restart with the raised reference maxima: drop what was accumulated.
+      wait_vm_lgkm0<0>();
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) zero_acc(acc[dt], bf16x8_t{});
+      lsum = 0.f;
+      lsr = 0.f;
+      __syncthreads();
+      if (threadIdx.x == 0) restart_flag = 0;
+      wait_vm_lgkm0<0>();
       __syncthreads();
     }
   }
 
-  lsum += shfl_xor(lsum, 16);
+  mfma_settle(acc);
   lsum += shfl_xor(lsum, 32);
+  lsr += shfl_xor(lsr, 32);
   if (!row_ok) return;
   const size_t row = ((size_t)b * p.q_len + tok) * H + head;
+  // Lane holds O^T[d = 32*dt + 8*(j/4) + 4*g + j%4][row]: 4 consecutive d per j/4.
   if (p.write_partials) {
     const size_t prow = (size_t)pidx * ((size_t)p.batch * nrows) + row;
     const bool any = lsum > 0.f;
-    const float inv = any ? 1.f / lsum : 0.f;
+    const float inv = any ? 1.f / lsr : 0.f;
     float* dst = p.part_o + prow * kDv;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
-      *(float4*)(dst + dt * 16 + g16 * 4) =
-          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
-    if (g16 == 0) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(float4*)(dst + dt * 32 + q4 * 8 + g * 4) =
+            make_float4(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv,
+                        acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+    if (g == 0) {
       p.part_m[prow] = any ? m * kLn2 : kNegInf;
       p.part_l[prow] = lsum;
     }
   } else {
-    float M = m, L = lsum, c = 1.f;
+    float M = m, L = lsum, Lr = lsr, c = 1.f;
     if (p.sink) {
       const float sig = p.sink[head] * kLog2e;
       const float M2 = fmaxf(M, sig);
       c = fast_exp2(M - M2);
-      L = L * c + fast_exp2(sig - M2);
+      const float e = fast_exp2(sig - M2);
+      L = L * c + e;
+      Lr = Lr * c + e;
       M = M2;
     }
     const bool any = L > 0.f;
-    const float inv = any ? c / L : 0.f;
+    const float inv = any ? c / Lr : 0.f;
     uint16_t* dst = (uint16_t*)p.out + row * kDv;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
-      *(uint2*)(dst + dt * 16 + g16 * 4) =
-          make_uint2(pack_bf16(acc[dt][0] * inv, acc[dt][1] * inv),
-                     pack_bf16(acc[dt][2] * inv, acc[dt][3] * inv));
-    if (g16 == 0 && p.lse) p.lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(uint2*)(dst + dt * 32 + q4 * 8 + g * 4) =
+            make_uint2(pack_bf16(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv),
+                       pack_bf16(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv));
+    if (g == 0 && p.lse) p.lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
   }
 }
 

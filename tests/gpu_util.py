@@ -45,8 +45,13 @@ def run_oracle(wl: W.Workload, inp: W.Inputs, rows=None):
                        depth_v=wl.dv, max_seq_len=wl.max_seq_len, rows=rows)
 
 
-def compare(wl: W.Workload, out, lse, ref_out, ref_lse, rows=None, what=""):
-    """Element-by-element check of the HIP result against the oracle."""
+def compare(wl: W.Workload, out, lse, ref_out, ref_lse, rows=None, what="", ulp_rel=False):
+    """Element-by-element check of the HIP result against the oracle.
+
+    ulp_rel: add one bf16 ulp of |ref| (2^-8 |ref|) to the absolute bound, for
+    inputs built to give outputs far larger than N(0,1) data does (a bf16 output
+    of magnitude 8..16 is only resolved to 2^-4).
+    """
     torch.cuda.synchronize()
     got = DA.to_numpy_f64(out)
     gl = DA.to_numpy_f64(lse)
@@ -56,7 +61,10 @@ def compare(wl: W.Workload, out, lse, ref_out, ref_lse, rows=None, what=""):
         ref_out = ref_out.reshape(got.shape)
         ref_lse = ref_lse.reshape(gl.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
-    err = np.abs(got - ref_out).max() if got.size else 0.0
+    diff = np.abs(got - ref_out)
+    if ulp_rel:
+        diff = diff - np.abs(ref_out) * 2.0 ** -8
+    err = diff.max() if got.size else 0.0
     fin = np.isfinite(ref_lse)
     assert np.array_equal(np.isfinite(gl), fin), f"{what}: LSE finiteness differs"
     assert np.array_equal(gl[~fin], ref_lse[~fin]), f"{what}: LSE infinities differ"
@@ -69,7 +77,7 @@ def compare(wl: W.Workload, out, lse, ref_out, ref_lse, rows=None, what=""):
     return err, lerr
 
 
-def check(wl: W.Workload, num_partitions=None, inp=None, rows=None, what=None):
+def check(wl: W.Workload, num_partitions=None, inp=None, rows=None, what=None, ulp_rel=False):
     what = what or f"{wl.name} P={num_partitions if num_partitions is not None else 'auto'}"
     say(f"[gpu] {what}: B={wl.batch} T={wl.q_len} H={wl.num_heads} KVH={wl.kv_heads} "
         f"D={wl.depth} S={wl.max_seq_len} page={wl.page_size} dtype={wl.dtype}")
@@ -77,4 +85,4 @@ def check(wl: W.Workload, num_partitions=None, inp=None, rows=None, what=None):
     dev = device_inputs(inp)
     out, lse = run_gpu(wl, dev, num_partitions)
     ref_out, ref_lse = run_oracle(wl, inp, rows)
-    return compare(wl, out, lse, ref_out, ref_lse, rows=rows, what=what)
+    return compare(wl, out, lse, ref_out, ref_lse, rows=rows, what=what, ulp_rel=ulp_rel)

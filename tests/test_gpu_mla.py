@@ -1,0 +1,77 @@
+"""GPU parity: mla_decode() through the C ABI against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import check
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(wl, n, seed):
+    rng = np.random.default_rng(seed)
+    total = wl.batch * wl.q_len * wl.num_heads
+    return np.sort(rng.choice(total, size=min(n, total), replace=False)).astype(np.int64)
+
+
+# ---- the MLA problem at full size (sampled rows: every row is 8192 keys x 1088 MACs) --
+
+@pytest.mark.parametrize("P", [0, 1])
+def test_mla_full_sampled(P):
+    check(W.MLA, num_partitions=P, rows=_sample_rows(W.MLA, 768, 1))
+
+
+def test_mla_mtp_full_sampled():
+    check(W.MLA_MTP, num_partitions=0, rows=_sample_rows(W.MLA_MTP, 768, 2))
+
+
+# ---- small MLA shapes: every row compared ----------------------------------------
+
+SMALL = [
+    # (B, T, H, S, page, causal, ragged)
+    (2, 1, 128, 300, 0, False, False),
+    (3, 1, 16, 97, 0, False, True),          # 16 heads: one partly filled row block
+    (2, 2, 128, 200, 64, True, True),        # MTP fold: two row blocks of 128
+    (2, 3, 64, 150, 32, True, True),         # 3 tokens x 64 heads = 192 rows
+    (1, 1, 160, 64, 0, False, False),        # 160 rows: second block 32 rows
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("P", [1, 3])
+def test_mla_small(shape, P):
+    B, T, H, S, page, causal, ragged = shape
+    wl = W.Workload(f"mla_small_{'x'.join(map(str, shape))}", 9200 + S + T, batch=B,
+                    num_heads=H, kv_heads=1, depth=576, depth_v=512, max_seq_len=S, q_len=T,
+                    mla=True, causal=causal, page_size=page,
+                    ragged=(1, S, 1) if ragged else None, scale=1.0 / np.sqrt(192.0),
+                    sink=(P == 3))
+    check(wl, num_partitions=P)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 33])
+def test_mla_mtp_causal_short(n):
+    """Two MTP tokens over a handful of keys: the causal mask moves the result by O(1)."""
+    wl = W.Workload(f"mla_mtp_short_{n}", 9300 + n, batch=2, num_heads=128, kv_heads=1,
+                    depth=576, depth_v=512, max_seq_len=64, q_len=2, mla=True, causal=True,
+                    scale=1.0 / np.sqrt(192.0))
+    inp = W.make_inputs(wl, poison=False)
+    inp.valid_length = np.array([n, max(1, n - 1)], np.uint32)
+    check(wl, num_partitions=1, inp=inp, what=f"mla mtp causal N={n}")
+
+
+def test_mla_score_jump_restart():
+    """Keys whose scores exceed the first tile's by ~900 (log2 units) force the
+    fixed-reference kernel to restart its partition; the result must not change."""
+    wl = W.Workload("mla_jump", 9400, batch=2, num_heads=128, kv_heads=1, depth=576,
+                    depth_v=512, max_seq_len=256, mla=True, scale=1.0 / np.sqrt(192.0))
+    inp = W.make_inputs(wl, poison=False)
+    q = W.bf16_bits_to_f32(inp.q)
+    for b, (j1, j2) in enumerate([(70, 200), (40, 250)]):
+        sgn = np.sign(q[b, 0, 0]).astype(np.float32)
+        inp.k[b, j1, 0] = W.f32_to_bf16_bits(sgn * 6.0)     # large aligned key
+        inp.k[b, j2, 0] = W.f32_to_bf16_bits(sgn * 12.0)    # larger still, later
+    # |out| reaches 12 here (V rows of +-6 / +-12), beyond the N(0,1) regime of
+    # the 1e-2 absolute bound: allow one bf16 ulp of the reference on top.
+    for P in (1, 2):
+        check(wl, num_partitions=P, inp=inp, what=f"mla score jump P={P}", ulp_rel=True)

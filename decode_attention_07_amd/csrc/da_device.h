@@ -61,6 +61,37 @@ __device__ __forceinline__ float sum8(float x) {
 
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// max(x, x of lane ^ 32) with v_permlane32_swap (a VALU op: no LDS round trip).
+// The swap of (x, x) leaves the low half of x in both halves of one result and
+// the high half in both halves of the other.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8 bytes addressed by lane
+// 4 j + i / 4, for j = 0..3.  So if lane s of the group addresses
+// &X[k0 + s / 4][n0 + 4 (s % 4)] of a row-major bf16 matrix X, lane i receives
+// the column X[k0 .. k0 + 3][n0 + i]: half of an MFMA operand whose k index runs
+// down the rows of X.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  typedef short s4_t __attribute__((ext_vector_type(4)));
+  const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ bf16x8_t concat_bf16x8(uint2 lo, uint2 hi) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 __device__ __forceinline__ int wave_id_uniform() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

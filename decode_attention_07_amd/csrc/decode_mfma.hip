@@ -40,7 +40,9 @@ struct MfmaCfg {
   static constexpr int CHUNKS = D * 2 / 16;         // 16-byte chunks per key row
   static constexpr int VLOADS = kTile * CHUNKS / 64;  // 16-byte V loads per lane per tile
   static constexpr int KEYS_PER_VLOAD = 64 / CHUNKS;
-  static constexpr int PITCH = D * 2 + 8;           // LDS bytes per V row (bank spread)
+  // LDS bytes per V row: 32 bytes past a multiple of 128, so the 4 rows x 32
+  // bytes that one 16-lane transposing read touches fall in different banks
+  static constexpr int PITCH = D * 2 + 32;
   static constexpr int VBUF = kTile * PITCH;        // LDS bytes per wave tile
   static constexpr int MERGE = kWaves * 16 * (D + 3) * 4;
   static constexpr int SMEM = (kWaves * VBUF > MERGE) ? kWaves * VBUF : MERGE;
@@ -167,22 +169,16 @@ __device__ __forceinline__ void mfma_process(const MfmaTile<D>& t, const bf16x8_
                        (bf16lo(pb2) + bf16hi(pb2)) + (bf16lo(pb3) + bf16hi(pb3)));
   const uint4 pbu = make_uint4(pb0, pb1, pb2, pb3);
   const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pbu);
-  // O^T += V^T . P^T; V^T operand read from LDS by column (same k-slot order).
-  const char* r0 = vl + (4 * g16) * C::PITCH;
-  const char* r1 = vl + (16 + 4 * g16) * C::PITCH;
+  // O^T += V^T . P^T.  V^T operand of depth tile dt: slots 0..3 hold keys
+  // 4 g16 + 0..3, slots 4..7 keys 16 + 4 g16 + 0..3 (the P^T slot order), at
+  // d = 16 dt + c16.  Each half is one transposing read: lane c16 supplies
+  // &V[4 g16 + c16 / 4][16 dt + 4 (c16 % 4)] (row-major tile, padded pitch).
+  const char* vt = vl + (4 * g16 + (c16 >> 2)) * C::PITCH + (c16 & 3) * 8;
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) {
-    const int col = (dt * 16 + c16) * 2;
-    uint16_t e[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      e[j] = *(const uint16_t*)(r0 + j * C::PITCH + col);
-      e[4 + j] = *(const uint16_t*)(r1 + j * C::PITCH + col);
-    }
-    const uint4 au = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                                e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
-    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, au), pb,
-                                                      acc[dt], 0, 0, 0);
+    const char* a = vt + dt * 32;
+    const bf16x8_t av = concat_bf16x8(lds_read_tr16(a), lds_read_tr16(a + 16 * C::PITCH));
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, acc[dt], 0, 0, 0);
   }
 }
 

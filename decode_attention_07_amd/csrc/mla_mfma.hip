@@ -7,8 +7,8 @@
 // those rows (4 waves x 32 rows, one wave per SIMD) and one partition of the
 // keys, so every cache row of the partition is read from HBM once per 128 rows.
 //
-// Per 32-key tile, shared by the block through a 3-stage LDS ring filled by
-// direct global->LDS loads (no staging registers; two tiles in flight):
+// Per 32-key tile, shared by the block through a 4-stage LDS ring filled by
+// direct global->LDS loads (no staging registers; three tiles in flight):
 //   S^T[32 keys x 32 rows] = K[32 x 576] . Q^T[576 x 32]    36 v_mfma_f32_32x32x16_bf16
 //       A = K from LDS, B = the wave's Q^T kept in registers for the whole
 //       kernel (144 VGPRs).
@@ -25,10 +25,11 @@
 //       from the S^T accumulators (bf16); O^T lives in the 256 accumulation
 //       registers.
 // LDS tile layout: column-major in 16-byte chunks with an XOR swizzle,
-//   chunk(key, col) = col * 32 + (key ^ (col & 3)),  col = 16-byte column 0..71,
-// so one 1 KB DMA instruction fills two columns of all 32 keys, the K-operand
-// reads of a half wave cover 512 contiguous bytes, and the V^T column reads of
-// a wave fall in 16 distinct bank groups.
+//   chunk(key, col) = col * 32 + (key ^ (4 * (col & 1))),  col = 16-byte column 0..71,
+// so one 1 KB DMA instruction fills two columns of all 32 keys, any 8
+// consecutive keys of a column sit in 8 different 16-byte bank groups (the K
+// operand reads), and so do the 4 keys x 2 adjacent columns that one 16-lane
+// transposing read of the V^T operand touches.
 // With two tokens (256 rows) a sequence needs two blocks that read the same
 // tiles; their block ids differ by a multiple of 8 so that both land on the same
 // XCD and the second read of each tile is served by that XCD's L2.
@@ -52,7 +53,7 @@ constexpr int kCols = kRowBytes / 16;        // 72 columns of 16 bytes
 constexpr int kTileBytes = kCols * kBN * 16; // 36 KB
 constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // 9
 static_assert(kDmaPerWave * kWaves * 1024 == kTileBytes, "tile must split into 1 KB pieces");
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr float kHeadroom = 100.0f;          // largest exp2 argument (log2 units)
 
 // 16 bytes per lane from global memory straight into LDS (gfx950
@@ -75,7 +76,7 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 
 // Requests the 32-key tile starting at key j0 into one LDS stage.  Instruction n
 // (n = wave + 4 i) fills columns 2n and 2n + 1; lane l of it takes column
-// 2n + (l >> 5) of key (l & 31) ^ (column & 3), which keeps the column-major
+// 2n + (l >> 5) of key (l & 31) ^ (4 (l >> 5)), which keeps the column-major
 // swizzled layout.  Keys at or past `kend` fetch row 0 of the tile instead
 // (finite data; those keys are masked out of the softmax), so every wave
 // issues exactly kDmaPerWave instructions.
@@ -90,7 +91,7 @@ __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage,
   }
   const int g = lane >> 5;
   const int col0 = 2 * wave + g;               // column of instruction i is col0 + 8 i
-  const int key = (lane & 31) ^ (col0 & 3);    // (col0 + 8 i) & 3 == col0 & 3
+  const int key = (lane & 31) ^ (4 * g);       // column parity is g
   const bool real = j0 + key < kend;
   const char* src =
       (const char*)p.k + row0 * kRowBytes + (real ? key * kRowBytes : 0) + col0 * 16;
@@ -107,11 +108,15 @@ __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage,
 // before the MFMA, and mfma_settle() before any VALU or accvgpr read of a
 // result.
 //
-// acc += A . B, acc in AGPRs.
+// acc += A . B, acc in AGPRs.  NOP: a VALU may have written A or B just before.
+template <bool NOP>
 __device__ __forceinline__ void mfma_acc(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-               : "+a"(acc)
-               : "v"(a), "v"(b));
+  if (NOP)
+    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+a"(acc)
+                 : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Score tile s (= / +=) A . B with s in arch VGPRs (the AGPRs hold O^T).  The
@@ -149,24 +154,52 @@ __device__ __forceinline__ constexpr int c32_row(int j, int g) {
 __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[kKS],
                                          f32x16_t (&acc)[kDT], float& m, float& lsum, float& lsr,
                                          int j0,
-                                         bool masked, int hi, float scale_log2, int* restart) {
+                                         bool masked, int hi, float scale_log2, bool& restart) {
   const int lane = threadIdx.x & 63;
   const int c32 = lane & 31, g = lane >> 5;
-  // S^T = K . Q^T; the A operand of depth step st is column 2 st + g of key c32.
+  // S^T = K . Q^T; the A operand of depth step st is column 2 st + g of key c32
+  // (column parity g).  Two accumulation chains (even / odd st); the K fragments
+  // come from a ring kPf pairs deep so that their LDS latency hides behind the
+  // MFMAs in flight.
   f32x16_t s0, s1;
-  const char* ka = buf + (g * 32 + (c32 ^ g)) * 16;        // even st: col & 3 = g
-  const char* kb = buf + (g * 32 + (c32 ^ (2 + g))) * 16;  // odd st:  col & 3 = 2 + g
+  const char* ka = buf + (g * 32 + (c32 ^ (4 * g))) * 16;
+  const char* kb = ka;
+  constexpr int kPairs = kKS / 2;
+  constexpr int kPf = 4;
+  bf16x8_t ra[kPf], rb[kPf];
 #pragma unroll
-  for (int st = 0; st < kKS; st += 2) {
-    const bf16x8_t a0 = *(const bf16x8_t*)(ka + st * 1024);
-    const bf16x8_t a1 = *(const bf16x8_t*)(kb + (st + 1) * 1024);
-    if (st == 0) {
-      mfma_v_first(s0, a0, qf[st]);
-      mfma_v_first(s1, a1, qf[st + 1]);
+  for (int q = 0; q < kPf; ++q) {
+    ra[q] = *(const bf16x8_t*)(ka + (2 * q) * 1024);
+    rb[q] = *(const bf16x8_t*)(kb + (2 * q + 1) * 1024);
+  }
+#pragma unroll
+  for (int pq = 0; pq < kPairs; ++pq) {
+    const int slot = pq % kPf;
+    if (pq == 0) {
+      mfma_v_first(s0, ra[slot], qf[0]);
+      mfma_v_first(s1, rb[slot], qf[1]);
     } else {
-      mfma_v(s0, a0, qf[st]);
-      mfma_v(s1, a1, qf[st + 1]);
+      mfma_v(s0, ra[slot], qf[2 * pq]);
+      mfma_v(s1, rb[slot], qf[2 * pq + 1]);
     }
+    if (pq + kPf < kPairs) {
+      ra[slot] = *(const bf16x8_t*)(ka + (2 * (pq + kPf)) * 1024);
+      rb[slot] = *(const bf16x8_t*)(kb + (2 * (pq + kPf) + 1) * 1024);
+    }
+  }
+  // V^T operand addresses (see below); the first kPf fragments are requested
+  // now so that they arrive while the softmax runs.
+  const int G = lane >> 4, i16 = lane & 15;
+  const int cl = 2 * (G & 1) + ((i16 & 3) >> 1);
+  const char* vt =
+      buf + cl * 512 + 64 * (g ^ (cl & 1)) + (i16 >> 2) * 16 + 8 * (i16 & 1);
+  constexpr int kFrags = kDT * 2;  // fragment f = (dt = f / 2, kh = f % 2)
+  uint2 vlo[kPf], vhi[kPf];
+#pragma unroll
+  for (int f = 0; f < kPf; ++f) {
+    const char* a = vt + (f / 2) * 2048 + (f % 2) * 256;
+    vlo[f] = lds_read_tr16(a);
+    vhi[f] = lds_read_tr16(a + 128);
   }
   mfma_settle(s0, s1);
   float x[16];
@@ -178,13 +211,13 @@ __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[k
     x[j] = v;
     mx = fmaxf(mx, v);
   }
-  mx = fmaxf(mx, shfl_xor(mx, 32));
+  mx = max_xor32(mx);
   // Fixed reference per row: exp2 arguments may reach kHeadroom; a row whose
   // tile max exceeds it raises the block's restart flag (the partition is then
   // recomputed from its first key with the larger reference).
   const bool grow = mx > m + kHeadroom;
   if (grow) {
-    if (m != kNegInf) *restart = 1;  // first visible tile of a row: acc is still 0, no restart
+    if (m != kNegInf) restart = true;  // first visible tile of a row: acc is still 0
     m = mx;
   }
   const float ms = (m == kNegInf) ? 0.f : m;
@@ -211,27 +244,25 @@ __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[k
     pb[kh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
   }
   lsr += pr;
-  // O^T += V^T . P^T.  V^T operand of depth tile dt, k-slot (g, j) of key-half kh:
-  // V[key = c32_row(8 kh + j, g)][d = 32 dt + c32], stored in column 4 dt + (c32 >> 3),
-  // byte 2 (c32 & 7) of the chunk at swizzled key (key & ~3) | ((key & 3) ^ (c32 >> 3)).
-  const int xs = c32 >> 3;
-  const char* vbase = buf + (xs * 32) * 16 + (c32 & 7) * 2 + g * 4 * 16;
-  const char* vr[4];
+  // O^T += V^T . P^T.  V^T operand of depth tile dt, key-half kh: slots 0..3 hold
+  // keys 16 kh + 4 g + 0..3 and slots 4..7 keys 16 kh + 8 + 4 g + 0..3 (the P^T
+  // slot order), at d = 32 dt + (lane % 32).  Each half is one transposing read:
+  // lane i of 16-lane group G supplies &V[16 kh + 4 g + i / 4][32 dt + 16 (G % 2) +
+  // 4 (i % 4)], i.e. column 4 dt + cl, byte 8 (i % 2) of the chunk of that key,
+  // with cl = 2 (G % 2) + (i % 4) / 2 and the swizzle key ^ (4 (cl & 1)).
 #pragma unroll
-  for (int r = 0; r < 4; ++r) vr[r] = vbase + ((r ^ xs) * 16);
-#pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      uint32_t e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key_hi = (2 * kh + j / 4) * 8;  // key & ~3, without the 4 g part
-        e[j] = *(const uint16_t*)(vr[j % 4] + dt * 4 * 32 * 16 + key_hi * 16);
-      }
-      const uint4 au = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16),
-                                  e[4] | (e[5] << 16), e[6] | (e[7] << 16));
-      mfma_acc(acc[dt], __builtin_bit_cast(bf16x8_t, au), pb[kh]);
+  for (int f = 0; f < kFrags; ++f) {
+    const int slot = f % kPf;
+    // the P^T operands were just written by VALU ops: only the first two MFMAs
+    // (one per key half) can be within reach of that hazard
+    if (f < 2)
+      mfma_acc<true>(acc[f / 2], concat_bf16x8(vlo[slot], vhi[slot]), pb[f % 2]);
+    else
+      mfma_acc<false>(acc[f / 2], concat_bf16x8(vlo[slot], vhi[slot]), pb[f % 2]);
+    if (f + kPf < kFrags) {
+      const char* a = vt + ((f + kPf) / 2) * 2048 + ((f + kPf) % 2) * 256;
+      vlo[slot] = lds_read_tr16(a);
+      vhi[slot] = lds_read_tr16(a + 128);
     }
   }
 }
@@ -286,16 +317,24 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   const int n_full = (hmin - k_lo) / kBN;
   const int n_tot = (hmax - k_lo + kBN - 1) / kBN;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  // 3-stage ring: tile i lives in stage i % 3; tile i + 2 is requested while
-  // tile i is consumed.  Before each barrier a wave waits until at most the
-  // kDmaPerWave requests of tile i + 2 are outstanding, i.e. tile i + 1 landed.
-  __shared__ int restart_flag;
-  if (threadIdx.x == 0) restart_flag = 0;
+  // 4-stage ring: tile i lives in stage i % 4; tile i + 3 is requested while
+  // tile i is consumed.  Before each barrier a wave waits until only the
+  // requests of tiles i + 2 and i + 3 are outstanding, i.e. tile i + 1 landed.
+  // Restart votes: each wave writes its own slot for tile i (every tile, 0 or 1)
+  // into buffer i & 1 before the tile's barrier; the slots of tile i - 1 are
+  // read at the top of tile i, so a read and the next write of the same buffer
+  // (tile i + 1) are always a barrier apart and every wave sees the same votes.
+  __shared__ __attribute__((aligned(16))) int votes[2][kWaves];
   if (n_tot > 0) {
     wait_vm_lgkm0<0>();  // Q loads done: only DMA requests are counted below
     for (;;) {  // one pass over the partition; repeated only after a restart
+      // tiles 0, 1, 2 requested; wait for tile 0
       mla_issue(p, lds0, b, k_lo, hmax, wave, lane);
-      if (n_tot > 1) {
+      if (n_tot > 2) {
+        mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, lane);
+        mla_issue(p, lds0 + 2 * kTileBytes, b, k_lo + 2 * kBN, hmax, wave, lane);
+        wait_vm_lgkm0<2 * kDmaPerWave>();
+      } else if (n_tot > 1) {
         mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, lane);
         wait_vm_lgkm0<kDmaPerWave>();
       } else {
@@ -303,39 +342,52 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       }
       __syncthreads();
       int cur = 0;
+      bool again = false;
       for (int i = 0; i < n_tot; ++i) {
-        const bool ahead = i + 2 < n_tot;
-        if (ahead) {
-          const int nxt = (cur + 2 >= kStages) ? cur + 2 - kStages : cur + 2;
-          mla_issue(p, lds0 + nxt * kTileBytes, b, k_lo + (i + 2) * kBN, hmax, wave, lane);
+        // Votes of tile i - 1, acted upon after tile i (the load has landed by
+        // then; what tile i adds is dropped with the rest on a restart).
+        int4 prev = make_int4(0, 0, 0, 0);
+        if (i > 0) prev = *(const int4*)votes[(i - 1) & 1];
+        const bool ahead = i + 3 < n_tot;
+        if (ahead) {  // stage of tile i + 3 was last read by tile i - 1, a barrier ago
+          const int nxt = (cur + 3 >= kStages) ? cur + 3 - kStages : cur + 3;
+          mla_issue(p, lds0 + nxt * kTileBytes, b, k_lo + (i + 3) * kBN, hmax, wave, lane);
         }
+        bool need = false;
         mla_tile(smem + cur * kTileBytes, qf, acc, m, lsum, lsr, k_lo + i * kBN, i >= n_full,
-                 hi, p.scale_log2, &restart_flag);
+                 hi, p.scale_log2, need);
+        if (lane == 0) votes[i & 1][wave] = __builtin_amdgcn_ballot_w64(need) != 0;
+        // tile i + 1 must have landed: tiles i + 2 and i + 3 may stay in flight
         if (ahead)
+          wait_vm_lgkm0<2 * kDmaPerWave>();
+        else if (i + 2 < n_tot)
           wait_vm_lgkm0<kDmaPerWave>();
         else
           wait_vm_lgkm0<0>();
         __syncthreads();
-        if (restart_flag) break;  // same value in every wave (read after the barrier)
+        if (prev.x | prev.y | prev.z | prev.w) {  // same votes in every wave
+          again = true;
+          break;
+        }
         cur = (cur + 1 == kStages) ? 0 : cur + 1;
       }
-      if (!restart_flag) break;
+      if (!again) {  // the last tile's votes have not been looked at yet
+        const int4 last = *(const int4*)votes[(n_tot - 1) & 1];
+        if (!(last.x | last.y | last.z | last.w)) break;
+      }
       // Restart with the raised reference maxima: drop what was accumulated.
       wait_vm_lgkm0<0>();
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) zero_acc(acc[dt], bf16x8_t{});
       lsum = 0.f;
       lsr = 0.f;
-      __syncthreads();
-      if (threadIdx.x == 0) restart_flag = 0;
-      wait_vm_lgkm0<0>();
-      __syncthreads();
+      __syncthreads();  // every wave has read the votes before the next pass writes them
     }
   }
 
   mfma_settle(acc);
-  lsum += shfl_xor(lsum, 32);
-  lsr += shfl_xor(lsr, 32);
+  lsum = sum_xor32(lsum);
+  lsr = sum_xor32(lsr);
   if (!row_ok) return;
   const size_t row = ((size_t)b * p.q_len + tok) * H + head;
   // Lane holds O^T[d = 32*dt + 8*(j/4) + 4*g + j%4][row]: 4 consecutive d per j/4.

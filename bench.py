@@ -124,7 +124,8 @@ def main():
     kv_bytes = footprint
     S = wl.max_seq_len
     B, T, H = wl.batch, wl.q_len, wl.num_heads
-    P = args.partitions or DA.num_partitions(B, T, H, wl.kv_heads, wl.depth, wl.dv, S)
+    P = args.partitions or DA.num_partitions(B, T, H, wl.kv_heads, wl.depth, wl.dv, S,
+                                             ragged=first.valid_length is not None)
     split = P > 1
     ws = torch.empty(DA.decode_workspace_size(P, B, T, H, wl.dv), dtype=torch.uint8,
                      device="cuda")

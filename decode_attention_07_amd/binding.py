@@ -41,7 +41,7 @@ def _declare(lib):
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.decode_attention_status_string.argtypes = [i32]
     lib.decode_attention_status_string.restype = ctypes.c_char_p
-    lib.decode_num_partitions.argtypes = [i32] * 8
+    lib.decode_num_partitions.argtypes = [i32] * 9
     lib.decode_num_partitions.restype = i32
     for name in ("decode_workspace_size", "decode_workspace_max_offset",
                  "decode_workspace_sum_offset"):
@@ -120,9 +120,9 @@ _U32 = (torch.int32, torch.uint32)
 
 
 def num_partitions(batch, q_len, num_q_heads, num_kv_heads, depth, depth_v, max_seq_len,
-                   num_cus=0) -> int:
+                   ragged=False, num_cus=0) -> int:
     p = library().decode_num_partitions(batch, q_len, num_q_heads, num_kv_heads, depth, depth_v,
-                                        max_seq_len, num_cus)
+                                        max_seq_len, int(bool(ragged)), num_cus)
     if p < 1:
         raise DecodeAttentionError(p, "decode_num_partitions")
     return p
@@ -165,9 +165,9 @@ def _cache_geometry(q, k, page_table, max_seq_len):
     return page_size, max_pages, S
 
 
-def _resolve_partitions(num_parts, batch, T, H, KVH, D, Dv, S):
+def _resolve_partitions(num_parts, batch, T, H, KVH, D, Dv, S, ragged):
     if num_parts is None or num_parts == 0:
-        return num_partitions(batch, T, H, KVH, D, Dv, S)
+        return num_partitions(batch, T, H, KVH, D, Dv, S, ragged)
     return int(num_parts)
 
 
@@ -198,7 +198,8 @@ def decode_attention(q, k, v, *, group, scale, page_table=None, valid_length=Non
     if k.shape[3] != D or v.shape[3] != D or k.shape[2] * group != H:
         raise ValueError("k/v shape does not match q and group")
     page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len)
-    P = _resolve_partitions(num_partitions, B, T, H, H // group, D, D, S)
+    P = _resolve_partitions(num_partitions, B, T, H, H // group, D, D, S,
+                            valid_length is not None)
     if out is None:
         out = torch.empty((B, T, H, D), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
@@ -246,7 +247,8 @@ def mla_decode(q, kv, *, scale, page_table=None, valid_length=None, max_seq_len=
     if D != MLA_DEPTH or kv.shape[3] != MLA_DEPTH or kv.shape[2] != 1:
         raise ValueError("MLA needs q [..., 576] and kv [..., 1, 576]")
     page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len)
-    P = _resolve_partitions(num_partitions, B, T, H, 1, MLA_DEPTH, MLA_DEPTH_V, S)
+    P = _resolve_partitions(num_partitions, B, T, H, 1, MLA_DEPTH, MLA_DEPTH_V, S,
+                            valid_length is not None)
     if out is None:
         out = torch.empty((B, T, H, MLA_DEPTH_V), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:

@@ -19,6 +19,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 instructions stay off (some of their forms are not trusted)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
+# Per-source additions.  The streaming kernel rescales its MFMA accumulators
+# with vector ops: the VGPR form of the MFMAs keeps them out of the
+# accumulation registers and saves a copy in each direction per tile.
+EXTRA = {"decode_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():
@@ -28,7 +32,8 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-x", "hip", "-c", src, "-o",
+           obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

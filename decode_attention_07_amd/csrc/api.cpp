@@ -16,12 +16,12 @@
 #include "da_params.h"
 
 namespace da {
-hipError_t launch_decode_valu(const DecodeParams& p, bool bf16, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeParams& p, hipStream_t s);
 int valu_step_keys(int rows_per_block);
 int valu_rows_per_block(int fold);
-hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s);
-int mfma_step_keys();
-int mfma_rows_per_block();
+hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s);
+int stream_step_keys();
+int stream_rows_per_block();
 hipError_t launch_mla(const DecodeParams& p, hipStream_t s);
 int mla_step_keys(int q_len);
 int mla_rows_per_block(int q_len, int num_q_heads);
@@ -36,7 +36,6 @@ namespace {
 constexpr int kMlaDepth = 576;
 constexpr int kMlaDepthV = 512;
 constexpr size_t kAlign = 256;
-constexpr bool kMfmaReady = true;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -72,7 +71,8 @@ int log2i(int x) {
 }
 
 // Which partition kernel runs, and its tiling.
-enum Variant { kValu = 0, kMfma = 1, kMla = 2 };
+enum Variant { kValu = 0, kStream = 1, kMla = 2 };
+
 
 struct Plan {
   Variant variant;
@@ -84,10 +84,10 @@ struct Plan {
 Plan plan_mha(int q_len, int group, bool bf16) {
   const int fold = q_len * group;
   Plan pl;
-  if (kMfmaReady && bf16 && fold >= 8) {
-    pl.variant = kMfma;
-    pl.rows_per_block = da::mfma_rows_per_block();
-    pl.step = da::mfma_step_keys();
+  if (bf16) {  // streaming matrix-core kernel; fp32 runs on the vector ALUs
+    pl.variant = kStream;
+    pl.rows_per_block = da::stream_rows_per_block();
+    pl.step = da::stream_step_keys();
   } else {
     pl.variant = kValu;
     pl.rows_per_block = da::valu_rows_per_block(fold < 8 ? fold : 8);
@@ -181,14 +181,18 @@ void ws_sections(void* ws, int P, size_t rows, int depth_v, float** po, float** 
 hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16,
                                  hipStream_t s) {
   switch (v) {
-    case kValu: return da::launch_decode_valu(p, bf16, s);
-    case kMfma: return da::launch_decode_mfma(p, s);
+    case kValu: return da::launch_decode_valu(p, s);
+    case kStream: return da::launch_decode_stream(p, s);
     default: return da::launch_mla(p, s);
   }
 }
 
 const char* variant_name(Variant v) {
-  return v == kValu ? "valu" : (v == kMfma ? "mfma" : "mla");
+  switch (v) {
+    case kValu: return "valu";
+    case kStream: return "stream";
+    default: return "mla";
+  }
 }
 
 // Shared driver of decode_attention / mla_decode (and their partial passes).
@@ -200,7 +204,7 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
   int P = num_partitions;
   if (P == 0) {
     P = decode_num_partitions(c.batch, c.q_len, c.num_q_heads, p.num_kv_heads, p.depth,
-                              p.depth_v, c.max_seq_len, 0);
+                              p.depth_v, c.max_seq_len, c.valid_length != nullptr, 0);
     if (P < 1) return P;
   }
   if (P < 1 || P > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
@@ -275,19 +279,23 @@ const char* decode_attention_status_string(int status) {
 }
 
 int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_heads, int depth,
-                          int depth_v, int max_seq_len, int num_cus) {
+                          int depth_v, int max_seq_len, int ragged, int num_cus) {
   if (batch < 1 || q_len < 1 || num_q_heads < 1 || num_kv_heads < 1 || depth < 1 ||
       depth_v < 1 || max_seq_len < 0 || num_q_heads % num_kv_heads != 0)
     return DA_ERR_INVALID_ARG;
   if (num_cus <= 0) num_cus = device_cus();
+  // The bf16 kernels keep one block per CU resident (their LDS rings take most
+  // of the CU's LDS), so a dense batch wants about one block per CU; a ragged
+  // one wants smaller partitions so that its long sequences spread out.
+  const int per_cu = ragged ? 8 : 1;
   if (depth == kMlaDepth && num_kv_heads == 1) {
     const Plan pl = plan_mla(q_len, num_q_heads);
     // MLA partials are 512 wide per row: keep partitions long so the partial
     // write-back stays a small fraction of the cache read.
-    return heuristic_partitions(batch * pl.row_blocks, max_seq_len, num_cus, 1, 1024);
+    return heuristic_partitions(batch * pl.row_blocks, max_seq_len, num_cus, per_cu, 1024);
   }
   const Plan pl = plan_mha(q_len, num_q_heads / num_kv_heads, true);
-  return heuristic_partitions(batch * num_kv_heads * pl.row_blocks, max_seq_len, num_cus, 4,
+  return heuristic_partitions(batch * num_kv_heads * pl.row_blocks, max_seq_len, num_cus, per_cu,
                               256);
 }
 

@@ -1,7 +1,8 @@
 // decode_valu.hip -- split-K decode attention on the vector ALUs (gfx950).
 //
-// Used for small head folds (fewer than 8 query rows per KV head) and for fp32
-// inputs, where the fold is too thin for a matrix-core contraction.  One block
+// Used for fp32 inputs, which have no matrix-core path at this precision here
+// (bf16 runs the streaming matrix-core kernel).  The element type stays a
+// template parameter; only fp32 is instantiated.  One block
 // of 4 waves handles one (partition, batch, KV head, row block): every query
 // row that shares the KV head is folded into the block, so each KV byte of the
 // partition is read from HBM exactly once.
@@ -383,13 +384,10 @@ static hipError_t launch_valu_d(const DecodeParams& p, int R, int grid, hipStrea
 int valu_step_keys(int rows_per_block) { return 32 * ((rows_per_block <= 4) ? 2 : 1); }
 int valu_rows_per_block(int fold) { return valu_rows_bucket(fold); }
 
-hipError_t launch_decode_valu(const DecodeParams& p, bool bf16, hipStream_t s) {
+// fp32 inputs (bf16 runs the streaming matrix-core kernel).
+hipError_t launch_decode_valu(const DecodeParams& p, hipStream_t s) {
   const int R = valu_rows_bucket(fold_rows(p));
   const int grid = p.num_partitions * p.batch * p.num_kv_heads * p.row_blocks;
-  if (bf16) {
-    if (p.depth == 64) return launch_valu_d<true, 64>(p, R, grid, s);
-    return launch_valu_d<true, 128>(p, R, grid, s);
-  }
   if (p.depth == 64) return launch_valu_d<false, 64>(p, R, grid, s);
   return launch_valu_d<false, 128>(p, R, grid, s);
 }

@@ -81,13 +81,17 @@ const char* decode_attention_status_string(int status);
  * `num_partitions_override`: 0 selects the automatic ladder;
  * "flare_mla_decoding_dispatch", Args `num_partitions`: None selects via
  * heuristic).  Picks P >= 1 so that the grid of (batch x KV head x row block x
- * partition) blocks fills `num_cus` compute units while each partition keeps
- * enough keys to amortise its prologue and its partial write-back.
- * num_cus <= 0 queries the current device.  MLA calls pass num_kv_heads = 1,
- * depth = 576, depth_v = 512.  Returns P, or a negative status.
+ * partition) blocks fills `num_cus` compute units (one resident block per CU
+ * for the bf16 kernels) while each partition keeps enough keys to amortise its
+ * prologue and its partial write-back.  ragged != 0 (a valid_length array will
+ * be passed) asks for about 8 blocks per CU instead, so that the long
+ * sequences of a mixed batch are spread over many CUs.  num_cus <= 0 queries
+ * the current device.  MLA calls pass num_kv_heads = 1, depth = 576,
+ * depth_v = 512.  decode_attention() / mla_decode() with num_partitions = 0 use
+ * this with ragged = (valid_length != NULL).  Returns P, or a negative status.
  */
 int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_heads, int depth,
-                          int depth_v, int max_seq_len, int num_cus);
+                          int depth_v, int max_seq_len, int ragged, int num_cus);
 
 /*
  * Bytes of the split-K workspace for `num_partitions` partitions.  A
@@ -122,7 +126,8 @@ size_t decode_workspace_sum_offset(int num_partitions, int batch, int q_len, int
  *                   Args `max_cache_valid_length_arg`); also the dense cache's
  *                   sequence stride.
  *   scale           multiplies q.k before the softmax.
- *   num_partitions  0 = decode_num_partitions(); > 0 is used verbatim.
+ *   num_partitions  0 = decode_num_partitions(..., ragged = valid_length != NULL, 0);
+ *                   > 0 is used verbatim.
  *   mask            DA_MASK_NONE or DA_MASK_CAUSAL.
  *   workspace       >= decode_workspace_size(P, ...) bytes when P > 1 (may be
  *                   NULL when P == 1).

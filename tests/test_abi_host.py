@@ -39,25 +39,31 @@ def test_status_strings():
     (1, 1, 1, 1, 64, 64, 0), (7, 3, 12, 4, 64, 64, 17), (512, 1, 64, 8, 128, 128, 128)])
 def test_heuristic_bounds_and_determinism(B, T, H, KVH, D, Dv, S):
     for cus in (1, 80, 256, 304):
-        p = DA.num_partitions(B, T, H, KVH, D, Dv, S, cus)
-        assert 1 <= p <= DA.DA_MAX_PARTITIONS
-        assert p == DA.num_partitions(B, T, H, KVH, D, Dv, S, cus)
+        for ragged in (False, True):
+            p = DA.num_partitions(B, T, H, KVH, D, Dv, S, ragged=ragged, num_cus=cus)
+            assert 1 <= p <= DA.DA_MAX_PARTITIONS
+            assert p == DA.num_partitions(B, T, H, KVH, D, Dv, S, ragged=ragged, num_cus=cus)
+            if ragged:  # a ragged batch never gets fewer partitions than a dense one
+                assert p >= DA.num_partitions(B, T, H, KVH, D, Dv, S, num_cus=cus)
 
 
 def test_heuristic_fills_the_device():
-    # 256 (batch, KV head) pairs on 256 compute units: split so that each unit gets
-    # several blocks.
-    assert DA.num_partitions(32, 1, 32, 8, 128, 128, 4096, 256) >= 2
-    # a single sequence of 131072 keys over 8 KV heads: many partitions
-    assert DA.num_partitions(1, 1, 32, 8, 128, 128, 131072, 256) >= 64
+    # 256 (batch, KV head) pairs on 256 compute units: one resident block each
+    assert DA.num_partitions(32, 1, 32, 8, 128, 128, 4096, num_cus=256) == 1
+    # the same pairs with ragged lengths: smaller partitions, several per unit
+    assert DA.num_partitions(32, 1, 32, 8, 128, 128, 4096, ragged=True, num_cus=256) >= 4
+    # a single sequence of 131072 keys over 8 KV heads: enough partitions for every unit
+    assert DA.num_partitions(1, 1, 32, 8, 128, 128, 131072, num_cus=256) >= 32
+    # 64 MLA sequences of 8192 keys: 4 partitions of 2048 keys
+    assert DA.num_partitions(64, 1, 128, 1, 576, 512, 8192, num_cus=256) == 4
     # short caches are not split below the minimum partition length
-    assert DA.num_partitions(1, 1, 8, 8, 64, 64, 256, 256) == 1
+    assert DA.num_partitions(1, 1, 8, 8, 64, 64, 256, num_cus=256) == 1
 
 
 def test_heuristic_rejects_bad_shapes():
     lib = DA.library()
-    assert lib.decode_num_partitions(0, 1, 8, 8, 64, 64, 10, 256) == DA.DA_ERR_INVALID_ARG
-    assert lib.decode_num_partitions(1, 1, 8, 3, 64, 64, 10, 256) == DA.DA_ERR_INVALID_ARG
+    assert lib.decode_num_partitions(0, 1, 8, 8, 64, 64, 10, 0, 256) == DA.DA_ERR_INVALID_ARG
+    assert lib.decode_num_partitions(1, 1, 8, 3, 64, 64, 10, 0, 256) == DA.DA_ERR_INVALID_ARG
 
 
 def test_workspace_layout():

@@ -147,7 +147,7 @@ def test_deterministic_and_guard_bands():
                                                           == 777.0).all())
 
 
-# ---- the matrix-core path (bf16, 8+ query rows per KV head) ------------------------
+# ---- the bf16 streaming matrix-core path -----------------------------------------
 
 def test_paged_ragged_full():
     check(W.PAGED, num_partitions=0)
@@ -170,4 +170,27 @@ def test_mfma_shapes(shape, P):
     wl = W.Workload(f"mfma_{'x'.join(map(str, shape))}", 8700 + S + T, batch=B, num_heads=H,
                     kv_heads=KVH, depth=D, max_seq_len=S, q_len=T, causal=causal,
                     page_size=page, ragged=(1, S, 1), sink=(P == 3))
+    check(wl, num_partitions=P)
+
+
+STREAM = [
+    # (B, T, H, KVH, D, S, page, causal, ragged)
+    (3, 1, 8, 8, 128, 1000, 32, False, True),   # MHA (one row per KV head), 32-key pages
+    (2, 1, 8, 2, 128, 20, 0, False, False),     # two 16-key tiles: waves 2 and 3 idle
+    (2, 1, 8, 2, 64, 5, 0, False, False),       # one partial tile, depth 64
+    (2, 1, 32, 16, 128, 777, 0, False, True),   # 16 KV heads: 4 KB between a head's keys
+    (2, 4, 16, 4, 128, 260, 64, True, True),    # 4 tokens x group 4 = one full 16-row block
+    (1, 1, 40, 2, 64, 2100, 128, False, False),  # group 20: 16 + 4 rows, depth 64 (8 stages)
+]
+
+
+@pytest.mark.parametrize("shape", STREAM, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("P", [1, 7])
+def test_stream_shapes(shape, P):
+    """Tile counts that do not divide among the 4 waves, partitions of C keys with
+    C not a multiple of 64, idle waves, and wide head strides."""
+    B, T, H, KVH, D, S, page, causal, ragged = shape
+    wl = W.Workload(f"stream_{'x'.join(map(str, shape))}", 8800 + S + T + H, batch=B,
+                    num_heads=H, kv_heads=KVH, depth=D, max_seq_len=S, q_len=T, causal=causal,
+                    page_size=page, ragged=(1, S, 1) if ragged else None, sink=(P == 7))
     check(wl, num_partitions=P)

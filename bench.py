@@ -18,6 +18,7 @@ the 256 MB last-level cache.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -37,6 +38,58 @@ ROTATE_BYTES = 2 << 30  # >= 8x the last-level cache
 WORKLOADS = {"tiny": W.TINY_MHA, "gqa": W.GQA, "paged": W.PAGED, "mla": W.MLA,
              "mla_mtp": W.MLA_MTP, "long": W.LONG}
 
+CSRC = os.path.join(ROOT, "decode_attention_07_amd", "csrc")
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic.md")
+COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
+
+
+def kernel_sources(wl: W.Workload):
+    """Source files of the partition-pass kernel a workload runs."""
+    main = "mla_mfma.hip" if wl.mla else ("decode_stream.hip" if wl.dtype == "bf16"
+                                          else "decode_valu.hip")
+    return [os.path.join(CSRC, f) for f in (main, "da_device.h", "da_params.h")]
+
+
+def kernel_hash(wl: W.Workload) -> str:
+    h = hashlib.sha256()
+    for f in kernel_sources(wl):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def recorded_traffic(workload: str, P: int, khash: str):
+    """HBM bytes per launch of the partition-pass kernel, as measured by the
+    FETCH_SIZE / WRITE_SIZE counter runs recorded in profiles/traffic.md for
+    this workload, partition count and kernel source; None when no record
+    matches (for instance after the kernel changed)."""
+    if not os.path.exists(TRAFFIC_TABLE):
+        return None
+    with open(TRAFFIC_TABLE) as fh:
+        for line in fh:
+            cols = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cols) >= 9 and cols[0] == workload and cols[1] == str(P) and cols[3] == khash:
+                try:
+                    return int(cols[8])
+                except ValueError:
+                    return None
+    return None
+
+
+def calibrate_copy():
+    """A plain copy kernel of known size for the FETCH_SIZE / WRITE_SIZE scale:
+    each launch reads COPY_BYTES and writes COPY_BYTES (fp32 negation)."""
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "fp32 negation", "bytes_read_per_launch": COPY_BYTES,
+                      "bytes_written_per_launch": COPY_BYTES, "launches": 5}), flush=True)
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -53,6 +106,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough budget of the CPU-oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the copy kernel that scales the memory counters")
     return ap.parse_args()
 
 
@@ -103,6 +158,9 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
     from decode_attention_07_amd import binding as DA
 
@@ -133,65 +191,83 @@ def main():
     lse = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
     po, pm, ps = DA.workspace_views(ws, P, B, T, H, wl.dv)
 
-    def partition_pass(d):
+    # Each launch is marshalled once (binding BoundCall): a timed step costs the host
+    # one ctypes call per kernel, far less than the kernel itself, so the device
+    # never waits for the host.
+    def partition_call(d):
         if wl.mla:
-            DA.mla_decode_partials(d["q"], d["k"], scale=wl.softmax_scale, num_partitions=P,
-                                   page_table=d["table"], valid_length=d["valid"],
-                                   max_seq_len=S, causal=wl.causal, workspace=ws)
-        else:
-            DA.decode_attention_partials(d["q"], d["k"], d["v"], group=wl.group,
-                                         scale=wl.softmax_scale, num_partitions=P,
-                                         page_table=d["table"], valid_length=d["valid"],
-                                         max_seq_len=S, causal=wl.causal, workspace=ws)
+            return DA.mla_decode_partials(d["q"], d["k"], scale=wl.softmax_scale,
+                                          num_partitions=P, page_table=d["table"],
+                                          valid_length=d["valid"], max_seq_len=S,
+                                          causal=wl.causal, workspace=ws, prepare=True)
+        return DA.decode_attention_partials(d["q"], d["k"], d["v"], group=wl.group,
+                                            scale=wl.softmax_scale, num_partitions=P,
+                                            page_table=d["table"], valid_length=d["valid"],
+                                            max_seq_len=S, causal=wl.causal, workspace=ws,
+                                            prepare=True)
 
-    def reduce_pass(d):
-        DA.splitk_reduce(po, pm, ps, num_q_heads=H, sink_weights=d["sink"], out=out.view(-1, wl.dv),
-                         lse=lse.view(-1))
+    def reduce_call(d):
+        return DA.splitk_reduce(po, pm, ps, num_q_heads=H, sink_weights=d["sink"],
+                                out=out.view(-1, wl.dv), lse=lse.view(-1), prepare=True)
 
     def full_call(d):
         kw = dict(scale=wl.softmax_scale, page_table=d["table"], valid_length=d["valid"],
                   max_seq_len=S, num_partitions=P, sink_weights=d["sink"], causal=wl.causal,
-                  out=out, lse=lse, workspace=ws)
+                  out=out, lse=lse, workspace=ws, prepare=True)
         if wl.mla:
-            DA.mla_decode(d["q"], d["k"], **kw)
-        else:
-            DA.decode_attention(d["q"], d["k"], d["v"], group=wl.group, **kw)
+            return DA.mla_decode(d["q"], d["k"], **kw)
+        return DA.decode_attention(d["q"], d["k"], d["v"], group=wl.group, **kw)
 
-    def step(i, ev_a=None, ev_b=None):
-        d = dev_sets[i % R]
-        if ev_a is not None:
-            ev_a.record()
-        if split:
-            partition_pass(d)
-            if ev_b is not None:
-                ev_b.record()
-            reduce_pass(d)
-        else:
-            full_call(d)
-            if ev_b is not None:
-                ev_b.record()
+    if split:
+        launches = [(partition_call(d), reduce_call(d)) for d in dev_sets]
+    else:
+        launches = [(full_call(d), None) for d in dev_sets]
+
+    def step(i):
+        first_kernel, second_kernel = launches[i % R]
+        first_kernel()
+        if second_kernel is not None:
+            second_kernel()
 
     log(f"P={P} split={split}; warmup {args.warmup}")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # Timed region: exactly K steps, synchronised on both sides, no per-step
+    # events (an event pair between launches costs several microseconds of idle
+    # device time per step).
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
     log(f"timing {K} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(K):
-        step(i, *evs[i])
+        step(i)
+    ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
-    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    ev_ms_per_step = ev0.elapsed_time(ev1) / K
+
+    # The dominant kernel (the partition pass, or the single decode kernel when
+    # the keys are not split) alone: K back-to-back launches between two HIP
+    # events on the stream it is launched on; the average includes the few
+    # hundred nanoseconds between consecutive launches.
+    for i in range(min(R, K)):
+        launches[i % R][0]()
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(K):
+        launches[i % R][0]()
+    ev1.record()
+    torch.cuda.synchronize()
+    kern_avg_ms = ev0.elapsed_time(ev1) / K
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (kern_avg_ms * 1e-3) / 1e9
-    log(f"{ms_per_step * 1e3:.1f} us/step, kernel {kern_avg_ms * 1e3:.1f} us")
+    log(f"{ms_per_step * 1e3:.1f} us/step ({ev_ms_per_step * 1e3:.1f} on events), "
+        f"kernel {kern_avg_ms * 1e3:.1f} us")
 
     res = {
         "metric": METRIC,
@@ -202,20 +278,25 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_device": round(ev_ms_per_step * 1e3, 2),
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1), shapes of the problem statement)",
+        "data": "synthetic: seeded N(0,1) q/k/v with the workload's shapes "
+                "(and its seeded lengths, page placement and sinks)",
         "config": {"workload": wl.name, "batch": B, "q_len": T, "num_q_heads": H,
                    "num_kv_heads": wl.kv_heads, "depth": wl.depth, "depth_v": wl.dv,
                    "max_seq_len": S, "page_size": wl.page_size, "partitions": P,
                    "kv_bytes_per_step": kv_bytes, "input_sets": R},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(args.workload, P, kernel_hash(wl)),
                      "kernel": "partition pass" if split else "decode (single partition)",
-                     "kernel_avg_us": round(kern_avg_ms * 1e3, 2)},
+                     "kernel_source": kernel_hash(wl),
+                     "kernel_avg_us": round(kern_avg_ms * 1e3, 2),
+                     "algorithmic_bytes": kv_bytes},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

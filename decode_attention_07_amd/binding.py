@@ -85,14 +85,41 @@ def _check(status: int, where: str):
         raise DecodeAttentionError(status, where)
 
 
+class BoundCall:
+    """A checked and marshalled C call.  Calling it enqueues the same call again
+    (same buffers, same stream) with a single ctypes call and no Python-side
+    argument handling, so that a loop of launches is not bound by the host.  It
+    keeps the tensors it points into alive."""
+
+    __slots__ = ("fn", "args", "where", "result", "keep")
+
+    def __init__(self, fn, args, where, result, keep):
+        self.fn = fn
+        self.args = tuple(t(a) if a is not None else None for t, a in zip(fn.argtypes, args))
+        self.where = where
+        self.result = result
+        self.keep = keep
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != DA_OK:
+            raise DecodeAttentionError(rc, self.where)
+        return self.result
+
+
+def _finish(fn, args, where, result, keep, prepare):
+    call = BoundCall(fn, args, where, result, keep)
+    return call if prepare else call()
+
+
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream.cuda_stream
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -184,8 +211,10 @@ def _workspace(workspace, P, B, T, H, Dv, device, always=False):
 
 def decode_attention(q, k, v, *, group, scale, page_table=None, valid_length=None,
                      max_seq_len=None, num_partitions=0, sink_weights=None, causal=False,
-                     out=None, lse=None, workspace=None, stream=None, want_lse=True):
-    """GQA/MHA decode attention.  Returns (out [B,T,H,D], lse [B,T,H] or None)."""
+                     out=None, lse=None, workspace=None, stream=None, want_lse=True,
+                     prepare=False):
+    """GQA/MHA decode attention.  Returns (out [B,T,H,D], lse [B,T,H] or None);
+    with prepare=True, a BoundCall that enqueues this call and returns them."""
     _need(q, "q", 4)
     _need(k, "k", 4)
     _need(v, "v", 4)
@@ -205,19 +234,20 @@ def decode_attention(q, k, v, *, group, scale, page_table=None, valid_length=Non
     if lse is None and want_lse:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     workspace, wbytes = _workspace(workspace, P, B, T, H, D, q.device)
-    rc = library().decode_attention(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(page_table), page_size, max_pages, _ptr(valid_length),
-        B, T, H, group, D, S, float(scale), P, _ptr(sink_weights),
-        DA_MASK_CAUSAL if causal else DA_MASK_NONE, dt, _ptr(out), _ptr(lse), _ptr(workspace),
-        wbytes, _stream(stream))
-    _check(rc, "decode_attention")
-    return out, lse
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(page_table), page_size, max_pages,
+            _ptr(valid_length), B, T, H, group, D, S, float(scale), P, _ptr(sink_weights),
+            DA_MASK_CAUSAL if causal else DA_MASK_NONE, dt, _ptr(out), _ptr(lse),
+            _ptr(workspace), wbytes, _stream(stream))
+    return _finish(library().decode_attention, args, "decode_attention", (out, lse),
+                   (q, k, v, page_table, valid_length, sink_weights, out, lse, workspace),
+                   prepare)
 
 
 def decode_attention_partials(q, k, v, *, group, scale, num_partitions, page_table=None,
                               valid_length=None, max_seq_len=None, causal=False, workspace=None,
-                              stream=None):
-    """Partition pass only.  Returns the workspace (uint8 tensor, header layout)."""
+                              stream=None, prepare=False):
+    """Partition pass only.  Returns the workspace (uint8 tensor, header layout), or
+    with prepare=True a BoundCall that enqueues the pass and returns it."""
     _need(q, "q", 4)
     _need(k, "k", 4)
     _need(v, "v", 4)
@@ -227,18 +257,19 @@ def decode_attention_partials(q, k, v, *, group, scale, num_partitions, page_tab
     page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len)
     P = int(num_partitions)
     workspace, wbytes = _workspace(workspace, P, B, T, H, D, q.device, always=True)
-    rc = library().decode_attention_partials(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(page_table), page_size, max_pages, _ptr(valid_length),
-        B, T, H, group, D, S, float(scale), P, DA_MASK_CAUSAL if causal else DA_MASK_NONE, dt,
-        _ptr(workspace), wbytes, _stream(stream))
-    _check(rc, "decode_attention_partials")
-    return workspace
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(page_table), page_size, max_pages,
+            _ptr(valid_length), B, T, H, group, D, S, float(scale), P,
+            DA_MASK_CAUSAL if causal else DA_MASK_NONE, dt, _ptr(workspace), wbytes,
+            _stream(stream))
+    return _finish(library().decode_attention_partials, args, "decode_attention_partials",
+                   workspace, (q, k, v, page_table, valid_length, workspace), prepare)
 
 
 def mla_decode(q, kv, *, scale, page_table=None, valid_length=None, max_seq_len=None,
                num_partitions=0, sink_weights=None, causal=False, out=None, lse=None,
-               workspace=None, stream=None, want_lse=True):
-    """MLA decode (one KV head, depth 576, V = K[..., :512]).  Returns (out, lse)."""
+               workspace=None, stream=None, want_lse=True, prepare=False):
+    """MLA decode (one KV head, depth 576, V = K[..., :512]).  Returns (out, lse), or
+    with prepare=True a BoundCall that enqueues the call and returns them."""
     _need(q, "q", 4, (torch.bfloat16,))
     _need(kv, "kv", 4, (torch.bfloat16,))
     _need(valid_length, "valid_length", 1, _U32)
@@ -254,16 +285,18 @@ def mla_decode(q, kv, *, scale, page_table=None, valid_length=None, max_seq_len=
     if lse is None and want_lse:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device)
-    rc = library().mla_decode(
-        _ptr(q), _ptr(kv), _ptr(page_table), page_size, max_pages, _ptr(valid_length), B, T, H, S,
-        float(scale), P, _ptr(sink_weights), DA_MASK_CAUSAL if causal else DA_MASK_NONE,
-        _ptr(out), _ptr(lse), _ptr(workspace), wbytes, _stream(stream))
-    _check(rc, "mla_decode")
-    return out, lse
+    args = (_ptr(q), _ptr(kv), _ptr(page_table), page_size, max_pages, _ptr(valid_length), B, T,
+            H, S, float(scale), P, _ptr(sink_weights),
+            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(out), _ptr(lse), _ptr(workspace),
+            wbytes, _stream(stream))
+    return _finish(library().mla_decode, args, "mla_decode", (out, lse),
+                   (q, kv, page_table, valid_length, sink_weights, out, lse, workspace), prepare)
 
 
 def mla_decode_partials(q, kv, *, scale, num_partitions, page_table=None, valid_length=None,
-                        max_seq_len=None, causal=False, workspace=None, stream=None):
+                        max_seq_len=None, causal=False, workspace=None, stream=None,
+                        prepare=False):
+    """MLA partition pass only.  Returns the workspace, or with prepare=True a BoundCall."""
     _need(q, "q", 4, (torch.bfloat16,))
     _need(kv, "kv", 4, (torch.bfloat16,))
     _need(valid_length, "valid_length", 1, _U32)
@@ -271,17 +304,18 @@ def mla_decode_partials(q, kv, *, scale, num_partitions, page_table=None, valid_
     page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len)
     P = int(num_partitions)
     workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device, always=True)
-    rc = library().mla_decode_partials(
-        _ptr(q), _ptr(kv), _ptr(page_table), page_size, max_pages, _ptr(valid_length), B, T, H, S,
-        float(scale), P, DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(workspace), wbytes,
-        _stream(stream))
-    _check(rc, "mla_decode_partials")
-    return workspace
+    args = (_ptr(q), _ptr(kv), _ptr(page_table), page_size, max_pages, _ptr(valid_length), B, T,
+            H, S, float(scale), P, DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(workspace),
+            wbytes, _stream(stream))
+    return _finish(library().mla_decode_partials, args, "mla_decode_partials", workspace,
+                   (q, kv, page_table, valid_length, workspace), prepare)
 
 
 def splitk_reduce(part_o, part_max, part_sum, *, num_q_heads, sink_weights=None,
-                  out_dtype=torch.bfloat16, out=None, lse=None, stream=None, want_lse=True):
-    """LSE merge of partials [P, rows, Dv] / [P, rows] -> (out [rows, Dv], lse [rows])."""
+                  out_dtype=torch.bfloat16, out=None, lse=None, stream=None, want_lse=True,
+                  prepare=False):
+    """LSE merge of partials [P, rows, Dv] / [P, rows] -> (out [rows, Dv], lse [rows]);
+    with prepare=True a BoundCall that enqueues the merge and returns them."""
     _need(part_o, "part_o", 3, (torch.float32,))
     _need(part_max, "part_max", 2, (torch.float32,))
     _need(part_sum, "part_sum", 2, (torch.float32,))
@@ -291,11 +325,10 @@ def splitk_reduce(part_o, part_max, part_sum, *, num_q_heads, sink_weights=None,
         out = torch.empty((rows, Dv), dtype=out_dtype, device=part_o.device)
     if lse is None and want_lse:
         lse = torch.empty((rows,), dtype=torch.float32, device=part_o.device)
-    rc = library().splitk_reduce(_ptr(part_o), _ptr(part_max), _ptr(part_sum), P, rows,
-                                 num_q_heads, Dv, _ptr(sink_weights), _ptr(out),
-                                 _dtype_code(out), _ptr(lse), _stream(stream))
-    _check(rc, "splitk_reduce")
-    return out, lse
+    args = (_ptr(part_o), _ptr(part_max), _ptr(part_sum), P, rows, num_q_heads, Dv,
+            _ptr(sink_weights), _ptr(out), _dtype_code(out), _ptr(lse), _stream(stream))
+    return _finish(library().splitk_reduce, args, "splitk_reduce", (out, lse),
+                   (part_o, part_max, part_sum, sink_weights, out, lse), prepare)
 
 
 # ---- host <-> device marshalling of the seeded numpy inputs ------------------------

@@ -290,13 +290,15 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
   char* ring = smem + wave * C::RING;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   if (my_cnt > 0) {
-    // Q loads done, so that only tile loads are in flight below.  The builtin
-    // form lets the compiler see that the Q registers are ready; the empty asm
-    // keeps memory accesses on their side of it.
+    // The first tile is requested while the Q loads are in flight; then
+    // everything so far is waited for, so that only tile loads are counted
+    // below.  The builtin form lets the compiler see that the Q registers are
+    // ready; the empty asm keeps memory accesses on their side of it.
+    stream_issue<D>(p, b, g, k_lo + wave * kTK, hmax, ring_lds, off, lane);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     asm volatile("" ::: "memory");
     const int pro = min(C::STAGES - 1, my_cnt);
-    for (int i = 0; i < pro; ++i)
+    for (int i = 1; i < pro; ++i)
       stream_issue<D>(p, b, g, k_lo + (wave + kWaves * i) * kTK, hmax, ring_lds + i * C::STAGE,
                       off, lane);
     int cur = 0;

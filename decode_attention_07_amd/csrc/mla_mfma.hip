@@ -326,10 +326,13 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   // (tile i + 1) are always a barrier apart and every wave sees the same votes.
   __shared__ __attribute__((aligned(16))) int votes[2][kWaves];
   if (n_tot > 0) {
-    wait_vm_lgkm0<0>();  // Q loads done: only DMA requests are counted below
+    // Tile 0 is requested while the Q loads are in flight; both are waited for
+    // before anything else is issued, so that only tile requests are counted
+    // below.
+    mla_issue(p, lds0, b, k_lo, hmax, wave, lane);
+    wait_vm_lgkm0<0>();
     for (;;) {  // one pass over the partition; repeated only after a restart
-      // tiles 0, 1, 2 requested; wait for tile 0
-      mla_issue(p, lds0, b, k_lo, hmax, wave, lane);
+      // tile 0 is requested on entry; tiles 1, 2 now; wait for tile 0
       if (n_tot > 2) {
         mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, lane);
         mla_issue(p, lds0 + 2 * kTileBytes, b, k_lo + 2 * kBN, hmax, wave, lane);
@@ -382,6 +385,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       lsum = 0.f;
       lsr = 0.f;
       __syncthreads();  // every wave has read the votes before the next pass writes them
+      mla_issue(p, lds0, b, k_lo, hmax, wave, lane);  // tile 0 of the next pass
     }
   }
 

@@ -194,3 +194,22 @@ def test_stream_shapes(shape, P):
                     num_heads=H, kv_heads=KVH, depth=D, max_seq_len=S, q_len=T, causal=causal,
                     page_size=page, ragged=(1, S, 1) if ragged else None, sink=(P == 7))
     check(wl, num_partitions=P)
+
+
+def test_prepared_call_matches_direct():
+    """The binding's prepared (marshal-once) call enqueues the very same C call."""
+    wl = W.Workload("prepared", 8901, batch=3, num_heads=16, kv_heads=4, depth=128,
+                    max_seq_len=700, page_size=64, ragged=(1, 700, 1), sink=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(inp)
+    ref_out, ref_lse = run_gpu(wl, dev, 3)
+    out = torch.empty_like(ref_out)
+    lse = torch.empty_like(ref_lse)
+    call = run_gpu(wl, dev, 3, out=out, lse=lse, prepare=True)
+    for _ in range(2):
+        out.zero_()
+        got_out, got_lse = call()
+        torch.cuda.synchronize()
+        assert got_out is out and got_lse is lse
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+        assert torch.equal(lse, ref_lse)

@@ -39,7 +39,7 @@ WORKLOADS = {"tiny": W.TINY_MHA, "gqa": W.GQA, "paged": W.PAGED, "mla": W.MLA,
              "mla_mtp": W.MLA_MTP, "long": W.LONG}
 
 CSRC = os.path.join(ROOT, "decode_attention_07_amd", "csrc")
-TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic.md")
+PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
 
 
@@ -60,19 +60,22 @@ def kernel_hash(wl: W.Workload) -> str:
 
 def recorded_traffic(workload: str, P: int, khash: str):
     """HBM bytes per launch of the partition-pass kernel, as measured by the
-    FETCH_SIZE / WRITE_SIZE counter runs recorded in profiles/traffic.md for
-    this workload, partition count and kernel source; None when no record
-    matches (for instance after the kernel changed)."""
-    if not os.path.exists(TRAFFIC_TABLE):
+    FETCH_SIZE / WRITE_SIZE counter runs recorded in the profiles/ summaries
+    (table rows: workload | partitions | kernel | kernel source | FETCH_SIZE |
+    WRITE_SIZE | KiB per unit x2 | HBM bytes) for this workload, partition count
+    and kernel source; None when no row matches (for instance after the kernel
+    changed)."""
+    if not os.path.isdir(PROFILES):
         return None
-    with open(TRAFFIC_TABLE) as fh:
-        for line in fh:
-            cols = [c.strip() for c in line.strip().strip("|").split("|")]
-            if len(cols) >= 9 and cols[0] == workload and cols[1] == str(P) and cols[3] == khash:
-                try:
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(PROFILES, name)) as fh:
+            for line in fh:
+                cols = [c.strip() for c in line.strip().strip("|").split("|")]
+                if (len(cols) >= 9 and cols[0] == workload and cols[1] == str(P)
+                        and cols[3] == khash and cols[8].isdigit()):
                     return int(cols[8])
-                except ValueError:
-                    return None
     return None
 
 

@@ -98,6 +98,29 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def read_ceiling():
+    """Context for the roofline: a plain streaming-read kernel's rate on this
+    device (torch's int32 row maximum over 4 GiB: reads 4 GiB, writes 4 MiB)."""
+    import torch
+    n = 1 << 30  # int32 elements = 4 GiB
+    x = torch.ones(n, dtype=torch.int32, device="cuda").view(-1, 1024)
+    for _ in range(3):
+        x.amax(dim=1)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        x.amax(dim=1)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = statistics.median(times)
+    print(json.dumps({"read_ceiling": "torch int32 row max over 4 GiB", "bytes_read": 4 * n,
+                      "ms": round(ms, 4), "GB/s": round(4 * n / ms / 1e6, 1),
+                      "frac_of_8TB/s": round(4 * n / ms / 1e6 / HBM_PEAK_GBS, 4)}), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +134,8 @@ def parse():
                     help="rough budget of the CPU-oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the copy kernel that scales the memory counters")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure a plain streaming-read kernel (context for the roofline)")
     return ap.parse_args()
 
 
@@ -163,6 +188,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.ceiling:
+        read_ceiling()
         return
     import torch
     from decode_attention_07_amd import binding as DA

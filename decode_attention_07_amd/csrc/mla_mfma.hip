@@ -24,12 +24,15 @@
 //       A = V^T read by column from the same LDS tile, B = P^T taken straight
 //       from the S^T accumulators (bf16); O^T lives in the 256 accumulation
 //       registers.
-// LDS tile layout: column-major in 16-byte chunks with an XOR swizzle,
-//   chunk(key, col) = col * 32 + (key ^ (4 * (col & 1))),  col = 16-byte column 0..71,
-// so one 1 KB DMA instruction fills two columns of all 32 keys, any 8
-// consecutive keys of a column sit in 8 different 16-byte bank groups (the K
-// operand reads), and so do the 4 keys x 2 adjacent columns that one 16-lane
-// transposing read of the V^T operand touches.
+// LDS tile layout: row-major in 16-byte chunks, chunk c of key k stored at
+// position c ^ swz(k) of its 72-chunk row, swz(k) = 4 ((k / 2) % 2) + (k / 4) % 4.
+// The XOR stays inside aligned groups of 8 chunks (one 128-byte line), so a
+// stage is filled linearly: each 1 KB load instruction fetches 8 whole cache
+// lines (which lets the loads carry the non-temporal hint).  swz() is chosen
+// for gfx950's 64-bank LDS (measured with the bank-conflict counter): the K
+// operand reads (16 keys x one chunk per 16 lanes) and the transposing V^T
+// reads (4 keys x 64 bytes per 32 lanes) are both conflict-free.  swz(k + 16)
+// = swz(k), swz(k + 8) differs.
 // With two tokens (256 rows) a sequence needs two blocks that read the same
 // tiles; their block ids differ by a multiple of 8 so that both land on the same
 // XCD and the second read of each tile is served by that XCD's L2.
@@ -56,19 +59,20 @@ static_assert(kDmaPerWave * kWaves * 1024 == kTileBytes, "tile must split into 1
 constexpr int kStages = 4;
 constexpr float kHeadroom = 100.0f;          // largest exp2 argument (log2 units)
 
-// 16 bytes per lane from global memory straight into LDS (gfx950
-// global_load_lds_dwordx4): lane i of the wave writes lds_base + 16 * i.  No
-// non-temporal hint here: the 4 waves each fetch a 32-byte quarter of the same
-// 128-byte lines, and an early-evicted line would be fetched again for each.
-// Issued through inline asm so that the compiler does not serialise later LDS
-// reads of other stages behind it; completion is tracked with explicit vmcnt
-// waits.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// 16 bytes per lane from base + voff straight into LDS (gfx950
+// global_load_lds_dwordx4, scalar base + 32-bit vector offset): lane i of the
+// wave writes lds_base + 16 * i.  The cache is streamed through once per block
+// and every instruction covers whole lines: non-temporal hint (nt).  Issued
+// through inline asm so that the compiler does not serialise later LDS reads of
+// other stages behind it; completion is tracked with explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
-               : "v"(src), "s"(lds_base)
+               : "v"(voff), "s"(base), "s"(lds_base)
                : "memory", "m0");
 }
+
+__device__ __forceinline__ constexpr int swz(int key) { return 4 * ((key >> 1) & 1) + ((key >> 2) & 3); }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt_hi[15:14]; expcnt left at its maximum).
@@ -77,30 +81,55 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
-// Requests the 32-key tile starting at key j0 into one LDS stage.  Instruction n
-// (n = wave + 4 i) fills columns 2n and 2n + 1; lane l of it takes column
-// 2n + (l >> 5) of key (l & 31) ^ (4 (l >> 5)), which keeps the column-major
-// swizzled layout.  Keys at or past `kend` fetch row 0 of the tile instead
-// (finite data; those keys are masked out of the softmax), so every wave
-// issues exactly kDmaPerWave instructions.
+// Load instruction n (n = wave + 4 i) of a tile writes stage chunks 64 n + lane:
+// chunk position q = (64 n + lane) % 72 of key (64 n + lane) / 72, which holds the
+// key's chunk q ^ swz(key).  As 72 is a multiple of 8, q % 8 = lane % 8 and the
+// source offset is 16 (64 n + lane) + 16 (((lane % 8) ^ swz(key)) - lane % 8).
+// Each lane's 9 offsets are computed once and kept in LDS (registers are all in
+// use), packed as offset * 32 + key.
+constexpr int kTabPerLane = 12;  // 9 used; 48 bytes per lane keeps 16-byte reads aligned
+
+__device__ __forceinline__ void dma_table_init(uint32_t* tab, int wave, int lane) {
+  const int l7 = lane & 7;
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const uint32_t c = 64u * (uint32_t)(wave + kWaves * i) + (uint32_t)lane;
+    const int key = (int)(c / 72u);
+    const uint32_t off = 16u * c + 16u * (uint32_t)((l7 ^ swz(key)) - l7);
+    tab[i] = off * 32u + (uint32_t)key;
+  }
+}
+
+// Requests the 32-key tile starting at key j0 into one LDS stage.  Keys at or
+// past `kend` fetch the same chunk of the tile's first key instead (finite data;
+// those keys are masked out of the softmax), so every wave issues exactly
+// kDmaPerWave instructions.
 __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage, int b, int j0,
-                                          int kend, int wave, int lane) {
+                                          int kend, int wave, const uint32_t* tab) {
   size_t row0;
-  if (p.page_table) {
-    const uint32_t phys = p.page_table[(size_t)b * p.max_pages + (j0 >> p.page_shift)];
+  if (p.page_table) {  // uniform index, table constant during the call: scalar cache
+    const __attribute__((address_space(4))) uint32_t* pt =
+        (const __attribute__((address_space(4))) uint32_t*)p.page_table;
+    const uint32_t phys = pt[(size_t)b * p.max_pages + (j0 >> p.page_shift)];
     row0 = ((size_t)phys << p.page_shift) + (size_t)(j0 & ((1 << p.page_shift) - 1));
   } else {
     row0 = (size_t)b * p.max_seq_len + j0;
   }
-  const int g = lane >> 5;
-  const int col0 = 2 * wave + g;               // column of instruction i is col0 + 8 i
-  const int key = (lane & 31) ^ (4 * g);       // column parity is g
-  const bool real = j0 + key < kend;
-  const char* src =
-      (const char*)p.k + row0 * kRowBytes + (real ? key * kRowBytes : 0) + col0 * 16;
+  const char* base = (const char*)p.k + row0 * kRowBytes;
+  const int nvalid = kend - j0;
+  const uint4 t0 = *(const uint4*)tab;
+  const uint4 t1 = *(const uint4*)(tab + 4);
+  const uint32_t e[kDmaPerWave] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w, tab[8]};
   const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + wave * 1024);
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) dma16(src + i * 128, dst + i * kWaves * 1024);
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    uint32_t off = e[i] >> 5;
+    if (nvalid < kBN) {
+      const int key = (int)(e[i] & 31u);
+      if (key >= nvalid) off -= (uint32_t)key * kRowBytes;
+    }
+    dma16(base, off, dst + i * kWaves * 1024);
+  }
 }
 
 // The MFMAs are written as inline asm so that the register classes are fixed:
@@ -160,20 +189,23 @@ __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[k
                                          bool masked, int hi, float scale_log2, bool& restart) {
   const int lane = threadIdx.x & 63;
   const int c32 = lane & 31, g = lane >> 5;
-  // S^T = K . Q^T; the A operand of depth step st is column 2 st + g of key c32
-  // (column parity g).  Two accumulation chains (even / odd st); the K fragments
-  // come from a ring kPf pairs deep so that their LDS latency hides behind the
-  // MFMAs in flight.
+  // S^T = K . Q^T; the A operand of depth step st is chunk 2 st + g of key c32,
+  // at byte (kofs ^ 32 (st % 4)) + 128 (st / 4) of the stage (the swizzle only
+  // touches bits 4..6 of the offset).  Two accumulation chains (even / odd st);
+  // the K fragments come from a ring kPf pairs deep so that their LDS latency
+  // hides behind the MFMAs in flight.
   f32x16_t s0, s1;
-  const char* ka = buf + (g * 32 + (c32 ^ (4 * g))) * 16;
-  const char* kb = ka;
+  const uint32_t kofs = kRowBytes * c32 + ((16u * g) ^ (16u * swz(c32)));
+  auto kfrag = [&](int st) {
+    return *(const bf16x8_t*)(buf + ((kofs ^ (32u * (st % 4))) + 128u * (st / 4)));
+  };
   constexpr int kPairs = kKS / 2;
   constexpr int kPf = 4;
   bf16x8_t ra[kPf], rb[kPf];
 #pragma unroll
   for (int q = 0; q < kPf; ++q) {
-    ra[q] = *(const bf16x8_t*)(ka + (2 * q) * 1024);
-    rb[q] = *(const bf16x8_t*)(kb + (2 * q + 1) * 1024);
+    ra[q] = kfrag(2 * q);
+    rb[q] = kfrag(2 * q + 1);
   }
 #pragma unroll
   for (int pq = 0; pq < kPairs; ++pq) {
@@ -186,23 +218,28 @@ __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[k
       mfma_v(s1, rb[slot], qf[2 * pq + 1]);
     }
     if (pq + kPf < kPairs) {
-      ra[slot] = *(const bf16x8_t*)(ka + (2 * (pq + kPf)) * 1024);
-      rb[slot] = *(const bf16x8_t*)(kb + (2 * (pq + kPf) + 1) * 1024);
+      ra[slot] = kfrag(2 * (pq + kPf));
+      rb[slot] = kfrag(2 * (pq + kPf) + 1);
     }
   }
   // V^T operand addresses (see below); the first kPf fragments are requested
   // now so that they arrive while the softmax runs.
   const int G = lane >> 4, i16 = lane & 15;
   const int cl = 2 * (G & 1) + ((i16 & 3) >> 1);
-  const char* vt =
-      buf + cl * 512 + 64 * (g ^ (cl & 1)) + (i16 >> 2) * 16 + 8 * (i16 & 1);
-  constexpr int kFrags = kDT * 2;  // fragment f = (dt = f / 2, kh = f % 2)
+  const int vkey = 4 * g + (i16 >> 2);
+  const uint32_t vofs0 = kRowBytes * vkey + ((16u * cl) ^ (16u * swz(vkey))) + 8u * (i16 & 1);
+  const uint32_t vofs1 =
+      kRowBytes * (vkey + 8) + ((16u * cl) ^ (16u * swz(vkey + 8))) + 8u * (i16 & 1);
+  constexpr int kFrags = kDT * 2;  // fragment f = (kh = f / 16, dt = f % 16)
+  auto vfrag = [&](int f, uint32_t vofs) {  // key half kh sits 16 keys on
+    const int dt = f % kDT, kh = f / kDT;
+    return buf + ((vofs ^ (64u * (dt % 2))) + 128u * (dt / 2) + 16u * kRowBytes * kh);
+  };
   uint2 vlo[kPf], vhi[kPf];
 #pragma unroll
   for (int f = 0; f < kPf; ++f) {
-    const char* a = vt + (f / 2) * 2048 + (f % 2) * 256;
-    vlo[f] = lds_read_tr16(a);
-    vhi[f] = lds_read_tr16(a + 128);
+    vlo[f] = lds_read_tr16(vfrag(f, vofs0));
+    vhi[f] = lds_read_tr16(vfrag(f, vofs1));
   }
   mfma_settle(s0, s1);
   float x[16];
@@ -251,21 +288,22 @@ __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[k
   // keys 16 kh + 4 g + 0..3 and slots 4..7 keys 16 kh + 8 + 4 g + 0..3 (the P^T
   // slot order), at d = 32 dt + (lane % 32).  Each half is one transposing read:
   // lane i of 16-lane group G supplies &V[16 kh + 4 g + i / 4][32 dt + 16 (G % 2) +
-  // 4 (i % 4)], i.e. column 4 dt + cl, byte 8 (i % 2) of the chunk of that key,
-  // with cl = 2 (G % 2) + (i % 4) / 2 and the swizzle key ^ (4 (cl & 1)).
+  // 4 (i % 4)], i.e. chunk 4 dt + cl of that key, byte 8 (i % 2), with
+  // cl = 2 (G % 2) + (i % 4) / 2; swz() of the key does not change by +16, so two
+  // per-lane offsets (keys 4 g + i / 4 and those + 8) serve every fragment.
 #pragma unroll
   for (int f = 0; f < kFrags; ++f) {
     const int slot = f % kPf;
-    // the P^T operands were just written by VALU ops: only the first two MFMAs
-    // (one per key half) can be within reach of that hazard
+    // fragment f = (kh = f / 16, dt = f % 16): consecutive MFMAs update different
+    // accumulators.  The P^T operands were just written by VALU ops: only the
+    // first two MFMAs can be within reach of that hazard.
     if (f < 2)
-      mfma_acc<true>(acc[f / 2], concat_bf16x8(vlo[slot], vhi[slot]), pb[f % 2]);
+      mfma_acc<true>(acc[f % kDT], concat_bf16x8(vlo[slot], vhi[slot]), pb[f / kDT]);
     else
-      mfma_acc<false>(acc[f / 2], concat_bf16x8(vlo[slot], vhi[slot]), pb[f % 2]);
+      mfma_acc<false>(acc[f % kDT], concat_bf16x8(vlo[slot], vhi[slot]), pb[f / kDT]);
     if (f + kPf < kFrags) {
-      const char* a = vt + ((f + kPf) / 2) * 2048 + ((f + kPf) % 2) * 256;
-      vlo[slot] = lds_read_tr16(a);
-      vhi[slot] = lds_read_tr16(a + 128);
+      vlo[slot] = lds_read_tr16(vfrag(f + kPf, vofs0));
+      vhi[slot] = lds_read_tr16(vfrag(f + kPf, vofs1));
     }
   }
 }
@@ -309,8 +347,8 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   const uint16_t* qrow =
       (const uint16_t*)p.q + (((size_t)b * p.q_len + tok) * H + head) * (size_t)kD;
 #pragma unroll
-  for (int s = 0; s < kKS; ++s)
-    qf[s] = row_ok ? *(const bf16x8_t*)(qrow + s * 16 + g * 8) : bf16x8_t{};
+  for (int s = 0; s < kKS; ++s)  // rows past the fold read row (b, 0, 0) and are zeroed later
+    qf[s] = *(const bf16x8_t*)(qrow + s * 16 + g * 8);
 
   f32x16_t acc[kDT];
 #pragma unroll
@@ -328,20 +366,25 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   // read at the top of tile i, so a read and the next write of the same buffer
   // (tile i + 1) are always a barrier apart and every wave sees the same votes.
   __shared__ __attribute__((aligned(16))) int votes[2][kWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t dma_tab[kThreads * kTabPerLane];
+  const uint32_t* tab = dma_tab + threadIdx.x * kTabPerLane;  // this lane's own entries
+  dma_table_init(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
   if (n_tot > 0) {
     // Tile 0 is requested while the Q loads are in flight; both are waited for
     // before anything else is issued, so that only tile requests are counted
     // below.
-    mla_issue(p, lds0, b, k_lo, hmax, wave, lane);
+    mla_issue(p, lds0, b, k_lo, hmax, wave, tab);
     wait_vm_lgkm0<0>();
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) qf[s] = row_ok ? qf[s] : bf16x8_t{};
     for (;;) {  // one pass over the partition; repeated only after a restart
       // tile 0 is requested on entry; tiles 1, 2 now; wait for tile 0
       if (n_tot > 2) {
-        mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, lane);
-        mla_issue(p, lds0 + 2 * kTileBytes, b, k_lo + 2 * kBN, hmax, wave, lane);
+        mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, tab);
+        mla_issue(p, lds0 + 2 * kTileBytes, b, k_lo + 2 * kBN, hmax, wave, tab);
         wait_vm_lgkm0<2 * kDmaPerWave>();
       } else if (n_tot > 1) {
-        mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, lane);
+        mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, tab);
         wait_vm_lgkm0<kDmaPerWave>();
       } else {
         wait_vm_lgkm0<0>();
@@ -357,7 +400,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         const bool ahead = i + 3 < n_tot;
         if (ahead) {  // stage of tile i + 3 was last read by tile i - 1, a barrier ago
           const int nxt = (cur + 3 >= kStages) ? cur + 3 - kStages : cur + 3;
-          mla_issue(p, lds0 + nxt * kTileBytes, b, k_lo + (i + 3) * kBN, hmax, wave, lane);
+          mla_issue(p, lds0 + nxt * kTileBytes, b, k_lo + (i + 3) * kBN, hmax, wave, tab);
         }
         bool need = false;
         mla_tile(smem + cur * kTileBytes, qf, acc, m, lsum, lsr, k_lo + i * kBN, i >= n_full,
@@ -388,7 +431,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       lsum = 0.f;
       lsr = 0.f;
       __syncthreads();  // every wave has read the votes before the next pass writes them
-      mla_issue(p, lds0, b, k_lo, hmax, wave, lane);  // tile 0 of the next pass
+      mla_issue(p, lds0, b, k_lo, hmax, wave, tab);  // tile 0 of the next pass
     }
   }
 

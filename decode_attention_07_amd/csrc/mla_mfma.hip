@@ -183,19 +183,13 @@ __device__ __forceinline__ constexpr int c32_row(int j, int g) {
   return (j / 4) * 8 + g * 4 + (j % 4);
 }
 
-__device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[kKS],
-                                         f32x16_t (&acc)[kDT], float& m, float& lsum, float& lsr,
-                                         int j0,
-                                         bool masked, int hi, float scale_log2, bool& restart) {
-  const int lane = threadIdx.x & 63;
-  const int c32 = lane & 31, g = lane >> 5;
-  // S^T = K . Q^T; the A operand of depth step st is chunk 2 st + g of key c32,
-  // at byte (kofs ^ 32 (st % 4)) + 128 (st / 4) of the stage (the swizzle only
-  // touches bits 4..6 of the offset).  Two accumulation chains (even / odd st);
-  // the K fragments come from a ring kPf pairs deep so that their LDS latency
-  // hides behind the MFMAs in flight.
-  f32x16_t s0, s1;
-  const uint32_t kofs = kRowBytes * c32 + ((16u * g) ^ (16u * swz(c32)));
+// Scores of one tile: S^T = K . Q^T.  The A operand of depth step st is chunk
+// 2 st + g of key c32, at byte (kofs ^ 32 (st % 4)) + 128 (st / 4) of the stage
+// (the swizzle only touches bits 4..6 of the offset).  Two accumulation chains
+// (even / odd st); the K fragments come from a ring kPf pairs deep so that their
+// LDS latency hides behind the MFMAs in flight.
+__device__ __forceinline__ void mla_scores(const char* buf, const bf16x8_t (&qf)[kKS],
+                                           uint32_t kofs, f32x16_t& s0, f32x16_t& s1) {
   auto kfrag = [&](int st) {
     return *(const bf16x8_t*)(buf + ((kofs ^ (32u * (st % 4))) + 128u * (st / 4)));
   };
@@ -222,26 +216,87 @@ __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[k
       rb[slot] = kfrag(2 * (pq + kPf) + 1);
     }
   }
-  // V^T operand addresses (see below); the first kPf fragments are requested
-  // now so that they arrive while the softmax runs.
-  const int G = lane >> 4, i16 = lane & 15;
-  const int cl = 2 * (G & 1) + ((i16 & 3) >> 1);
-  const int vkey = 4 * g + (i16 >> 2);
-  const uint32_t vofs0 = kRowBytes * vkey + ((16u * cl) ^ (16u * swz(vkey))) + 8u * (i16 & 1);
-  const uint32_t vofs1 =
-      kRowBytes * (vkey + 8) + ((16u * cl) ^ (16u * swz(vkey + 8))) + 8u * (i16 & 1);
-  constexpr int kFrags = kDT * 2;  // fragment f = (kh = f / 16, dt = f % 16)
-  auto vfrag = [&](int f, uint32_t vofs) {  // key half kh sits 16 keys on
+  mfma_settle(s0, s1);
+}
+
+// O^T += V^T . P^T for one tile, one fragment per call of step(f).  V^T operand
+// of depth tile dt, key-half kh (fragment f: kh = f / 16, dt = f % 16, so that
+// consecutive MFMAs update different accumulators): slots 0..3 hold keys
+// 16 kh + 4 g + 0..3 and slots 4..7 keys 16 kh + 8 + 4 g + 0..3 (the P^T slot
+// order), at d = 32 dt + (lane % 32).  Each half is one transposing read: lane i
+// of 16-lane group G supplies &V[16 kh + 4 g + i / 4][32 dt + 16 (G % 2) +
+// 4 (i % 4)], i.e. chunk 4 dt + cl of that key, byte 8 (i % 2), with
+// cl = 2 (G % 2) + (i % 4) / 2.  swz() of a key does not change by +16, so two
+// per-lane offsets (keys 4 g + i / 4 and those + 8) serve every fragment.  The V
+// fragments come from a ring kPf deep.
+struct MlaPV {
+  static constexpr int kFrags = kDT * 2;
+  static constexpr int kPf = 4;
+  const char* buf;
+  uint32_t vofs0, vofs1;
+  uint2 vlo[kPf], vhi[kPf];
+
+  __device__ __forceinline__ const char* frag(int f, uint32_t vofs) const {
     const int dt = f % kDT, kh = f / kDT;
     return buf + ((vofs ^ (64u * (dt % 2))) + 128u * (dt / 2) + 16u * kRowBytes * kh);
-  };
-  uint2 vlo[kPf], vhi[kPf];
-#pragma unroll
-  for (int f = 0; f < kPf; ++f) {
-    vlo[f] = lds_read_tr16(vfrag(f, vofs0));
-    vhi[f] = lds_read_tr16(vfrag(f, vofs1));
   }
-  mfma_settle(s0, s1);
+  __device__ __forceinline__ void start(const char* b, uint32_t o0, uint32_t o1) {
+    buf = b;
+    vofs0 = o0;
+    vofs1 = o1;
+#pragma unroll
+    for (int f = 0; f < kPf; ++f) {
+      vlo[f] = lds_read_tr16(frag(f, vofs0));
+      vhi[f] = lds_read_tr16(frag(f, vofs1));
+    }
+  }
+  // NOP: the P^T operands may have been written by VALU ops just before.
+  template <bool NOP>
+  __device__ __forceinline__ void step(int f, f32x16_t (&acc)[kDT], const bf16x8_t (&pb)[2]) {
+    const int slot = f % kPf;
+    mfma_acc<NOP>(acc[f % kDT], concat_bf16x8(vlo[slot], vhi[slot]), pb[f / kDT]);
+    if (f + kPf < kFrags) {
+      vlo[slot] = lds_read_tr16(frag(f + kPf, vofs0));
+      vhi[slot] = lds_read_tr16(frag(f + kPf, vofs1));
+    }
+  }
+};
+
+// Softmax of one tile's scores (s0 + s1) into the bf16 weights pb, and, when PV,
+// interleaved with it the P.V contraction of the previous tile (weights pb_prev,
+// V rows in pv's stage): the vector ALU works on this tile while the matrix core
+// works on the last one.
+//
+// Softmax on the accumulator layout: lane l owns row l % 32 and 16 of the 32
+// keys, lane l ^ 32 the other 16.  Each row keeps a fixed reference max, set by
+// its first visible tile: p = 2^(s - m) may grow to 2^100 (fp32 and bf16 hold
+// that, and the sums stay below 2^128), so O is never rescaled inside the loop.
+// If a row ever exceeds its reference by more than that, the block restarts its
+// partition with the raised reference.  The weights enter the MFMA rounded to
+// bf16; their rounded sum (lsr) is what O is normalised by, so the effective
+// weights still sum to one.
+template <bool PV>
+__device__ __forceinline__ void mla_softmax_pv(const f32x16_t& s0, const f32x16_t& s1, MlaPV& pv,
+                                               const bf16x8_t (&pb_prev)[2], bf16x8_t (&pb)[2],
+                                               f32x16_t (&acc)[kDT], float& m, float& lsum,
+                                               float& lsr, int j0, bool masked, int hi,
+                                               float scale_log2, bool& restart) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  int f = 0;
+  // One P.V MFMA of the previous tile; the scheduling barrier keeps the
+  // compiler from regrouping the interleaved vector and matrix work.
+  auto pv_step = [&]() {
+    if (PV && f < MlaPV::kFrags) {
+      pv.step<false>(f, acc, pb_prev);
+      ++f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The running max and sums pass through an empty volatile asm at their place in
+  // the interleave: volatile asm keeps its order, so the arithmetic they depend
+  // on cannot be sunk below the MFMAs it is meant to run beside.
+  auto pin = [](float& v) { asm volatile("" : "+v"(v)); };
   float x[16];
   float mx = kNegInf;
 #pragma unroll
@@ -250,28 +305,30 @@ __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[k
     if (masked) v = (j0 + c32_row(j, g) < hi) ? v : kNegInf;
     x[j] = v;
     mx = fmaxf(mx, v);
+    if (j % 2 == 1) {
+      pin(mx);
+      pv_step();
+    }
   }
   mx = max_xor32(mx);
-  // Fixed reference per row: exp2 arguments may reach kHeadroom; a row whose
-  // tile max exceeds it raises the block's restart flag (the partition is then
-  // recomputed from its first key with the larger reference).
+  pin(mx);
+  pv_step();
   const bool grow = mx > m + kHeadroom;
-  if (grow) {
-    if (m != kNegInf) restart = true;  // first visible tile of a row: acc is still 0
-    m = mx;
-  }
-  const float ms = (m == kNegInf) ? 0.f : m;
+  restart = restart || (grow && m != kNegInf);  // a row's first visible tile: acc is still 0
+  m = grow ? mx : m;
+  float ms = (m == kNegInf) ? 0.f : m;
+  pin(ms);
   float ps = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     x[j] = fast_exp2(x[j] - ms);
     ps += x[j];
+    if (j % 2 == 1) {
+      pin(ps);
+      pv_step();
+    }
   }
   lsum += ps;
-  // P^T operands: the 16 keys of key-half kh are this lane's accumulators 8kh..8kh+7.
-  // The weights enter the MFMA rounded to bf16; their rounded sum (lsr) is what
-  // O is normalised by, so the effective weights still sum to one.
-  bf16x8_t pb[2];
   float pr = 0.f;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
@@ -280,32 +337,14 @@ __device__ __forceinline__ void mla_tile(const char* buf, const bf16x8_t (&qf)[k
     for (int q = 0; q < 4; ++q) {
       w[q] = pack_bf16(x[8 * kh + 2 * q], x[8 * kh + 2 * q + 1]);
       pr += bf16lo(w[q]) + bf16hi(w[q]);
+      pin(pr);
+      pv_step();
     }
     pb[kh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
   }
   lsr += pr;
-  // O^T += V^T . P^T.  V^T operand of depth tile dt, key-half kh: slots 0..3 hold
-  // keys 16 kh + 4 g + 0..3 and slots 4..7 keys 16 kh + 8 + 4 g + 0..3 (the P^T
-  // slot order), at d = 32 dt + (lane % 32).  Each half is one transposing read:
-  // lane i of 16-lane group G supplies &V[16 kh + 4 g + i / 4][32 dt + 16 (G % 2) +
-  // 4 (i % 4)], i.e. chunk 4 dt + cl of that key, byte 8 (i % 2), with
-  // cl = 2 (G % 2) + (i % 4) / 2; swz() of the key does not change by +16, so two
-  // per-lane offsets (keys 4 g + i / 4 and those + 8) serve every fragment.
 #pragma unroll
-  for (int f = 0; f < kFrags; ++f) {
-    const int slot = f % kPf;
-    // fragment f = (kh = f / 16, dt = f % 16): consecutive MFMAs update different
-    // accumulators.  The P^T operands were just written by VALU ops: only the
-    // first two MFMAs can be within reach of that hazard.
-    if (f < 2)
-      mfma_acc<true>(acc[f % kDT], concat_bf16x8(vlo[slot], vhi[slot]), pb[f / kDT]);
-    else
-      mfma_acc<false>(acc[f % kDT], concat_bf16x8(vlo[slot], vhi[slot]), pb[f / kDT]);
-    if (f + kPf < kFrags) {
-      vlo[slot] = lds_read_tr16(vfrag(f + kPf, vofs0));
-      vhi[slot] = lds_read_tr16(vfrag(f + kPf, vofs1));
-    }
-  }
+  for (int r = 0; r < MlaPV::kFrags; ++r) pv_step();  // the rest of the previous tile
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -358,9 +397,19 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   const int n_full = (hmin - k_lo) / kBN;
   const int n_tot = (hmax - k_lo + kBN - 1) / kBN;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  // 4-stage ring: tile i lives in stage i % 4; tile i + 3 is requested while
-  // tile i is consumed.  Before each barrier a wave waits until only the
-  // requests of tiles i + 2 and i + 3 are outstanding, i.e. tile i + 1 landed.
+  // Per-lane LDS offsets of the operand reads (see mla_scores / MlaPV).
+  const uint32_t kofs = kRowBytes * c32 + ((16u * g) ^ (16u * swz(c32)));
+  const int G = lane >> 4, i16 = lane & 15;
+  const int cl = 2 * (G & 1) + ((i16 & 3) >> 1);
+  const int vkey = 4 * g + (i16 >> 2);
+  const uint32_t vofs0 = kRowBytes * vkey + ((16u * cl) ^ (16u * swz(vkey))) + 8u * (i16 & 1);
+  const uint32_t vofs1 =
+      kRowBytes * (vkey + 8) + ((16u * cl) ^ (16u * swz(vkey + 8))) + 8u * (i16 & 1);
+  // 4-stage ring, software-pipelined: iteration i computes the scores and the
+  // softmax of tile i while the matrix core contracts tile i - 1 with its
+  // weights (pb_prev), so stages i and i - 1 are being read; tile i + 2 is
+  // requested into the stage tile i - 2 left, and before each barrier a wave
+  // waits until only tile i + 2's requests are outstanding (tile i + 1 landed).
   // Restart votes: each wave writes its own slot for tile i (every tile, 0 or 1)
   // into buffer i & 1 before the tile's barrier; the slots of tile i - 1 are
   // read at the top of tile i, so a read and the next write of the same buffer
@@ -377,39 +426,44 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     wait_vm_lgkm0<0>();
 #pragma unroll
     for (int s = 0; s < kKS; ++s) qf[s] = row_ok ? qf[s] : bf16x8_t{};
+    bf16x8_t pb_prev[2];
     for (;;) {  // one pass over the partition; repeated only after a restart
-      // tile 0 is requested on entry; tiles 1, 2 now; wait for tile 0
-      if (n_tot > 2) {
-        mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, tab);
-        mla_issue(p, lds0 + 2 * kTileBytes, b, k_lo + 2 * kBN, hmax, wave, tab);
-        wait_vm_lgkm0<2 * kDmaPerWave>();
-      } else if (n_tot > 1) {
+      // tile 0 is requested on entry; tile 1 now; wait for tile 0
+      if (n_tot > 1) {
         mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, tab);
         wait_vm_lgkm0<kDmaPerWave>();
       } else {
         wait_vm_lgkm0<0>();
       }
       __syncthreads();
-      int cur = 0;
       bool again = false;
       for (int i = 0; i < n_tot; ++i) {
         // Votes of tile i - 1, acted upon after tile i (the load has landed by
         // then; what tile i adds is dropped with the rest on a restart).
         int4 prev = make_int4(0, 0, 0, 0);
         if (i > 0) prev = *(const int4*)votes[(i - 1) & 1];
-        const bool ahead = i + 3 < n_tot;
-        if (ahead) {  // stage of tile i + 3 was last read by tile i - 1, a barrier ago
-          const int nxt = (cur + 3 >= kStages) ? cur + 3 - kStages : cur + 3;
-          mla_issue(p, lds0 + nxt * kTileBytes, b, k_lo + (i + 3) * kBN, hmax, wave, tab);
-        }
+        const bool ahead = i + 2 < n_tot;
+        if (ahead)  // into the stage of tile i - 2, last read a barrier ago
+          mla_issue(p, lds0 + ((i + 2) & (kStages - 1)) * kTileBytes, b, k_lo + (i + 2) * kBN,
+                    hmax, wave, tab);
+        f32x16_t s0, s1;
+        mla_scores(smem + (i & (kStages - 1)) * kTileBytes, qf, kofs, s0, s1);
         bool need = false;
-        mla_tile(smem + cur * kTileBytes, qf, acc, m, lsum, lsr, k_lo + i * kBN, i >= n_full,
-                 hi, p.scale_log2, need);
+        bf16x8_t pb[2];
+        MlaPV pv;
+        if (i == 0) {
+          mla_softmax_pv<false>(s0, s1, pv, pb_prev, pb, acc, m, lsum, lsr, k_lo, 0 >= n_full,
+                                hi, p.scale_log2, need);
+        } else {
+          pv.start(smem + ((i - 1) & (kStages - 1)) * kTileBytes, vofs0, vofs1);
+          mla_softmax_pv<true>(s0, s1, pv, pb_prev, pb, acc, m, lsum, lsr, k_lo + i * kBN,
+                               i >= n_full, hi, p.scale_log2, need);
+        }
+        pb_prev[0] = pb[0];
+        pb_prev[1] = pb[1];
         if (lane == 0) votes[i & 1][wave] = __builtin_amdgcn_ballot_w64(need) != 0;
-        // tile i + 1 must have landed: tiles i + 2 and i + 3 may stay in flight
+        // tile i + 1 must have landed: tile i + 2 may stay in flight
         if (ahead)
-          wait_vm_lgkm0<2 * kDmaPerWave>();
-        else if (i + 2 < n_tot)
           wait_vm_lgkm0<kDmaPerWave>();
         else
           wait_vm_lgkm0<0>();
@@ -418,11 +472,19 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
           again = true;
           break;
         }
-        cur = (cur + 1 == kStages) ? 0 : cur + 1;
       }
       if (!again) {  // the last tile's votes have not been looked at yet
         const int4 last = *(const int4*)votes[(n_tot - 1) & 1];
-        if (!(last.x | last.y | last.z | last.w)) break;
+        if (!(last.x | last.y | last.z | last.w)) {
+          // the last tile's P.V (its stage is no longer written)
+          MlaPV pv;
+          pv.start(smem + ((n_tot - 1) & (kStages - 1)) * kTileBytes, vofs0, vofs1);
+          pv.step<true>(0, acc, pb_prev);
+          pv.step<true>(1, acc, pb_prev);
+#pragma unroll
+          for (int f = 2; f < MlaPV::kFrags; ++f) pv.step<false>(f, acc, pb_prev);
+          break;
+        }
       }
       // Restart with the raised reference maxima: drop what was accumulated.
       wait_vm_lgkm0<0>();

@@ -1,0 +1,147 @@
+// da_merge.h -- log-sum-exp merge of split-K partials for one row (the body of
+// the splitk_reduce kernel).
+//
+// Per row: M = max(max_p m_p, sigma), w_p = l_p * exp(m_p - M) (0 when l_p = 0),
+// L = sum_p w_p + exp(sigma - M), out = sum_p w_p * O_p / L, lse = M + ln L
+// ("mha_decoding_single_batch_pipelined", description: the mha_splitk_reduce
+// pass).  One wave per row: lanes take the partitions' (m_p, l_p) 64 at a time,
+// so the row max and the weights need one load round trip and two wave
+// reductions; the weights are then broadcast one partition at a time through
+// scalar lane reads while every lane accumulates its DV/64 consecutive columns
+// of O_p (one coalesced row read per partition, up to 32 partitions in flight).
+// Empty partitions (weight 0) are skipped without loading their row.
+#pragma once
+
+#include "da_device.h"
+
+namespace da {
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, shfl_xor(x, s));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x += shfl_xor(x, s);
+  return x;
+}
+
+template <int EPL>
+struct MergeCols {
+  float v[EPL];
+};
+
+template <int EPL>
+__device__ __forceinline__ MergeCols<EPL> merge_load_cols(const float* p) {
+  MergeCols<EPL> c;
+  if constexpr (EPL % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < EPL / 4; ++i) {
+      const float4 f = *(const float4*)(p + 4 * i);
+      c.v[4 * i] = f.x;
+      c.v[4 * i + 1] = f.y;
+      c.v[4 * i + 2] = f.z;
+      c.v[4 * i + 3] = f.w;
+    }
+  } else if constexpr (EPL == 2) {
+    const float2 f = *(const float2*)p;
+    c.v[0] = f.x;
+    c.v[1] = f.y;
+  } else {
+    c.v[0] = *p;
+  }
+  return c;
+}
+
+// Merges row `row` (of `rows` per partition) of part_o [P, rows, DV],
+// part_m / part_l [P, rows]; writes out[row, :] (bf16 or fp32) and lse[row]
+// (if lse).  Called by all 64 lanes of one wave; sink (or nullptr) is indexed by
+// row % num_heads.
+template <int DV, bool BF16OUT>
+__device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
+                                          const float* __restrict__ part_m,
+                                          const float* __restrict__ part_l, int P, int rows,
+                                          int row, const float* __restrict__ sink,
+                                          int num_heads, void* __restrict__ out,
+                                          float* __restrict__ lse, int lane) {
+  constexpr int EPL = DV / 64;  // consecutive columns per lane
+  // Partial rows requested ahead: 64 values per lane in flight (8 rows at
+  // DV = 512, 32 at DV <= 128, where a long split of few rows is latency bound).
+  constexpr int kInFlight = (64 / EPL) < 32 ? (64 / EPL) : 32;
+  float mx = kNegInf;
+  for (int pp = lane; pp < P; pp += 64) {
+    const float lp = part_l[(size_t)pp * rows + row];
+    if (lp > 0.f) mx = fmaxf(mx, part_m[(size_t)pp * rows + row] * kLog2e);
+  }
+  float M = wave_max(mx);
+  float sig = kNegInf;
+  if (sink) {
+    sig = sink[row % num_heads] * kLog2e;
+    M = fmaxf(M, sig);
+  }
+  const float Ms = (M == kNegInf) ? 0.f : M;
+
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float lsum = 0.f;
+  const float* orow = part_o + (size_t)row * DV + lane * EPL;
+  const size_t pstride = (size_t)rows * DV;
+  for (int base = 0; base < P; base += 64) {
+    const int pp = base + lane;  // this lane's partition of the chunk and its weight
+    float w = 0.f;
+    if (pp < P) {
+      const float lp = part_l[(size_t)pp * rows + row];
+      if (lp > 0.f) w = lp * fast_exp2(part_m[(size_t)pp * rows + row] * kLog2e - Ms);
+    }
+    lsum += w;
+    const int n = min(64, P - base);
+    // kInFlight partition rows are requested before any is used, without
+    // branches (a branch around each load makes the compiler wait for every
+    // load at the join).  A slot past the end of the chunk or of an empty
+    // partition (weight 0) re-reads the first row of the batch, already in
+    // flight, and a select drops its value (j + u <= 63 for the lane read).
+    for (int j = 0; j < n; j += kInFlight) {
+      float wj[kInFlight];
+      MergeCols<EPL> c[kInFlight];
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u) {
+        wj[u] = (j + u < n)
+                    ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u))
+                    : 0.f;
+        const int src = base + j + (wj[u] != 0.f ? u : 0);
+        c[u] = merge_load_cols<EPL>(orow + (size_t)src * pstride);
+      }
+#pragma unroll
+      for (int u = 0; u < kInFlight; ++u)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float t = fmaf(wj[u], c[u].v[e], acc[e]);
+          acc[e] = (wj[u] != 0.f) ? t : acc[e];
+        }
+    }
+  }
+  float L = wave_sum(lsum);
+  if (sink) L += fast_exp2(sig - Ms);
+
+  const bool any = L > 0.f;
+  const float inv = any ? 1.f / L : 0.f;
+  if constexpr (BF16OUT) {
+    uint16_t* dst = (uint16_t*)out + (size_t)row * DV + lane * EPL;
+    if constexpr (EPL == 1) {
+      dst[0] = to_bf16(acc[0] * inv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; e += 2)
+        *(uint32_t*)(dst + e) = pack_bf16(acc[e] * inv, acc[e + 1] * inv);
+    }
+  } else {
+    float* dst = (float*)out + (size_t)row * DV + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[e] * inv;
+  }
+  if (lse && lane == 0) lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
+}
+
+}  // namespace da

@@ -213,3 +213,20 @@ def test_prepared_call_matches_direct():
         assert got_out is out and got_lse is lse
         assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
         assert torch.equal(lse, ref_lse)
+
+
+def test_workspace_reuse_across_partition_counts():
+    """Consecutive decode_attention() calls that share one workspace, sized for
+    the largest P, with different inputs and partition counts are each correct."""
+    from gpu_util import compare, run_oracle
+    wl = W.Workload("ws_reuse", 8951, batch=3, num_heads=16, kv_heads=4, depth=128,
+                    max_seq_len=900, page_size=64, ragged=(1, 900, 1), sink=True)
+    B, H = wl.batch, wl.num_heads
+    ws = torch.empty(DA.decode_workspace_size(7, B, 1, H, wl.depth), dtype=torch.uint8,
+                     device="cuda")
+    for variant, P in ((0, 7), (1, 3), (2, 7), (3, 1), (4, 5)):
+        inp = W.make_inputs(wl, variant=variant)
+        dev = device_inputs(inp)
+        out, lse = run_gpu(wl, dev, P, workspace=ws)
+        ref_out, ref_lse = run_oracle(wl, inp)
+        compare(wl, out, lse, ref_out, ref_lse, what=f"workspace reuse P={P}")

@@ -75,3 +75,26 @@ def test_mla_score_jump_restart():
     # the 1e-2 absolute bound: allow one bf16 ulp of the reference on top.
     for P in (1, 2):
         check(wl, num_partitions=P, inp=inp, what=f"mla score jump P={P}", ulp_rel=True)
+
+
+def test_mla_partials_plus_reduce_equals_full_call():
+    """mla_decode() with P > 1 equals, bit for bit, its two halves called through
+    the boundary: the partials pass, then splitk_reduce()."""
+    import torch
+    from decode_attention_07_amd import binding as DA
+    from gpu_util import device_inputs, run_gpu
+    wl = W.Workload("mla_halves", 9500, batch=3, num_heads=128, kv_heads=1, depth=576,
+                    depth_v=512, max_seq_len=700, q_len=2, mla=True, causal=True,
+                    ragged=(2, 700, 0), scale=1.0 / np.sqrt(192.0), sink=True)
+    inp = W.make_inputs(wl)
+    dev = device_inputs(inp)
+    P = 3
+    out, lse = run_gpu(wl, dev, P)
+    ws = DA.mla_decode_partials(dev["q"], dev["k"], scale=wl.softmax_scale, num_partitions=P,
+                                valid_length=dev["valid_length"], causal=True)
+    po, pm, ps = DA.workspace_views(ws, P, wl.batch, wl.q_len, wl.num_heads, wl.dv)
+    out2, lse2 = DA.splitk_reduce(po, pm, ps, num_q_heads=wl.num_heads,
+                                  sink_weights=dev["sink"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(-1, wl.dv).view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse.view(-1), lse2)

@@ -1,8 +1,8 @@
 // mla_mfma.hip -- matrix-core MLA decode for gfx950 ("flare_mla_decoding_dispatch").
 //
-// One KV head (kv_num_heads must be 1), depth 576 for q.K^T and V = K[..., :512]
-// read from the same cache rows ("V is derived as K[:, :, :depth_v], so V is not
-// loaded separately").  The q_len tokens of a sequence and its num_q_heads heads
+// One KV head, depth 576 for q.K^T, and V = K[..., :512] taken from the same
+// cache rows (Args `k` and `kv_num_heads` of that page: V has no operand of its
+// own).  The q_len tokens of a sequence and its num_q_heads heads
 // are folded into one set of T*H rows (the MTP token fold); a block owns 128 of
 // those rows (4 waves x 32 rows, one wave per SIMD) and one partition of the
 // keys, so every cache row of the partition is read from HBM once per 128 rows.

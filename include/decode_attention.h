@@ -154,9 +154,9 @@ int decode_attention_partials(const void* q, const void* k, const void* v,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * MLA decode ("flare_mla_decoding_dispatch"): one KV head ("kv_num_heads ...
- * Must be 1 for MLA"), depth 576, and V = K[..., :512] read from the same cache
- * rows ("V is derived as K[:, :, :depth_v], so V is not loaded separately").
+ * MLA decode ("flare_mla_decoding_dispatch", Args `k` and `kv_num_heads`): a
+ * single KV head, depth 576, and no separate V operand: V is the first 512
+ * columns of each K row, taken from the same cache rows.
  *   q    bf16 [batch, q_len, num_q_heads, 576]; the q_len tokens of a sequence
  *        are folded into one block of rows (the MTP token fold).
  *   kv   bf16 dense [batch, max_seq_len, 1, 576] or pool [num_pages, page_size, 1, 576]

@@ -10,16 +10,15 @@
  *   out[d] = sum_j softmax_j( scale * <q, k_j> ) * v_j[d]      (visible keys j)
  *
  * as stated in the description of "mha_decoding_single_batch_pipelined"
- * (FA2 decode: the decoding, single-query case of attention, Args `scale`
- * "applied to Q.K^T") and in "mha_sm100_dispatch", Args `scale` (applied to the
- * Q@K' product before softmax).  It is written out directly, two passes over
+ * (FA2 decode: attention for a single query per row) and in
+ * "mha_sm100_dispatch", Args `scale` (the factor on the product of Q and K
+ * before the softmax).  It is written out directly, two passes over
  * the keys (max, then exp-sum and weighted sum), no online rescaling, no
  * blocking, everything accumulated in double.
  *
- * Readings taken where the pages leave a step open (each also listed in the
- * design notes):
- *   - KV head of query head h is floor(h / group): `group` is the number of
- *     query heads per KV head ("mha_sm100_dispatch", Parameters `group`).
+ * Readings taken where the pages leave a step open:
+ *   - KV head of query head h is floor(h / group), `group` counting the query
+ *     heads that share one KV head ("mha_sm100_dispatch", Parameters `group`).
  *   - Keys visible to row (b, t): N_b = valid_length[b] if given, else
  *     max_seq_len ("mha_sm100_dispatch", Args `valid_length`,
  *     `max_cache_valid_length_arg`).  N_b counts the current tokens too.  With
@@ -33,9 +32,9 @@
  *     score sigma_h and a zero value row), not multiplied by `scale`.
  *   - LSE = m + ln(l) of the full denominator, sink included.
  *   - A row with no visible key and no sink: out = 0, LSE = -inf.
- *   - Split-K ("mha_decoding_single_batch_pipelined", description: each block
- *     takes a contiguous slice of the key dimension and records its exp-sum and
- *     running max for a later "mha_splitk_reduce" pass): partition p covers
+ *   - Split-K ("mha_decoding_single_batch_pipelined", description: the keys
+ *     are cut into consecutive ranges, one per block, whose max and exp-sum a
+ *     separate merge pass combines): partition p covers
  *     keys [p*C, (p+1)*C); its partial output is normalised by its own exp-sum;
  *     the merge is by log-sum-exp.
  *

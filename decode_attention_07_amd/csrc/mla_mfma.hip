@@ -64,12 +64,12 @@ constexpr float kHeadroom = 100.0f;          // largest exp2 argument (log2 unit
 // wave writes lds_base + 16 * i.  The cache is streamed through once per block
 // and every instruction covers whole lines: non-temporal hint (nt).  Issued
 // through inline asm so that the compiler does not serialise later LDS reads of
-// other stages behind it; completion is tracked with explicit vmcnt waits.
+// other stages behind it; completion is tracked with explicit vmcnt waits.  The
+// LDS address goes in through an m0 operand, so the compiler computes it into m0
+// directly (one scalar op per load).
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :
-               : "v"(voff), "s"(base), "s"(lds_base)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(base), "{m0}"(lds_base)
+               : "memory");
 }
 
 __device__ __forceinline__ constexpr int swz(int key) { return 4 * ((key >> 1) & 1) + ((key >> 2) & 3); }
@@ -121,14 +121,17 @@ __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage,
   const uint4 t1 = *(const uint4*)(tab + 4);
   const uint32_t e[kDmaPerWave] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w, tab[8]};
   const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + wave * 1024);
+  if (nvalid >= kBN) {  // whole tile (uniform branch)
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    uint32_t off = e[i] >> 5;
-    if (nvalid < kBN) {
+    for (int i = 0; i < kDmaPerWave; ++i) dma16(base, e[i] >> 5, dst + i * kWaves * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      uint32_t off = e[i] >> 5;
       const int key = (int)(e[i] & 31u);
       if (key >= nvalid) off -= (uint32_t)key * kRowBytes;
+      dma16(base, off, dst + i * kWaves * 1024);
     }
-    dma16(base, off, dst + i * kWaves * 1024);
   }
 }
 
@@ -275,12 +278,17 @@ struct MlaPV {
 // partition with the raised reference.  The weights enter the MFMA rounded to
 // bf16; their rounded sum (lsr) is what O is normalised by, so the effective
 // weights still sum to one.
-template <bool PV>
+//
+// The scale enters once per weight, p = 2^(fma(q.k, sl, -m)) with sl = scale *
+// log2(e) >= 0 (a negative scale was moved into Q by flipping its sign), and the
+// row max is taken over the unscaled scores (sl >= 0 keeps their order).  Only
+// tiles that reach past some row's last visible key (MASKED) compare keys.
+template <bool PV, bool MASKED>
 __device__ __forceinline__ void mla_softmax_pv(const f32x16_t& s0, const f32x16_t& s1, MlaPV& pv,
                                                const bf16x8_t (&pb_prev)[2], bf16x8_t (&pb)[2],
                                                f32x16_t (&acc)[kDT], float& m, float& lsum,
-                                               float& lsr, int j0, bool masked, int hi,
-                                               float scale_log2, bool& restart) {
+                                               float& lsr, int j0, int hi, float sl,
+                                               bool& restart) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   int f = 0;
@@ -301,27 +309,27 @@ __device__ __forceinline__ void mla_softmax_pv(const f32x16_t& s0, const f32x16_
   float mx = kNegInf;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    float v = (s0[j] + s1[j]) * scale_log2;
-    if (masked) v = (j0 + c32_row(j, g) < hi) ? v : kNegInf;
-    x[j] = v;
-    mx = fmaxf(mx, v);
+    x[j] = s0[j] + s1[j];
+    mx = fmaxf(mx, (!MASKED || j0 + c32_row(j, g) < hi) ? x[j] : kNegInf);
     if (j % 2 == 1) {
       pin(mx);
       pv_step();
     }
   }
   mx = max_xor32(mx);
+  mx = (mx == kNegInf) ? kNegInf : mx * sl;
   pin(mx);
   pv_step();
   const bool grow = mx > m + kHeadroom;
   restart = restart || (grow && m != kNegInf);  // a row's first visible tile: acc is still 0
   m = grow ? mx : m;
-  float ms = (m == kNegInf) ? 0.f : m;
-  pin(ms);
+  float nms = (m == kNegInf) ? 0.f : -m;
+  pin(nms);
   float ps = 0.f;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    x[j] = fast_exp2(x[j] - ms);
+    x[j] = fast_exp2(fmaf(x[j], sl, nms));
+    if (MASKED) x[j] = (j0 + c32_row(j, g) < hi) ? x[j] : 0.f;
     ps += x[j];
     if (j % 2 == 1) {
       pin(ps);
@@ -336,7 +344,7 @@ __device__ __forceinline__ void mla_softmax_pv(const f32x16_t& s0, const f32x16_
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       w[q] = pack_bf16(x[8 * kh + 2 * q], x[8 * kh + 2 * q + 1]);
-      pr += bf16lo(w[q]) + bf16hi(w[q]);
+      pr = dot2_bf16(w[q], 0x3f803f80u, pr);  // + both rounded weights (times bf16 1.0)
       pin(pr);
       pv_step();
     }
@@ -346,6 +354,11 @@ __device__ __forceinline__ void mla_softmax_pv(const f32x16_t& s0, const f32x16_
 #pragma unroll
   for (int r = 0; r < MlaPV::kFrags; ++r) pv_step();  // the rest of the previous tile
 }
+
+template <bool V>
+struct BoolTag {
+  static constexpr bool value = V;
+};
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
@@ -424,8 +437,15 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     // below.
     mla_issue(p, lds0, b, k_lo, hmax, wave, tab);
     wait_vm_lgkm0<0>();
+    // Rows outside the fold get Q = 0; a negative scale flips Q's sign (exact).
+    const uint32_t qx = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int s = 0; s < kKS; ++s) qf[s] = row_ok ? qf[s] : bf16x8_t{};
+    for (int s = 0; s < kKS; ++s) {
+      uint4 u = __builtin_bit_cast(uint4, qf[s]);
+      u = make_uint4(u.x ^ qx, u.y ^ qx, u.z ^ qx, u.w ^ qx);
+      qf[s] = row_ok ? __builtin_bit_cast(bf16x8_t, u) : bf16x8_t{};
+    }
+    const float sl = fabsf(p.scale_log2);
     bf16x8_t pb_prev[2];
     for (;;) {  // one pass over the partition; repeated only after a restart
       // tile 0 is requested on entry; tile 1 now; wait for tile 0
@@ -436,12 +456,18 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         wait_vm_lgkm0<0>();
       }
       __syncthreads();
-      bool again = false;
-      for (int i = 0; i < n_tot; ++i) {
+      // One tile: returns true when the votes of the tile before it ask for a
+      // restart.  PV: contract the previous tile; MASKED: compare keys against
+      // each row's last visible key.  Tile 0, the tiles every row sees whole
+      // and the tail are three loops, so that each loop body holds a single
+      // copy of the softmax / P.V interleave (registers are all in use).
+      auto tile = [&](int i, auto pv_tag, auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool PV = decltype(pv_tag)::value;
+        constexpr bool MASKED = decltype(mask_tag)::value;
         // Votes of tile i - 1, acted upon after tile i (the load has landed by
         // then; what tile i adds is dropped with the rest on a restart).
         int4 prev = make_int4(0, 0, 0, 0);
-        if (i > 0) prev = *(const int4*)votes[(i - 1) & 1];
+        if (PV) prev = *(const int4*)votes[(i - 1) & 1];
         const bool ahead = i + 2 < n_tot;
         if (ahead)  // into the stage of tile i - 2, last read a barrier ago
           mla_issue(p, lds0 + ((i + 2) & (kStages - 1)) * kTileBytes, b, k_lo + (i + 2) * kBN,
@@ -451,14 +477,9 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         bool need = false;
         bf16x8_t pb[2];
         MlaPV pv;
-        if (i == 0) {
-          mla_softmax_pv<false>(s0, s1, pv, pb_prev, pb, acc, m, lsum, lsr, k_lo, 0 >= n_full,
-                                hi, p.scale_log2, need);
-        } else {
-          pv.start(smem + ((i - 1) & (kStages - 1)) * kTileBytes, vofs0, vofs1);
-          mla_softmax_pv<true>(s0, s1, pv, pb_prev, pb, acc, m, lsum, lsr, k_lo + i * kBN,
-                               i >= n_full, hi, p.scale_log2, need);
-        }
+        if (PV) pv.start(smem + ((i - 1) & (kStages - 1)) * kTileBytes, vofs0, vofs1);
+        mla_softmax_pv<PV, MASKED>(s0, s1, pv, pb_prev, pb, acc, m, lsum, lsr, k_lo + i * kBN,
+                                   hi, sl, need);
         pb_prev[0] = pb[0];
         pb_prev[1] = pb[1];
         if (lane == 0) votes[i & 1][wave] = __builtin_amdgcn_ballot_w64(need) != 0;
@@ -468,11 +489,12 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         else
           wait_vm_lgkm0<0>();
         __syncthreads();
-        if (prev.x | prev.y | prev.z | prev.w) {  // same votes in every wave
-          again = true;
-          break;
-        }
-      }
+        return (prev.x | prev.y | prev.z | prev.w) != 0;  // same votes in every wave
+      };
+      bool again = tile(0, BoolTag<false>{}, BoolTag<true>{});
+      int i = 1;
+      for (; !again && i < n_full; ++i) again = tile(i, BoolTag<true>{}, BoolTag<false>{});
+      for (; !again && i < n_tot; ++i) again = tile(i, BoolTag<true>{}, BoolTag<true>{});
       if (!again) {  // the last tile's votes have not been looked at yet
         const int4 last = *(const int4*)votes[(n_tot - 1) & 1];
         if (!(last.x | last.y | last.z | last.w)) {

@@ -98,3 +98,15 @@ def test_mla_partials_plus_reduce_equals_full_call():
     torch.cuda.synchronize()
     assert torch.equal(out.view(-1, wl.dv).view(torch.int16), out2.view(torch.int16))
     assert torch.equal(lse.view(-1), lse2)
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0 / np.sqrt(192.0), -0.05], ids=["zero", "neg", "neg_small"])
+@pytest.mark.parametrize("P", [1, 3])
+def test_mla_zero_and_negative_scale(scale, P):
+    """A zero or negative scale: the kernel folds the sign into Q (exact in bf16)
+    and applies the magnitude once per weight, after the row max; masked keys
+    (causal MTP, ragged tails) must still drop out when the scale is 0."""
+    wl = W.Workload(f"mla_scale_{P}_{int(round(scale * 1000))}", 9400 + P, batch=3,
+                    num_heads=128, kv_heads=1, depth=576, depth_v=512, max_seq_len=230, q_len=2,
+                    mla=True, causal=True, ragged=(1, 230, 1), scale=scale, sink=(P == 3))
+    check(wl, num_partitions=P)

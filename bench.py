@@ -216,8 +216,8 @@ def main():
     P = args.partitions or DA.num_partitions(B, T, H, wl.kv_heads, wl.depth, wl.dv, S,
                                              ragged=first.valid_length is not None)
     split = P > 1
-    ws = torch.empty(DA.decode_workspace_size(P, B, T, H, wl.dv), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.zeros(DA.decode_workspace_size(P, B, T, H, wl.dv), dtype=torch.uint8,
+                     device="cuda")  # zero-filled once: the work-queue word starts at 0
     out = torch.empty((B, T, H, wl.dv), dtype=dev_sets[0]["q"].dtype, device="cuda")
     lse = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
     po, pm, ps = DA.workspace_views(ws, P, B, T, H, wl.dv)

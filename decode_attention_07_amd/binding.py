@@ -24,7 +24,8 @@ DA_MAX_PARTITIONS = 1024
 MLA_DEPTH, MLA_DEPTH_V = 576, 512
 
 EXPORTS = ("decode_attention_status_string", "decode_num_partitions", "decode_workspace_size",
-           "decode_workspace_max_offset", "decode_workspace_sum_offset", "decode_attention",
+           "decode_workspace_o_offset", "decode_workspace_max_offset",
+           "decode_workspace_sum_offset", "decode_attention",
            "decode_attention_partials", "mla_decode", "mla_decode_partials", "splitk_reduce")
 
 _lock = threading.Lock()
@@ -43,8 +44,8 @@ def _declare(lib):
     lib.decode_attention_status_string.restype = ctypes.c_char_p
     lib.decode_num_partitions.argtypes = [i32] * 9
     lib.decode_num_partitions.restype = i32
-    for name in ("decode_workspace_size", "decode_workspace_max_offset",
-                 "decode_workspace_sum_offset"):
+    for name in ("decode_workspace_size", "decode_workspace_o_offset",
+                 "decode_workspace_max_offset", "decode_workspace_sum_offset"):
         getattr(lib, name).argtypes = [i32] * 5
         getattr(lib, name).restype = sz
     lib.decode_attention.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, i32, i32,
@@ -168,10 +169,12 @@ def workspace_views(workspace: torch.Tensor, num_partitions, batch, q_len, num_q
     """(part_o, part_max, part_sum) float32 views of a workspace (layout of the header)."""
     lib = library()
     rows = batch * q_len * num_q_heads
+    oo = lib.decode_workspace_o_offset(num_partitions, batch, q_len, num_q_heads, depth_v)
     mo = lib.decode_workspace_max_offset(num_partitions, batch, q_len, num_q_heads, depth_v)
     so = lib.decode_workspace_sum_offset(num_partitions, batch, q_len, num_q_heads, depth_v)
     n = num_partitions * rows
-    po = workspace[: n * depth_v * 4].view(torch.float32).view(num_partitions, rows, depth_v)
+    po = workspace[oo: oo + n * depth_v * 4].view(torch.float32).view(num_partitions, rows,
+                                                                      depth_v)
     pm = workspace[mo: mo + n * 4].view(torch.float32).view(num_partitions, rows)
     ps = workspace[so: so + n * 4].view(torch.float32).view(num_partitions, rows)
     return po, pm, ps
@@ -202,8 +205,8 @@ def _workspace(workspace, P, B, T, H, Dv, device, always=False):
     need = decode_workspace_size(P, B, T, H, Dv)
     if P == 1 and not always:
         return workspace, (0 if workspace is None else workspace.numel())
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is None:  # zero-filled: the work-queue word starts at 0
+        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
     elif workspace.numel() < need:
         raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
     return workspace, workspace.numel()

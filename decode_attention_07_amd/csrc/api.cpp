@@ -169,13 +169,19 @@ da::DecodeParams base_params(const Common& c, const void* q, const void* k, cons
   return p;
 }
 
-void ws_sections(void* ws, int P, size_t rows, int depth_v, float** po, float** pm, float** pl) {
+// Workspace sections: the work-queue word (its own 256 bytes, at offset 0 so
+// that its place does not depend on P), part_o, part_max, part_sum.
+constexpr size_t kQueueBytes = 256;
+
+void ws_sections(void* ws, int P, size_t rows, int depth_v, float** po, float** pm, float** pl,
+                 unsigned long long** queue) {
   char* base = (char*)ws;
   const size_t o_bytes = align_up((size_t)P * rows * depth_v * sizeof(float));
   const size_t m_bytes = align_up((size_t)P * rows * sizeof(float));
-  *po = (float*)base;
-  *pm = (float*)(base + o_bytes);
-  *pl = (float*)(base + o_bytes + m_bytes);
+  *queue = (unsigned long long*)base;
+  *po = (float*)(base + kQueueBytes);
+  *pm = (float*)(base + kQueueBytes + o_bytes);
+  *pl = (float*)(base + kQueueBytes + o_bytes + m_bytes);
 }
 
 hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16,
@@ -223,21 +229,30 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
   p.lse = lse;
   p.write_partials = split ? 1 : 0;
   float *po = nullptr, *pm = nullptr, *pl = nullptr;
-  if (split) ws_sections(workspace, P, rows, p.depth_v, &po, &pm, &pl);
+  unsigned long long* queue = nullptr;
+  if (split) ws_sections(workspace, P, rows, p.depth_v, &po, &pm, &pl, &queue);
   p.part_o = po;
   p.part_m = pm;
   p.part_l = pl;
+  // Ragged batches on the bf16 GQA kernel take their work items from a queue
+  // (blocks that finish early take more), with two resident blocks per CU.
+  p.queue = nullptr;
+  p.queue_blocks = 0;
+  if (split && plan.variant == kStream && c.valid_length && plan.row_blocks == 1) {
+    p.queue = queue;
+    p.queue_blocks = 2 * device_cus();
+  }
 
   hipStream_t s = (hipStream_t)stream;
   if (log_enabled())
     std::fprintf(stderr,
                  "[decode_attention] variant=%s B=%d T=%d H=%d KVH=%d D=%d Dv=%d S=%d P=%d C=%d "
-                 "rows/block=%d row_blocks=%d grid=%d paged=%d reduce=%d\n",
+                 "rows/block=%d row_blocks=%d grid=%d paged=%d reduce=%d queue=%d\n",
                  variant_name(plan.variant), c.batch, c.q_len, c.num_q_heads, p.num_kv_heads,
                  p.depth, p.depth_v, c.max_seq_len, P, p.keys_per_partition,
                  plan.rows_per_block, plan.row_blocks,
                  P * c.batch * p.num_kv_heads * plan.row_blocks, c.page_table != nullptr,
-                 (!partials_only && P > 1) ? 1 : 0);
+                 (!partials_only && P > 1) ? 1 : 0, p.queue != nullptr);
   if (launch_partition_pass(p, plan.variant, bf16, s) != hipSuccess) return DA_ERR_HIP;
   if (!partials_only && P > 1) {
     if (da::launch_splitk_reduce(po, pm, pl, P, (int)rows, c.num_q_heads, p.depth_v, sink, out,
@@ -284,11 +299,12 @@ int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_head
       depth_v < 1 || max_seq_len < 0 || num_q_heads % num_kv_heads != 0)
     return DA_ERR_INVALID_ARG;
   if (num_cus <= 0) num_cus = device_cus();
-  // The bf16 kernels keep one block per CU resident (their LDS rings take most
-  // of the CU's LDS), so a dense batch wants about one block per CU; a ragged
-  // one wants smaller partitions so that its long sequences spread out.
-  const int per_cu = ragged ? 8 : 1;
-  if (depth == kMlaDepth && num_kv_heads == 1) {
+  // A dense batch wants about one block per CU.  A ragged one wants smaller
+  // partitions so that its long sequences spread out: the GQA kernel takes
+  // them from a work queue (about 16 items per CU), MLA from its grid.
+  const bool mla = depth == kMlaDepth && num_kv_heads == 1;
+  const int per_cu = ragged ? (mla ? 8 : 16) : 1;
+  if (mla) {
     const Plan pl = plan_mla(q_len, num_q_heads);
     // MLA partials are 512 wide per row: keep partitions long so the partial
     // write-back stays a small fraction of the cache read.
@@ -303,14 +319,16 @@ size_t decode_workspace_size(int num_partitions, int batch, int q_len, int num_q
                              int depth_v) {
   if (num_partitions < 1 || batch < 0 || q_len < 1 || num_q_heads < 1 || depth_v < 1) return 0;
   const size_t rows = (size_t)batch * q_len * num_q_heads;
-  return align_up((size_t)num_partitions * rows * depth_v * sizeof(float)) +
+  return kQueueBytes + align_up((size_t)num_partitions * rows * depth_v * sizeof(float)) +
          2 * align_up((size_t)num_partitions * rows * sizeof(float));
 }
+
+size_t decode_workspace_o_offset(int, int, int, int, int) { return kQueueBytes; }
 
 size_t decode_workspace_max_offset(int num_partitions, int batch, int q_len, int num_q_heads,
                                    int depth_v) {
   const size_t rows = (size_t)batch * q_len * num_q_heads;
-  return align_up((size_t)num_partitions * rows * depth_v * sizeof(float));
+  return kQueueBytes + align_up((size_t)num_partitions * rows * depth_v * sizeof(float));
 }
 
 size_t decode_workspace_sum_offset(int num_partitions, int batch, int q_len, int num_q_heads,

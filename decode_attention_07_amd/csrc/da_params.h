@@ -28,6 +28,11 @@ struct DecodeParams {
   int row_blocks;               // row tiles per (batch, KV head)
   int write_partials;           // 1: write part_*; 0: write out / lse directly
   float scale_log2;             // scale * log2(e)
+  // Work queue of the bf16 GQA kernel (ragged split calls; nullptr otherwise):
+  // one 64-bit word in the workspace, low half = next work item, high half =
+  // blocks done; zero between calls.
+  unsigned long long* queue;
+  int queue_blocks;             // persistent blocks launched when queue is set
 };
 
 // Row-block geometry of a (batch, KV head): T*group rows (token-major:

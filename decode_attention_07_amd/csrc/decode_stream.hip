@@ -122,7 +122,13 @@ __device__ __forceinline__ void stream_issue(const DecodeParams& p, int b, int g
                                              int lane) {
   using C = StreamCfg<D>;
   const size_t row0 = stream_row0(p, b, j0);
-  const size_t head_off = (row0 * p.num_kv_heads + g) * (size_t)C::ROW;
+  // Uniform by construction; read through readfirstlane so that the compiler
+  // keeps it in scalar registers (the loads take a scalar base) even where it
+  // reaches here through a phi after a divergent branch.
+  const size_t head_off0 = (row0 * p.num_kv_heads + g) * (size_t)C::ROW;
+  const size_t head_off =
+      ((size_t)__builtin_amdgcn_readfirstlane((uint32_t)(head_off0 >> 32)) << 32) |
+      (size_t)__builtin_amdgcn_readfirstlane((uint32_t)head_off0);
   const char* kb = (const char*)p.k + head_off;
   const char* vb = (const char*)p.v + head_off;
   const uint32_t rs = (uint32_t)p.num_kv_heads * C::ROW;  // bytes between keys of a head
@@ -215,27 +221,14 @@ __device__ __forceinline__ void stream_tile(const char* st, const bf16x8_t (&qf)
   }
 }
 
+// One work item: rows rb*16.. of (sequence b, KV head g) over partition pidx.
 template <int D>
-__global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
+__device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, int b, int g,
+                                            int pidx, int rb) {
   using C = StreamCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id_uniform();
   const int c16 = lane & 15, g16 = lane >> 4;
-
-  // Block -> (partition, sequence, KV head, row block); the row blocks of one
-  // (partition, sequence, KV head) get ids 8 apart, so that they share an XCD
-  // and its L2 serves the second read of their tiles.
-  const int id = blockIdx.x;
-  const int xcd = id & 7;
-  const int rq = id >> 3;
-  const int rb = rq % p.row_blocks;
-  int work = (rq / p.row_blocks) * 8 + xcd;
-  const int n_work = p.num_partitions * p.batch * p.num_kv_heads;
-  if (work >= n_work) return;  // padding block: no barrier reached yet
-  const int g = work % p.num_kv_heads; work /= p.num_kv_heads;
-  const int b = work % p.batch;
-  const int pidx = work / p.batch;
 
   // This lane's query row (16 rows per block: rows of the token-major fold).
   const int nrows = fold_rows(p);
@@ -393,6 +386,56 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
   }
 }
 
+// Static mapping: block -> (partition, sequence, KV head, row block); the row
+// blocks of one (partition, sequence, KV head) get ids 8 apart, so that they
+// share an XCD and its L2 serves the second read of their tiles.
+//
+// Work queue (ragged batches, one row block): items (partition, sequence, KV
+// head), partition-major, so that long items tend to go first.  A block takes
+// its next item, (queue's low half)++, only when it has finished the last one
+// (a block that reserved ahead would hold items back from blocks that run out
+// first), until the items run out; blocks with shorter items, or on faster
+// parts of the chip, take more.  The queue is a single 64-bit word, so relaxed
+// atomics order every access to it: a block counts itself done in the high half
+// after its last take, and the block that completes the count (every take is
+// then behind it) sets the word back to zero for the next call.
+template <int D>
+__global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
+  using C = StreamCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  __shared__ int s_next[2];
+  const int n_work = p.num_partitions * p.batch * p.num_kv_heads;
+  if (p.queue == nullptr) {
+    const int id = blockIdx.x;
+    const int xcd = id & 7;
+    const int rq = id >> 3;
+    const int rb = rq % p.row_blocks;
+    int work = (rq / p.row_blocks) * 8 + xcd;
+    if (work >= n_work) return;  // padding block: no barrier reached yet
+    const int g = work % p.num_kv_heads;
+    work /= p.num_kv_heads;
+    stream_item<D>(p, smem, work % p.batch, g, work / p.batch, rb);
+    return;
+  }
+  // s_next is double-buffered: slot it & 1 is written again two barriers after
+  // every wave has read it.
+  for (int it = 0;; ++it) {
+    if (threadIdx.x == 0) s_next[it & 1] = (int)(uint32_t)atomicAdd(p.queue, 1ull);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
+    if (item >= n_work) break;
+    int w = item;
+    const int g = w % p.num_kv_heads;
+    w /= p.num_kv_heads;
+    stream_item<D>(p, smem, w % p.batch, g, w / p.batch, 0);
+    __syncthreads();  // the LDS is free again
+  }
+  if (threadIdx.x == 0) {
+    const unsigned long long old = atomicAdd(p.queue, 1ull << 32);
+    if ((uint32_t)(old >> 32) == gridDim.x - 1) atomicExch(p.queue, 0ull);
+  }
+}
+
 }  // namespace
 
 int stream_rows_per_block() { return 16; }
@@ -400,7 +443,11 @@ int stream_step_keys() { return kTK; }
 
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s) {
   const int n_work = p.num_partitions * p.batch * p.num_kv_heads;
-  const int grid = ((n_work + 7) / 8) * 8 * p.row_blocks;
+  int grid = ((n_work + 7) / 8) * 8 * p.row_blocks;
+  if (p.queue) {
+    if (p.row_blocks != 1 || p.queue_blocks < 1) return hipErrorInvalidValue;
+    grid = n_work < p.queue_blocks ? n_work : p.queue_blocks;
+  }
   if (p.depth == 64)
     hipLaunchKernelGGL(decode_stream_kernel<64>, dim3(grid), dim3(256), 0, s, p);
   else

@@ -98,15 +98,29 @@ int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_head
  * decode_attention() / mla_decode() call that runs with one partition does not
  * touch the workspace (it may be NULL); the *_partials() passes always write it.
  * Workspace layout (each section 256-byte aligned):
+ *   queue    uint64, 256 bytes        work queue of ragged calls (below), at offset 0
  *   part_o   fp32 [P, rows, depth_v]  partial outputs, each normalised by its exp-sum
  *   part_max fp32 [P, rows]           partial max, natural-log units (-inf if empty)
  *   part_sum fp32 [P, rows]           partial exp-sum relative to part_max (0 if empty)
  * with rows = batch * q_len * num_q_heads.  Returns 0 for invalid arguments.
+ *
+ * Work queue.  A bf16 decode_attention() / decode_attention_partials() call
+ * with valid_length, more than one partition and at most 16 query rows per KV
+ * head runs a fixed set of blocks that take their (partition, sequence, KV
+ * head) items from the queue word with device-scope atomics, so that blocks
+ * whose items are short, or which run on faster parts of the chip, take more.
+ * The word must be zero when such a call starts: fill a new workspace with zero
+ * bytes once (hipMemset) before its first use; every completed call leaves it
+ * zero again.  Its place does not depend on the partition count, so one
+ * workspace sized for the largest P serves calls with any P.  Calls that share a
+ * workspace must not run concurrently.
  */
 size_t decode_workspace_size(int num_partitions, int batch, int q_len, int num_q_heads,
                              int depth_v);
 
-/* Byte offsets of part_max and part_sum inside that workspace (part_o is at 0). */
+/* Byte offsets of part_o, part_max and part_sum inside that workspace. */
+size_t decode_workspace_o_offset(int num_partitions, int batch, int q_len, int num_q_heads,
+                                 int depth_v);
 size_t decode_workspace_max_offset(int num_partitions, int batch, int q_len, int num_q_heads,
                                    int depth_v);
 size_t decode_workspace_sum_offset(int num_partitions, int batch, int q_len, int num_q_heads,
@@ -130,7 +144,8 @@ size_t decode_workspace_sum_offset(int num_partitions, int batch, int q_len, int
  *                   > 0 is used verbatim.
  *   mask            DA_MASK_NONE or DA_MASK_CAUSAL.
  *   workspace       >= decode_workspace_size(P, ...) bytes when P > 1 (may be
- *                   NULL when P == 1).
+ *                   NULL when P == 1); its queue word zero (see
+ *                   decode_workspace_size).
  */
 int decode_attention(const void* q, const void* k, const void* v, const uint32_t* page_table,
                      int page_size, int max_pages_per_seq, const uint32_t* valid_length,

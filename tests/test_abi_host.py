@@ -20,7 +20,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(DA.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
@@ -71,10 +71,14 @@ def test_workspace_layout():
     P, B, T, H, Dv = 4, 3, 2, 5, 128
     rows = B * T * H
     o = P * rows * Dv * 4
+    oo = lib.decode_workspace_o_offset(P, B, T, H, Dv)
     mo = lib.decode_workspace_max_offset(P, B, T, H, Dv)
     so = lib.decode_workspace_sum_offset(P, B, T, H, Dv)
     size = lib.decode_workspace_size(P, B, T, H, Dv)
-    assert mo >= o and mo % 256 == 0 and mo - o < 256
+    # the 8-byte work-queue word owns the first 256 bytes, whatever P is
+    assert oo == 256 and all(lib.decode_workspace_o_offset(q, B, T, H, Dv) == 256
+                             for q in (1, 2, 7, 64))
+    assert mo >= oo + o and mo % 256 == 0 and mo - oo - o < 256
     assert so >= mo + P * rows * 4 and so % 256 == 0
     assert size >= so + P * rows * 4 and size % 256 == 0
     assert lib.decode_workspace_size(0, B, T, H, Dv) == 0

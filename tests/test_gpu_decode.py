@@ -216,13 +216,14 @@ def test_prepared_call_matches_direct():
 
 
 def test_workspace_reuse_across_partition_counts():
-    """Consecutive decode_attention() calls that share one workspace, sized for
-    the largest P, with different inputs and partition counts are each correct."""
+    """Consecutive decode_attention() calls that share one zero-filled workspace,
+    sized for the largest P, with different inputs and partition counts are each
+    correct, and each leaves the work-queue word of the ragged calls at zero."""
     from gpu_util import compare, run_oracle
     wl = W.Workload("ws_reuse", 8951, batch=3, num_heads=16, kv_heads=4, depth=128,
                     max_seq_len=900, page_size=64, ragged=(1, 900, 1), sink=True)
     B, H = wl.batch, wl.num_heads
-    ws = torch.empty(DA.decode_workspace_size(7, B, 1, H, wl.depth), dtype=torch.uint8,
+    ws = torch.zeros(DA.decode_workspace_size(7, B, 1, H, wl.depth), dtype=torch.uint8,
                      device="cuda")
     for variant, P in ((0, 7), (1, 3), (2, 7), (3, 1), (4, 5)):
         inp = W.make_inputs(wl, variant=variant)
@@ -230,3 +231,15 @@ def test_workspace_reuse_across_partition_counts():
         out, lse = run_gpu(wl, dev, P, workspace=ws)
         ref_out, ref_lse = run_oracle(wl, inp)
         compare(wl, out, lse, ref_out, ref_lse, what=f"workspace reuse P={P}")
+        assert int(ws[:8].view(torch.int64).item()) == 0, "work-queue word not back at zero"
+
+
+def test_work_queue_many_items_per_block():
+    """A ragged batch with far more (partition, sequence, KV head) items than
+    resident blocks: every block runs many items from the queue, short and
+    empty ones among them, and the result matches the oracle at every P."""
+    from gpu_util import check
+    wl = W.Workload("queue_many", 8960, batch=48, num_heads=32, kv_heads=8, depth=128,
+                    max_seq_len=3000, page_size=32, ragged=(1, 3000, 5), sink=True)
+    for P in (8, 23, 64):
+        check(wl, num_partitions=P)

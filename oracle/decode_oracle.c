@@ -51,9 +51,27 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+/* Problem dtype 2: q in bf16, k and v in ORACLE_E4M3 with per-tensor scales. */
+#define ORACLE_BF16_Q_E4M3_KV 2
+#define ORACLE_E4M3 3
+
+/* 8-bit float e4m3 (the OCP FP8 E4M3 format): 1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6;
+ * there is no infinity, and S.1111.111 is NaN. */
+static double e4m3_value(uint8_t c) {
+  int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
 
 static double elem(const void* base, size_t idx, int dtype) {
   if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+  if (dtype == ORACLE_E4M3) return e4m3_value(((const uint8_t*)base)[idx]);
   uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
@@ -65,7 +83,10 @@ typedef struct {
   const void* q;              /* [B, T, H, D]                                   */
   const void* k;              /* contiguous [B, S, KVH, D] or pool [pages, ps, KVH, D] */
   const void* v;              /* same layout with Dv, or NULL => V = K[..., :Dv] */
-  int dtype;
+  int q_dtype, kv_dtype;      /* element types of q, and of k and v             */
+  double k_scale, v_scale;    /* real key = k_scale * stored element; real value
+                                 = v_scale * stored element (k_scale when V is a
+                                 slice of K: the same stored numbers)            */
   const uint32_t* page_table; /* [B, max_pages] or NULL (contiguous)            */
   int page_size, max_pages;
   const uint32_t* valid_length; /* [B] or NULL                                  */
@@ -89,12 +110,12 @@ static size_t kv_index(const problem_t* p, int b, int j, int g, int d, int width
 }
 
 static double key_elem(const problem_t* p, int b, int j, int g, int d) {
-  return elem(p->k, kv_index(p, b, j, g, d, p->D), p->dtype);
+  return p->k_scale * elem(p->k, kv_index(p, b, j, g, d, p->D), p->kv_dtype);
 }
 
 static double value_elem(const problem_t* p, int b, int j, int g, int d) {
-  if (p->v == NULL) return elem(p->k, kv_index(p, b, j, g, d, p->D), p->dtype);
-  return elem(p->v, kv_index(p, b, j, g, d, p->Dv), p->dtype);
+  if (p->v == NULL) return p->k_scale * elem(p->k, kv_index(p, b, j, g, d, p->D), p->kv_dtype);
+  return p->v_scale * elem(p->v, kv_index(p, b, j, g, d, p->Dv), p->kv_dtype);
 }
 
 /* Number of keys visible to row (b, t). */
@@ -114,7 +135,7 @@ static void scores(const problem_t* p, int b, int t, int h, int lo, int hi, doub
   for (int j = lo; j < hi; ++j) {
     double dot = 0.0;
     for (int d = 0; d < p->D; ++d)
-      dot += elem(p->q, qbase + d, p->dtype) * key_elem(p, b, j, g, d);
+      dot += elem(p->q, qbase + d, p->q_dtype) * key_elem(p, b, j, g, d);
     s[j - lo] = p->scale * dot;
   }
 }
@@ -154,11 +175,15 @@ static void attend(const problem_t* p, int b, int t, int h, int lo, int hi, int 
 }
 
 static problem_t make_problem(const void* q, const void* k, const void* v, int dtype,
-                              const uint32_t* page_table, int page_size, int max_pages,
-                              const uint32_t* valid_length, int B, int T, int H, int KVH,
-                              int D, int Dv, int S, float scale, const float* sink, int causal) {
+                              float k_scale, float v_scale, const uint32_t* page_table,
+                              int page_size, int max_pages, const uint32_t* valid_length, int B,
+                              int T, int H, int KVH, int D, int Dv, int S, float scale,
+                              const float* sink, int causal) {
   problem_t p;
-  p.q = q; p.k = k; p.v = v; p.dtype = dtype;
+  p.q = q; p.k = k; p.v = v;
+  p.q_dtype = (dtype == ORACLE_BF16_Q_E4M3_KV) ? ORACLE_BF16 : dtype;
+  p.kv_dtype = (dtype == ORACLE_BF16_Q_E4M3_KV) ? ORACLE_E4M3 : dtype;
+  p.k_scale = (double)k_scale; p.v_scale = (double)v_scale;
   p.page_table = page_table; p.page_size = page_size; p.max_pages = max_pages;
   p.valid_length = valid_length;
   p.B = B; p.T = T; p.H = H; p.KVH = KVH; p.D = D; p.Dv = Dv; p.S = S;
@@ -167,6 +192,7 @@ static problem_t make_problem(const void* q, const void* k, const void* v, int d
 }
 
 static int check_problem(const problem_t* p) {
+  if (p->q_dtype < ORACLE_F32 || p->q_dtype > ORACLE_BF16) return -1;
   if (p->B < 0 || p->T < 1 || p->H < 1 || p->KVH < 1 || p->D < 1 || p->Dv < 1 || p->S < 0)
     return -1;
   if (p->H % p->KVH != 0) return -1;
@@ -188,13 +214,13 @@ static int longest_cache(const problem_t* p) {
  * B*T*H rows when rows == NULL.  out: [num_rows, Dv]; lse: [num_rows].
  */
 int oracle_decode_attention(const void* q, const void* k, const void* v, int dtype,
-                            const uint32_t* page_table, int page_size, int max_pages,
+                            float k_scale, float v_scale, const uint32_t* page_table, int page_size, int max_pages,
                             const uint32_t* valid_length, int B, int T, int H, int KVH, int D,
                             int Dv, int S, float scale, const float* sink, int causal,
                             const int64_t* rows, int64_t num_rows, double* out, double* lse,
                             int num_threads) {
-  problem_t p = make_problem(q, k, v, dtype, page_table, page_size, max_pages, valid_length,
-                             B, T, H, KVH, D, Dv, S, scale, sink, causal);
+  problem_t p = make_problem(q, k, v, dtype, k_scale, v_scale, page_table, page_size, max_pages,
+                             valid_length, B, T, H, KVH, D, Dv, S, scale, sink, causal);
   if (check_problem(&p)) return -1;
   int64_t n_rows = rows ? num_rows : (int64_t)B * T * H;
   int smax = longest_cache(&p);
@@ -232,13 +258,13 @@ int oracle_decode_attention(const void* q, const void* k, const void* v, int dty
  * part_m: [P, B*T*H] natural-log max (-inf if empty); part_l: exp-sum (0 if empty).
  */
 int oracle_decode_partials(const void* q, const void* k, const void* v, int dtype,
-                           const uint32_t* page_table, int page_size, int max_pages,
+                           float k_scale, float v_scale, const uint32_t* page_table, int page_size, int max_pages,
                            const uint32_t* valid_length, int B, int T, int H, int KVH, int D,
                            int Dv, int S, float scale, int causal, int num_partitions,
                            int keys_per_partition, double* part_o, double* part_m,
                            double* part_l, int num_threads) {
-  problem_t p = make_problem(q, k, v, dtype, page_table, page_size, max_pages, valid_length,
-                             B, T, H, KVH, D, Dv, S, scale, NULL, causal);
+  problem_t p = make_problem(q, k, v, dtype, k_scale, v_scale, page_table, page_size, max_pages,
+                             valid_length, B, T, H, KVH, D, Dv, S, scale, NULL, causal);
   if (check_problem(&p) || num_partitions < 1 || keys_per_partition < 1) return -1;
   int64_t n_rows = (int64_t)B * T * H;
   int64_t n_items = n_rows * num_partitions;

@@ -43,11 +43,13 @@ def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH, extra_flag
 
 def _bind(lib):
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
-    lib.oracle_decode_attention.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp, i32, i32, i32, i32,
-                                            i32, i32, i32, f32, vp, i32, vp, i64, vp, vp, i32]
+    lib.oracle_decode_attention.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, i32, vp, i32, i32,
+                                            i32, i32, i32, i32, i32, f32, vp, i32, vp, i64, vp, vp,
+                                            i32]
     lib.oracle_decode_attention.restype = i32
-    lib.oracle_decode_partials.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp, i32, i32, i32, i32,
-                                           i32, i32, i32, f32, i32, i32, i32, vp, vp, vp, i32]
+    lib.oracle_decode_partials.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, i32, vp, i32, i32,
+                                           i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp,
+                                           i32]
     lib.oracle_decode_partials.restype = i32
     lib.oracle_splitk_merge.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp, vp]
     lib.oracle_splitk_merge.restype = i32
@@ -72,12 +74,18 @@ def _ptr(a):
 
 
 def _dtype_code(q, k, v):
+    """0: all float32; 1: all bf16 (uint16 bits); 2: q bf16 with k / v in 8-bit
+    e4m3 (uint8 bits, dequantised with k_scale / v_scale)."""
     kinds = {a.dtype for a in (q, k, v) if a is not None}
     if kinds == {np.dtype(np.float32)}:
         return 0
     if kinds == {np.dtype(np.uint16)}:
         return 1
-    raise TypeError(f"q/k/v must all be float32 or all uint16 (bf16 bits), got {kinds}")
+    kv = {a.dtype for a in (k, v) if a is not None}
+    if q.dtype == np.uint16 and kv == {np.dtype(np.uint8)}:
+        return 2
+    raise TypeError(f"q/k/v must all be float32, all uint16 (bf16 bits), or bf16 q with uint8 "
+                    f"(e4m3 bits) k/v; got {kinds}")
 
 
 def _contig(a, dtype=None):
@@ -113,8 +121,12 @@ def _common(q, k, v, page_table, valid_length, sink, depth_v, max_seq_len):
 
 
 def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=None,
-              causal=False, depth_v=None, max_seq_len=None, rows=None, threads=0, lib=None):
+              causal=False, depth_v=None, max_seq_len=None, rows=None, threads=0, lib=None,
+              k_scale=1.0, v_scale=1.0):
     """Reference attention.  Returns (out, lse) as float64.
+
+    k_scale / v_scale: the real key (value) is the scale times the stored element
+    (meant for e4m3 k / v; the value slice of MLA, v=None, uses k_scale).
 
     With rows=None: out [B, T, H, Dv], lse [B, T, H].  With rows (int64 row ids
     (b*T + t)*H + h): out [len(rows), Dv], lse [len(rows)].
@@ -130,7 +142,8 @@ def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=N
         n = B * T * H
     out = np.zeros((n, Dv), np.float64)
     lse = np.zeros((n,), np.float64)
-    rc = lib.oracle_decode_attention(_ptr(q), _ptr(k), _ptr(v), code, _ptr(page_table), page_size,
+    rc = lib.oracle_decode_attention(_ptr(q), _ptr(k), _ptr(v), code, float(k_scale),
+                                     float(v_scale), _ptr(page_table), page_size,
                                      max_pages, _ptr(valid_length), B, T, H, KVH, D, Dv, S,
                                      float(scale), _ptr(sink), int(bool(causal)), _ptr(rows),
                                      n, _ptr(out), _ptr(lse), int(threads))
@@ -143,7 +156,7 @@ def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=N
 
 def partials(q, k, v=None, *, scale, num_partitions, keys_per_partition, page_table=None,
              valid_length=None, causal=False, depth_v=None, max_seq_len=None, threads=0,
-             lib=None):
+             lib=None, k_scale=1.0, v_scale=1.0):
     """Split-K partials.  Returns (O_p [P, B*T*H, Dv], m_p [P, B*T*H], l_p [P, B*T*H])."""
     lib = lib or load_library()
     q, k, v, page_table, valid_length, _, code, dims = _common(
@@ -153,7 +166,8 @@ def partials(q, k, v=None, *, scale, num_partitions, keys_per_partition, page_ta
     po = np.zeros((num_partitions, rows, Dv), np.float64)
     pm = np.zeros((num_partitions, rows), np.float64)
     pl = np.zeros((num_partitions, rows), np.float64)
-    rc = lib.oracle_decode_partials(_ptr(q), _ptr(k), _ptr(v), code, _ptr(page_table), page_size,
+    rc = lib.oracle_decode_partials(_ptr(q), _ptr(k), _ptr(v), code, float(k_scale),
+                                    float(v_scale), _ptr(page_table), page_size,
                                     max_pages, _ptr(valid_length), B, T, H, KVH, D, Dv, S,
                                     float(scale), int(bool(causal)), int(num_partitions),
                                     int(keys_per_partition), _ptr(po), _ptr(pm), _ptr(pl),

@@ -465,6 +465,58 @@ def pin_splitk_single_nonempty(lib):
     _close(lse, pm[2] + np.log(pl[2]), what="its LSE")
 
 
+# --------------------------------------------------------------------------
+# 8-bit e4m3 keys / values with per-tensor scales
+# --------------------------------------------------------------------------
+
+def _e4m3_torch(codes):
+    """torch's own e4m3 (float8_e4m3fn) conversion of uint8 codes, as float64."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def pin_e4m3_all_codes_single_key(lib):
+    """One key: out is its value row, so every one of the 256 codes comes back
+    as v_scale times torch's e4m3 value of it (NaN for the two NaN codes)."""
+    rng = _rng(40)
+    q = _randn(rng, (1, 1, 1, 8), "bf16")
+    k = rng.integers(0, 0x7f, size=(1, 1, 1, 8), dtype=np.uint8)  # finite key codes
+    v = np.arange(256, dtype=np.uint8).reshape(1, 1, 1, 256)
+    v_scale = 0.8125
+    out, lse = O.attention(q, k, v, scale=0.5, k_scale=1.0, v_scale=v_scale, lib=lib)
+    ref = v_scale * _e4m3_torch(v[0, 0, 0])
+    got = out[0, 0, 0]
+    if not np.array_equal(np.isnan(got), np.isnan(ref)):
+        raise AssertionError("NaN codes differ from torch's e4m3")
+    fin = ~np.isnan(ref)
+    _close(got[fin], ref[fin], tol=0, what="e4m3 values")
+    s0 = 0.5 * float(np.dot(_f64(q[0, 0, 0]), _e4m3_torch(k[0, 0, 0])))
+    _close(lse[0, 0, 0], s0, what="lse == scale * q.k")
+
+
+def pin_sdpa_e4m3_scaled_kv(lib):
+    """bf16 q against e4m3 k / v with different scales, ragged and grouped:
+    equals fp64 SDPA on keys / values dequantised by torch (code * scale)."""
+    rng = _rng(41)
+    B, T, H, KVH, D, Dv, S = 2, 1, 6, 2, 16, 24, 29
+    q = _randn(rng, (B, T, H, D), "bf16")
+    codes = np.concatenate([np.arange(0, 0x7f), np.arange(0x80, 0xff)]).astype(np.uint8)
+    k = rng.choice(codes, size=(B, S, KVH, D))
+    v = rng.choice(codes, size=(B, S, KVH, Dv))
+    lens = np.array([29, 11], np.uint32)
+    k_scale, v_scale = 0.0625, 1.75  # exact in fp32, as the oracle takes them
+    scale = float(np.float32(0.4))
+    out, lse = O.attention(q, k, v, scale=scale, valid_length=lens, k_scale=k_scale,
+                           v_scale=v_scale, lib=lib)
+    kd = k_scale * _e4m3_torch(k)
+    vd = v_scale * _e4m3_torch(v)
+    g = H // KVH
+    allowed = np.broadcast_to(_visible(lens, T, S, False)[:, None], (B, H, T, S)).copy()
+    ro, rl = _sdpa(q, _expand_heads(kd, g), _expand_heads(vd, g), scale, allowed=allowed)
+    _close(out, ro, what="out")
+    _close(lse, rl, what="lse")
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}
 
 

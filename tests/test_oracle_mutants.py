@@ -33,8 +33,20 @@ MUTANTS = [
      "row = (size_t)phys * p->page_size + (size_t)(j / p->page_size);"),
     ("page_table_row_stride", "p->page_table[(size_t)b * p->max_pages",
      "p->page_table[(size_t)b * (p->max_pages - 1)"),
-    ("mla_value_tail", "if (p->v == NULL) return elem(p->k, kv_index(p, b, j, g, d, p->D), p->dtype);",
-     "if (p->v == NULL) return elem(p->k, kv_index(p, b, j, g, d + (p->D - p->Dv), p->D), p->dtype);"),
+    ("mla_value_tail",
+     "if (p->v == NULL) return p->k_scale * elem(p->k, kv_index(p, b, j, g, d, p->D), p->kv_dtype);",
+     "if (p->v == NULL) return p->k_scale * elem(p->k, kv_index(p, b, j, g, d + (p->D - p->Dv), p->D), "
+     "p->kv_dtype);"),
+    # 8-bit e4m3 keys / values with per-tensor scales
+    ("e4m3_bias_8", "mag = ldexp(1.0 + (double)m / 8.0, e - 7);", "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("e4m3_subnormal_as_normal", "mag = ldexp((double)m / 8.0, -6);", "mag = ldexp(1.0 + (double)m / 8.0, -7);"),
+    ("e4m3_mantissa_4bit", "mag = ldexp(1.0 + (double)m / 8.0, e - 7);", "mag = ldexp(1.0 + (double)m / 16.0, e - 7);"),
+    ("e4m3_top_code_inf", "if (e == 15 && m == 7) return NAN;", "if (e == 15) return INFINITY;"),
+    ("e4m3_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("k_scale_dropped", "return p->k_scale * elem(p->k, kv_index(p, b, j, g, d, p->D), p->kv_dtype);\n}",
+     "return elem(p->k, kv_index(p, b, j, g, d, p->D), p->kv_dtype);\n}"),
+    ("v_scale_is_k_scale", "return p->v_scale * elem(p->v,", "return p->k_scale * elem(p->v,"),
+    ("v_scale_dropped", "return p->v_scale * elem(p->v,", "return elem(p->v,"),
     ("cache_layout_head_major", "return (row * p->KVH + (size_t)g) * (size_t)width + (size_t)d;",
      "return ((size_t)g * ((size_t)p->B * p->S + 1) + row) * (size_t)width + (size_t)d;"),
     ("q_layout_head_token_swapped", "size_t qbase = (((size_t)b * p->T + t) * p->H + h) * (size_t)p->D;",

@@ -36,7 +36,8 @@ HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 2 << 30  # >= 8x the last-level cache
 
 WORKLOADS = {"tiny": W.TINY_MHA, "gqa": W.GQA, "paged": W.PAGED, "mla": W.MLA,
-             "mla_mtp": W.MLA_MTP, "long": W.LONG}
+             "mla_mtp": W.MLA_MTP, "long": W.LONG, "gqa_fp8": W.GQA_FP8,
+             "paged_fp8": W.PAGED_FP8}
 
 CSRC = os.path.join(ROOT, "decode_attention_07_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -45,9 +46,15 @@ COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
 
 def kernel_sources(wl: W.Workload):
     """Source files of the partition-pass kernel a workload runs."""
-    main = "mla_mfma.hip" if wl.mla else ("decode_stream.hip" if wl.dtype == "bf16"
-                                          else "decode_valu.hip")
-    return [os.path.join(CSRC, f) for f in (main, "da_device.h", "da_params.h")]
+    if wl.mla:
+        main = ["mla_mfma.hip"]
+    elif wl.kv_type == "e4m3":
+        main = ["decode_stream_fp8.hip", "da_stream.h"]
+    elif wl.dtype == "bf16":
+        main = ["decode_stream.hip", "da_stream.h"]
+    else:
+        main = ["decode_valu.hip"]
+    return [os.path.join(CSRC, f) for f in (*main, "da_device.h", "da_params.h")]
 
 
 def kernel_hash(wl: W.Workload) -> str:
@@ -159,7 +166,8 @@ def cpu_baseline(inp: W.Inputs, budget_s: float):
     t0 = time.perf_counter()
     O.attention(probe.q, probe.k, probe.v, scale=wl.softmax_scale, page_table=probe.page_table,
                 valid_length=probe.valid_length, sink=probe.sink, causal=wl.causal,
-                depth_v=wl.dv, max_seq_len=wl.max_seq_len)
+                depth_v=wl.dv, max_seq_len=wl.max_seq_len, k_scale=wl.k_scale,
+                v_scale=wl.v_scale)
     per_seq = max(time.perf_counter() - t0, 1e-4)
     nb = int(max(1, min(wl.batch, budget_s / 3 / per_seq)))
     smp = sample_inputs(inp, nb)
@@ -169,7 +177,8 @@ def cpu_baseline(inp: W.Inputs, budget_s: float):
         t0 = time.perf_counter()
         O.attention(smp.q, smp.k, smp.v, scale=wl.softmax_scale, page_table=smp.page_table,
                     valid_length=smp.valid_length, sink=smp.sink, causal=wl.causal,
-                    depth_v=wl.dv, max_seq_len=wl.max_seq_len)
+                    depth_v=wl.dv, max_seq_len=wl.max_seq_len,
+                    k_scale=wl.k_scale, v_scale=wl.v_scale)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     gbs = smp.kv_bytes() / t / 1e9
@@ -231,11 +240,13 @@ def main():
                                           num_partitions=P, page_table=d["table"],
                                           valid_length=d["valid"], max_seq_len=S,
                                           causal=wl.causal, workspace=ws, prepare=True)
-        return DA.decode_attention_partials(d["q"], d["k"], d["v"], group=wl.group,
-                                            scale=wl.softmax_scale, num_partitions=P,
-                                            page_table=d["table"], valid_length=d["valid"],
-                                            max_seq_len=S, causal=wl.causal, workspace=ws,
-                                            prepare=True)
+        kw = dict(group=wl.group, scale=wl.softmax_scale, num_partitions=P,
+                  page_table=d["table"], valid_length=d["valid"], max_seq_len=S,
+                  causal=wl.causal, workspace=ws, prepare=True)
+        if wl.kv_type == "e4m3":
+            return DA.decode_attention_fp8kv_partials(d["q"], d["k"], d["v"], k_scale=wl.k_scale,
+                                                      v_scale=wl.v_scale, **kw)
+        return DA.decode_attention_partials(d["q"], d["k"], d["v"], **kw)
 
     def reduce_call(d):
         return DA.splitk_reduce(po, pm, ps, num_q_heads=H, sink_weights=d["sink"],
@@ -247,6 +258,9 @@ def main():
                   out=out, lse=lse, workspace=ws, prepare=True)
         if wl.mla:
             return DA.mla_decode(d["q"], d["k"], **kw)
+        if wl.kv_type == "e4m3":
+            return DA.decode_attention_fp8kv(d["q"], d["k"], d["v"], k_scale=wl.k_scale,
+                                             v_scale=wl.v_scale, group=wl.group, **kw)
         return DA.decode_attention(d["q"], d["k"], d["v"], group=wl.group, **kw)
 
     if split:
@@ -314,7 +328,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "dtype": ("bf16 (e4m3 KV)" if wl.kv_type == "e4m3" else "bf16") if wl.dtype == "bf16"
+                 else "f32",
         "data": "synthetic: seeded N(0,1) q/k/v with the workload's shapes "
                 "(and its seeded lengths, page placement and sinks)",
         "config": {"workload": wl.name, "batch": B, "q_len": T, "num_q_heads": H,

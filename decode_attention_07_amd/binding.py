@@ -25,7 +25,8 @@ MLA_DEPTH, MLA_DEPTH_V = 576, 512
 
 EXPORTS = ("decode_attention_status_string", "decode_num_partitions", "decode_workspace_size",
            "decode_workspace_o_offset", "decode_workspace_max_offset",
-           "decode_workspace_sum_offset", "decode_attention",
+           "decode_workspace_sum_offset", "decode_attention", "decode_attention_fp8kv",
+           "decode_attention_fp8kv_partials",
            "decode_attention_partials", "mla_decode", "mla_decode_partials", "splitk_reduce")
 
 _lock = threading.Lock()
@@ -54,6 +55,13 @@ def _declare(lib):
     lib.decode_attention_partials.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32,
                                               i32, i32, f32, i32, i32, i32, vp, sz, vp]
     lib.decode_attention_partials.restype = i32
+    lib.decode_attention_fp8kv.argtypes = [vp, vp, vp, f32, f32, vp, i32, i32, vp, i32, i32, i32,
+                                           i32, i32, i32, f32, i32, vp, i32, vp, vp, vp, sz, vp]
+    lib.decode_attention_fp8kv.restype = i32
+    lib.decode_attention_fp8kv_partials.argtypes = [vp, vp, vp, f32, f32, vp, i32, i32, vp, i32,
+                                                    i32, i32, i32, i32, i32, f32, i32, i32, vp,
+                                                    sz, vp]
+    lib.decode_attention_fp8kv_partials.restype = i32
     lib.mla_decode.argtypes = [vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, f32, i32, vp, i32,
                                vp, vp, vp, sz, vp]
     lib.mla_decode.restype = i32
@@ -266,6 +274,63 @@ def decode_attention_partials(q, k, v, *, group, scale, num_partitions, page_tab
             _stream(stream))
     return _finish(library().decode_attention_partials, args, "decode_attention_partials",
                    workspace, (q, k, v, page_table, valid_length, workspace), prepare)
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def decode_attention_fp8kv(q, k, v, *, k_scale, v_scale, group, scale, page_table=None,
+                           valid_length=None, max_seq_len=None, num_partitions=0,
+                           sink_weights=None, causal=False, out=None, lse=None, workspace=None,
+                           stream=None, want_lse=True, prepare=False):
+    """GQA/MHA decode attention over an 8-bit e4m3 KV cache (k, v: uint8 bits or
+    float8_e4m3fn; real key = k_scale * k, real value = v_scale * v); q and out
+    bf16.  Returns (out, lse), or with prepare=True a BoundCall."""
+    _need(q, "q", 4, (torch.bfloat16,))
+    _need(k, "k", 4, _FP8)
+    _need(v, "v", 4, _FP8)
+    _need(valid_length, "valid_length", 1, _U32)
+    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    B, T, H, D = q.shape
+    if k.shape[3] != D or v.shape[3] != D or k.shape[2] * group != H:
+        raise ValueError("k/v shape does not match q and group")
+    page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len)
+    P = _resolve_partitions(num_partitions, B, T, H, H // group, D, D, S,
+                            valid_length is not None)
+    if out is None:
+        out = torch.empty((B, T, H, D), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    workspace, wbytes = _workspace(workspace, P, B, T, H, D, q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), float(k_scale), float(v_scale), _ptr(page_table),
+            page_size, max_pages, _ptr(valid_length), B, T, H, group, D, S, float(scale), P,
+            _ptr(sink_weights), DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(out),
+            _ptr(lse), _ptr(workspace), wbytes, _stream(stream))
+    return _finish(library().decode_attention_fp8kv, args, "decode_attention_fp8kv", (out, lse),
+                   (q, k, v, page_table, valid_length, sink_weights, out, lse, workspace),
+                   prepare)
+
+
+def decode_attention_fp8kv_partials(q, k, v, *, k_scale, v_scale, group, scale, num_partitions,
+                                    page_table=None, valid_length=None, max_seq_len=None,
+                                    causal=False, workspace=None, stream=None, prepare=False):
+    """Partition pass of decode_attention_fp8kv() only.  Returns the workspace, or
+    with prepare=True a BoundCall."""
+    _need(q, "q", 4, (torch.bfloat16,))
+    _need(k, "k", 4, _FP8)
+    _need(v, "v", 4, _FP8)
+    _need(valid_length, "valid_length", 1, _U32)
+    B, T, H, D = q.shape
+    page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len)
+    P = int(num_partitions)
+    workspace, wbytes = _workspace(workspace, P, B, T, H, D, q.device, always=True)
+    args = (_ptr(q), _ptr(k), _ptr(v), float(k_scale), float(v_scale), _ptr(page_table),
+            page_size, max_pages, _ptr(valid_length), B, T, H, group, D, S, float(scale), P,
+            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(workspace), wbytes,
+            _stream(stream))
+    return _finish(library().decode_attention_fp8kv_partials, args,
+                   "decode_attention_fp8kv_partials", workspace,
+                   (q, k, v, page_table, valid_length, workspace), prepare)
 
 
 def mla_decode(q, kv, *, scale, page_table=None, valid_length=None, max_seq_len=None,

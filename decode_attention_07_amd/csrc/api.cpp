@@ -22,6 +22,8 @@ int valu_rows_per_block(int fold);
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s);
 int stream_step_keys();
 int stream_rows_per_block();
+hipError_t launch_decode_stream_fp8(const DecodeParams& p, hipStream_t s);
+int stream_fp8_step_keys();
 hipError_t launch_mla(const DecodeParams& p, hipStream_t s);
 int mla_step_keys(int q_len);
 int mla_rows_per_block(int q_len, int num_q_heads);
@@ -71,8 +73,7 @@ int log2i(int x) {
 }
 
 // Which partition kernel runs, and its tiling.
-enum Variant { kValu = 0, kStream = 1, kMla = 2 };
-
+enum Variant { kValu = 0, kStream = 1, kMla = 2, kStreamFp8 = 3 };
 
 struct Plan {
   Variant variant;
@@ -94,6 +95,16 @@ Plan plan_mha(int q_len, int group, bool bf16) {
     pl.step = da::valu_step_keys(pl.rows_per_block);
   }
   pl.row_blocks = (fold + pl.rows_per_block - 1) / pl.rows_per_block;
+  return pl;
+}
+
+// bf16 q with an 8-bit e4m3 KV cache: the streaming kernel's 8-bit form.
+Plan plan_fp8(int q_len, int group) {
+  Plan pl;
+  pl.variant = kStreamFp8;
+  pl.rows_per_block = da::stream_rows_per_block();
+  pl.step = da::stream_fp8_step_keys();
+  pl.row_blocks = (q_len * group + pl.rows_per_block - 1) / pl.rows_per_block;
   return pl;
 }
 
@@ -166,6 +177,7 @@ da::DecodeParams base_params(const Common& c, const void* q, const void* k, cons
   p.max_pages = c.page_table ? c.max_pages : 0;
   p.causal = c.mask == DA_MASK_CAUSAL;
   p.scale_log2 = c.scale * 1.4426950408889634f;
+  p.v_scale = 1.f;
   return p;
 }
 
@@ -189,6 +201,7 @@ hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16
   switch (v) {
     case kValu: return da::launch_decode_valu(p, s);
     case kStream: return da::launch_decode_stream(p, s);
+    case kStreamFp8: return da::launch_decode_stream_fp8(p, s);
     default: return da::launch_mla(p, s);
   }
 }
@@ -197,6 +210,7 @@ const char* variant_name(Variant v) {
   switch (v) {
     case kValu: return "valu";
     case kStream: return "stream";
+    case kStreamFp8: return "stream_fp8";
     default: return "mla";
   }
 }
@@ -238,7 +252,8 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
   // (blocks that finish early take more), with two resident blocks per CU.
   p.queue = nullptr;
   p.queue_blocks = 0;
-  if (split && plan.variant == kStream && c.valid_length && plan.row_blocks == 1) {
+  if (split && (plan.variant == kStream || plan.variant == kStreamFp8) && c.valid_length &&
+      plan.row_blocks == 1) {
     p.queue = queue;
     p.queue_blocks = 2 * device_cus();
   }
@@ -271,6 +286,32 @@ int check_mha(const Common& c, const void* q, const void* k, const void* v, int 
   if (dtype != DA_F32 && dtype != DA_BF16) return DA_ERR_UNSUPPORTED;
   if (depth != 64 && depth != 128) return DA_ERR_UNSUPPORTED;
   return DA_OK;
+}
+
+int check_fp8kv(const Common& c, const void* q, const void* k, const void* v, int group,
+                int depth, float k_scale, float v_scale) {
+  if (!q || !k || !v) return DA_ERR_INVALID_ARG;
+  int rc = check_common(c);
+  if (rc) return rc;
+  if (group < 1 || c.num_q_heads % group != 0) return DA_ERR_INVALID_ARG;
+  if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !std::isfinite(c.scale * k_scale))
+    return DA_ERR_INVALID_ARG;
+  if (depth != 128) return DA_ERR_UNSUPPORTED;
+  return DA_OK;
+}
+
+// The partition pass and, for P > 1, the merge of bf16 q over an 8-bit KV
+// cache: k_scale joins the softmax scale and v_scale the output factor.
+int run_fp8kv(const Common& c, const void* q, const void* k, const void* v, float k_scale,
+              float v_scale, int group, int depth, int num_partitions, bool partials_only,
+              const float* sink, void* out, float* lse, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  const int kv_heads = c.num_q_heads / group;
+  da::DecodeParams p = base_params(c, q, k, v, kv_heads, group, depth, depth);
+  p.scale_log2 = c.scale * k_scale * 1.4426950408889634f;
+  p.v_scale = v_scale;
+  return run(c, p, plan_fp8(c.q_len, group), true, num_partitions, partials_only, sink, out, lse,
+             workspace, workspace_bytes, stream);
 }
 
 int check_mla(const Common& c, const void* q, const void* kv) {
@@ -373,6 +414,38 @@ int decode_attention_partials(const void* q, const void* k, const void* v,
   const da::DecodeParams p = base_params(c, q, k, v, kv_heads, group, depth, depth);
   return run(c, p, plan_mha(q_len, group, bf16), bf16, num_partitions, true, nullptr, nullptr,
              nullptr, workspace, workspace_bytes, stream);
+}
+
+int decode_attention_fp8kv(const void* q, const void* k, const void* v, float k_scale,
+                           float v_scale, const uint32_t* page_table, int page_size,
+                           int max_pages_per_seq, const uint32_t* valid_length, int batch,
+                           int q_len, int num_q_heads, int group, int depth, int max_seq_len,
+                           float scale, int num_partitions, const float* sink_weights, int mask,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+                 q_len,      num_q_heads, max_seq_len, mask, scale};
+  int rc = check_fp8kv(c, q, k, v, group, depth, k_scale, v_scale);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  return run_fp8kv(c, q, k, v, k_scale, v_scale, group, depth, num_partitions, false,
+                   sink_weights, out, lse, workspace, workspace_bytes, stream);
+}
+
+int decode_attention_fp8kv_partials(const void* q, const void* k, const void* v, float k_scale,
+                                    float v_scale, const uint32_t* page_table, int page_size,
+                                    int max_pages_per_seq, const uint32_t* valid_length,
+                                    int batch, int q_len, int num_q_heads, int group, int depth,
+                                    int max_seq_len, float scale, int num_partitions, int mask,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  const Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+                 q_len,      num_q_heads, max_seq_len, mask, scale};
+  int rc = check_fp8kv(c, q, k, v, group, depth, k_scale, v_scale);
+  if (rc) return rc;
+  if (num_partitions < 1 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  return run_fp8kv(c, q, k, v, k_scale, v_scale, group, depth, num_partitions, true, nullptr,
+                   nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 int mla_decode(const void* q, const void* kv, const uint32_t* page_table, int page_size,

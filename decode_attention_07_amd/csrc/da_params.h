@@ -27,7 +27,8 @@ struct DecodeParams {
   int keys_per_partition;       // C: partition p covers keys [p*C, (p+1)*C)
   int row_blocks;               // row tiles per (batch, KV head)
   int write_partials;           // 1: write part_*; 0: write out / lse directly
-  float scale_log2;             // scale * log2(e)
+  float scale_log2;             // scale * log2(e) (times k_scale for an 8-bit KV cache)
+  float v_scale;                // 8-bit KV cache: real value = v_scale * stored value
   // Work queue of the bf16 GQA kernel (ragged split calls; nullptr otherwise):
   // one 64-bit word in the workspace, low half = next work item, high half =
   // blocks done; zero between calls.

@@ -105,7 +105,7 @@ int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_head
  * with rows = batch * q_len * num_q_heads.  Returns 0 for invalid arguments.
  *
  * Work queue.  A bf16 decode_attention() / decode_attention_partials() call
- * with valid_length, more than one partition and at most 16 query rows per KV
+ * (or its 8-bit KV form) with valid_length, more than one partition and at most 16 query rows per KV
  * head runs a fixed set of blocks that take their (partition, sequence, KV
  * head) items from the queue word with device-scope atomics, so that blocks
  * whose items are short, or which run on faster parts of the chip, take more.
@@ -167,6 +167,36 @@ int decode_attention_partials(const void* q, const void* k, const void* v,
                               int num_q_heads, int group, int depth, int max_seq_len,
                               float scale, int num_partitions, int mask, int dtype,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode attention with an 8-bit KV cache: q bf16, k and v one byte per element
+ * in the e4m3 format (the OCP FP8 E4M3 encoding: bias 7, subnormals, no
+ * infinity, S.1111.111 is NaN), out bf16.  The pages admit float8_e4m3fn
+ * elements with a bf16 output and fold a scale into the softmax
+ * ("flare_mla_decoding_dispatch", Parameters `dtype`, Args `output` and
+ * `q_scale_ptr`) but give no scale convention for the cache; the reading taken
+ * here is one fp32 scale per tensor: the real key is k_scale * (stored key),
+ * the real value v_scale * (stored value).
+ * Arguments, layouts (with 1-byte elements), workspace and status codes are
+ * those of decode_attention(); depth must be 128 (else DA_ERR_UNSUPPORTED), and
+ * k_scale, v_scale and scale * k_scale must be finite.
+ */
+int decode_attention_fp8kv(const void* q, const void* k, const void* v, float k_scale,
+                           float v_scale, const uint32_t* page_table, int page_size,
+                           int max_pages_per_seq, const uint32_t* valid_length, int batch,
+                           int q_len, int num_q_heads, int group, int depth, int max_seq_len,
+                           float scale, int num_partitions, const float* sink_weights, int mask,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* The partition pass of decode_attention_fp8kv() alone (partials as for
+ * decode_attention_partials(); the partial outputs include v_scale). */
+int decode_attention_fp8kv_partials(const void* q, const void* k, const void* v, float k_scale,
+                                    float v_scale, const uint32_t* page_table, int page_size,
+                                    int max_pages_per_seq, const uint32_t* valid_length,
+                                    int batch, int q_len, int num_q_heads, int group, int depth,
+                                    int max_seq_len, float scale, int num_partitions, int mask,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * MLA decode ("flare_mla_decoding_dispatch", Args `k` and `kv_num_heads`): a

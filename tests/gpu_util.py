@@ -36,13 +36,17 @@ def run_gpu(wl: W.Workload, dev: dict, num_partitions=None, **kw):
     common.update(kw)
     if wl.mla:
         return DA.mla_decode(dev["q"], dev["k"], **common)
+    if wl.kv_type == "e4m3":
+        return DA.decode_attention_fp8kv(dev["q"], dev["k"], dev["v"], k_scale=wl.k_scale,
+                                         v_scale=wl.v_scale, group=wl.group, **common)
     return DA.decode_attention(dev["q"], dev["k"], dev["v"], group=wl.group, **common)
 
 
 def run_oracle(wl: W.Workload, inp: W.Inputs, rows=None):
     return O.attention(inp.q, inp.k, inp.v, scale=wl.softmax_scale, page_table=inp.page_table,
                        valid_length=inp.valid_length, sink=inp.sink, causal=wl.causal,
-                       depth_v=wl.dv, max_seq_len=wl.max_seq_len, rows=rows)
+                       depth_v=wl.dv, max_seq_len=wl.max_seq_len, rows=rows,
+                       k_scale=wl.k_scale, v_scale=wl.v_scale)
 
 
 def compare(wl: W.Workload, out, lse, ref_out, ref_lse, rows=None, what="", ulp_rel=False):

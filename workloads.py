@@ -110,7 +110,14 @@ class Workload:
     sink: bool = False
     scale: float | None = None
     num_partitions: int = 0   # 0 = library heuristic
+    kv_dtype: str | None = None  # None -> dtype; 'e4m3' -> 8-bit K / V bits (q and out bf16)
+    k_scale: float = 1.0      # 8-bit cache: real key = k_scale * stored key
+    v_scale: float = 1.0      # 8-bit cache: real value = v_scale * stored value
     extra: dict = field(default_factory=dict, compare=False)
+
+    @property
+    def kv_type(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def group(self) -> int:
@@ -142,7 +149,14 @@ MLA_MTP = MLA.with_(name="mla_mtp2_bf16_b64_h128_d576_dv512_s8192", q_len=2, cau
 LONG = Workload("long_sink_bf16_b1_h32_kv8_d128_s131072", 7005, batch=1, num_heads=32,
                 kv_heads=8, depth=128, max_seq_len=131072, sink=True)
 
-ALL = {w.name: w for w in (TINY_MHA, GQA, PAGED, MLA, MLA_MTP, LONG)}
+# The GQA and ragged paged problems with an 8-bit e4m3 KV cache (stored elements
+# e4m3(8 N(0,1)); k_scale = v_scale = 1/8, so the real keys and values are N(0,1)-like).
+GQA_FP8 = GQA.with_(name="gqa_fp8_b32_h32_kv8_d128_s4096", kv_dtype="e4m3", k_scale=0.125,
+                    v_scale=0.125)
+PAGED_FP8 = PAGED.with_(name="paged_ragged_fp8_b64_h64_kv8_d128_s32768_p128", kv_dtype="e4m3",
+                        k_scale=0.125, v_scale=0.125)
+
+ALL = {w.name: w for w in (TINY_MHA, GQA, PAGED, MLA, MLA_MTP, LONG, GQA_FP8, PAGED_FP8)}
 
 
 @dataclass
@@ -163,7 +177,7 @@ class Inputs:
 
     def kv_bytes(self) -> int:
         """Bytes of K (and V unless MLA) over the valid keys, each read once."""
-        esize = 2 if self.wl.dtype == "bf16" else 4
+        esize = {"bf16": 2, "f32": 4, "e4m3": 1}[self.wl.kv_type]
         per_key = self.wl.kv_heads * self.wl.depth * esize
         if not self.wl.mla:
             per_key += self.wl.kv_heads * self.wl.dv * esize
@@ -176,8 +190,27 @@ def _streams(wl: Workload, variant: int):
                     np.random.SeedSequence(entropy).spawn(6)))
 
 
+E4M3_NAN = np.uint8(0x7F)
+E4M3_SPREAD = 8.0  # stored 8-bit elements are e4m3(8 x N(0,1)): well inside +-448
+
+
+def e4m3_tensor(seed_seq: np.random.SeedSequence, shape) -> np.ndarray:
+    """8-bit e4m3 bit patterns (uint8) of E4M3_SPREAD x N(0,1), rounded to nearest
+    by torch's float8_e4m3fn conversion."""
+    import torch
+    x = normal_tensor(seed_seq, shape, "f32") * np.float32(E4M3_SPREAD)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _kv_tensor(seed_seq, shape, kv_type: str) -> np.ndarray:
+    return e4m3_tensor(seed_seq, shape) if kv_type == "e4m3" else normal_tensor(seed_seq, shape,
+                                                                                kv_type)
+
+
 def _poison(arr: np.ndarray, dtype: str):
-    if dtype == "bf16":
+    if dtype == "e4m3":
+        arr[...] = E4M3_NAN
+    elif dtype == "bf16":
         arr[...] = BF16_NAN
     else:
         arr[...] = np.float32(np.nan)
@@ -219,24 +252,24 @@ def make_inputs(wl: Workload, variant: int = 0, poison: bool = True) -> Inputs:
             page_table[b, :need[b]] = perm[pos:pos + need[b]]
             pos += need[b]
         pool_shape = (total + 1, ps, KVH, D)
-        k = normal_tensor(st["k"], pool_shape, wl.dtype)
-        v = None if wl.mla else normal_tensor(st["v"], (total + 1, ps, KVH, wl.dv), wl.dtype)
+        k = _kv_tensor(st["k"], pool_shape, wl.kv_type)
+        v = None if wl.mla else _kv_tensor(st["v"], (total + 1, ps, KVH, wl.dv), wl.kv_type)
         if poison:
             for arr in (k, v):
                 if arr is None:
                     continue
-                _poison(arr[poison_page], wl.dtype)
+                _poison(arr[poison_page], wl.kv_type)
                 for b in range(B):
                     n = int(lens[b])
                     if n % ps and need[b]:
-                        _poison(arr[page_table[b, need[b] - 1], n % ps:], wl.dtype)
+                        _poison(arr[page_table[b, need[b] - 1], n % ps:], wl.kv_type)
     else:
-        k = normal_tensor(st["k"], (B, S, KVH, D), wl.dtype)
-        v = None if wl.mla else normal_tensor(st["v"], (B, S, KVH, wl.dv), wl.dtype)
+        k = _kv_tensor(st["k"], (B, S, KVH, D), wl.kv_type)
+        v = None if wl.mla else _kv_tensor(st["v"], (B, S, KVH, wl.dv), wl.kv_type)
         if poison and valid is not None:
             for arr in (k, v):
                 if arr is None:
                     continue
                 for b in range(B):
-                    _poison(arr[b, int(valid[b]):], wl.dtype)
+                    _poison(arr[b, int(valid[b]):], wl.kv_type)
     return Inputs(wl, q, k, v, valid, page_table, sink)

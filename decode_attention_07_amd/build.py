@@ -19,10 +19,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 instructions stay off (some of their forms are not trusted)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
-# Per-source additions.  The streaming kernel rescales its MFMA accumulators
+# Per-source additions.  The streaming kernels rescale their MFMA accumulators
 # with vector ops: the VGPR form of the MFMAs keeps them out of the
 # accumulation registers and saves a copy in each direction per tile.
-EXTRA = {"decode_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"decode_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode_stream_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

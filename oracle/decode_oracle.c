@@ -94,7 +94,33 @@ typedef struct {
   double scale;
   const float* sink;          /* [H] or NULL                                    */
   int causal;
+  const uint32_t* q_offsets;  /* ragged q: [B+1] cumulative token offsets, the tokens of
+                                 sequence b being rows q_offsets[b]..q_offsets[b+1] of a
+                                 [total, H, D] q; NULL: T tokens per sequence  */
 } problem_t;
+
+/* Query tokens of sequence b, and the q row of its first token. */
+static int seq_tokens(const problem_t* p, int b) {
+  return p->q_offsets ? (int)(p->q_offsets[b + 1] - p->q_offsets[b]) : p->T;
+}
+static size_t first_token(const problem_t* p, int b) {
+  return p->q_offsets ? (size_t)p->q_offsets[b] : (size_t)b * p->T;
+}
+static int64_t total_tokens(const problem_t* p) {
+  return p->q_offsets ? (int64_t)p->q_offsets[p->B] : (int64_t)p->B * p->T;
+}
+/* Sequence and token index of q row `token`. */
+static void locate_token(const problem_t* p, int64_t token, int* b, int* t) {
+  if (!p->q_offsets) {
+    *b = (int)(token / p->T);
+    *t = (int)(token % p->T);
+    return;
+  }
+  int s = 0;
+  while (s + 1 < p->B && (int64_t)p->q_offsets[s + 1] <= token) ++s;
+  *b = s;
+  *t = (int)(token - (int64_t)p->q_offsets[s]);
+}
 
 /* Flat element index of depth element d of key j (of sequence b, KV head g)
  * in a cache whose rows hold `width` elements. */
@@ -122,7 +148,7 @@ static double value_elem(const problem_t* p, int b, int j, int g, int d) {
 static int visible_keys(const problem_t* p, int b, int t) {
   int n = p->valid_length ? (int)p->valid_length[b] : p->S;
   if (p->causal) {
-    int lim = n - p->T + t + 1;
+    int lim = n - seq_tokens(p, b) + t + 1;
     if (lim < n) n = lim;
   }
   return n < 0 ? 0 : n;
@@ -131,7 +157,7 @@ static int visible_keys(const problem_t* p, int b, int t) {
 /* Scores s_j = scale * <q_row, k_j> for keys j in [lo, hi). */
 static void scores(const problem_t* p, int b, int t, int h, int lo, int hi, double* s) {
   int g = h / (p->H / p->KVH);
-  size_t qbase = (((size_t)b * p->T + t) * p->H + h) * (size_t)p->D;
+  size_t qbase = ((first_token(p, b) + (size_t)t) * p->H + h) * (size_t)p->D;
   for (int j = lo; j < hi; ++j) {
     double dot = 0.0;
     for (int d = 0; d < p->D; ++d)
@@ -178,8 +204,9 @@ static problem_t make_problem(const void* q, const void* k, const void* v, int d
                               float k_scale, float v_scale, const uint32_t* page_table,
                               int page_size, int max_pages, const uint32_t* valid_length, int B,
                               int T, int H, int KVH, int D, int Dv, int S, float scale,
-                              const float* sink, int causal) {
+                              const float* sink, int causal, const uint32_t* q_offsets) {
   problem_t p;
+  p.q_offsets = q_offsets;
   p.q = q; p.k = k; p.v = v;
   p.q_dtype = (dtype == ORACLE_BF16_Q_E4M3_KV) ? ORACLE_BF16 : dtype;
   p.kv_dtype = (dtype == ORACLE_BF16_Q_E4M3_KV) ? ORACLE_E4M3 : dtype;
@@ -193,6 +220,10 @@ static problem_t make_problem(const void* q, const void* k, const void* v, int d
 
 static int check_problem(const problem_t* p) {
   if (p->q_dtype < ORACLE_F32 || p->q_dtype > ORACLE_BF16) return -1;
+  if (p->q_offsets) {
+    for (int b = 0; b < p->B; ++b)
+      if (p->q_offsets[b + 1] < p->q_offsets[b]) return -1;
+  }
   if (p->B < 0 || p->T < 1 || p->H < 1 || p->KVH < 1 || p->D < 1 || p->Dv < 1 || p->S < 0)
     return -1;
   if (p->H % p->KVH != 0) return -1;
@@ -210,19 +241,21 @@ static int longest_cache(const problem_t* p) {
 }
 
 /*
- * Full attention for the listed rows (row id = (b*T + t)*H + h), or for all
- * B*T*H rows when rows == NULL.  out: [num_rows, Dv]; lse: [num_rows].
+ * Full attention for the listed rows (row id = (token)*H + h, token = b*T + t,
+ * or q_offsets[b] + t for a ragged q), or for all rows when rows == NULL.
+ * out: [num_rows, Dv]; lse: [num_rows].
  */
 int oracle_decode_attention(const void* q, const void* k, const void* v, int dtype,
                             float k_scale, float v_scale, const uint32_t* page_table, int page_size, int max_pages,
                             const uint32_t* valid_length, int B, int T, int H, int KVH, int D,
                             int Dv, int S, float scale, const float* sink, int causal,
-                            const int64_t* rows, int64_t num_rows, double* out, double* lse,
-                            int num_threads) {
+                            const uint32_t* q_offsets, const int64_t* rows, int64_t num_rows,
+                            double* out, double* lse, int num_threads) {
   problem_t p = make_problem(q, k, v, dtype, k_scale, v_scale, page_table, page_size, max_pages,
-                             valid_length, B, T, H, KVH, D, Dv, S, scale, sink, causal);
+                             valid_length, B, T, H, KVH, D, Dv, S, scale, sink, causal,
+                             q_offsets);
   if (check_problem(&p)) return -1;
-  int64_t n_rows = rows ? num_rows : (int64_t)B * T * H;
+  int64_t n_rows = rows ? num_rows : total_tokens(&p) * H;
   int smax = longest_cache(&p);
 #ifdef _OPENMP
   if (num_threads > 0) omp_set_num_threads(num_threads);
@@ -240,8 +273,8 @@ int oracle_decode_attention(const void* q, const void* k, const void* v, int dty
       if (!s) continue;
       int64_t r = rows ? rows[i] : i;
       int h = (int)(r % H);
-      int t = (int)((r / H) % T);
-      int b = (int)(r / ((int64_t)H * T));
+      int b, t;
+      locate_token(&p, r / H, &b, &t);
       double m, l;
       attend(&p, b, t, h, 0, visible_keys(&p, b, t), 1, s, out + (size_t)i * Dv, &m, &l);
       lse[i] = (l > 0.0) ? m + log(l) : -INFINITY;
@@ -260,13 +293,14 @@ int oracle_decode_attention(const void* q, const void* k, const void* v, int dty
 int oracle_decode_partials(const void* q, const void* k, const void* v, int dtype,
                            float k_scale, float v_scale, const uint32_t* page_table, int page_size, int max_pages,
                            const uint32_t* valid_length, int B, int T, int H, int KVH, int D,
-                           int Dv, int S, float scale, int causal, int num_partitions,
-                           int keys_per_partition, double* part_o, double* part_m,
-                           double* part_l, int num_threads) {
+                           int Dv, int S, float scale, int causal, const uint32_t* q_offsets,
+                           int num_partitions, int keys_per_partition, double* part_o,
+                           double* part_m, double* part_l, int num_threads) {
   problem_t p = make_problem(q, k, v, dtype, k_scale, v_scale, page_table, page_size, max_pages,
-                             valid_length, B, T, H, KVH, D, Dv, S, scale, NULL, causal);
+                             valid_length, B, T, H, KVH, D, Dv, S, scale, NULL, causal,
+                             q_offsets);
   if (check_problem(&p) || num_partitions < 1 || keys_per_partition < 1) return -1;
-  int64_t n_rows = (int64_t)B * T * H;
+  int64_t n_rows = total_tokens(&p) * H;
   int64_t n_items = n_rows * num_partitions;
 #ifdef _OPENMP
   if (num_threads > 0) omp_set_num_threads(num_threads);
@@ -285,8 +319,8 @@ int oracle_decode_partials(const void* q, const void* k, const void* v, int dtyp
       int part = (int)(i / n_rows);
       int64_t r = i % n_rows;
       int h = (int)(r % H);
-      int t = (int)((r / H) % T);
-      int b = (int)(r / ((int64_t)H * T));
+      int b, t;
+      locate_token(&p, r / H, &b, &t);
       int n = visible_keys(&p, b, t);
       int64_t lo64 = (int64_t)part * keys_per_partition;
       int lo = lo64 < n ? (int)lo64 : n;

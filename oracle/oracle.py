@@ -44,12 +44,12 @@ def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH, extra_flag
 def _bind(lib):
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.oracle_decode_attention.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, i32, vp, i32, i32,
-                                            i32, i32, i32, i32, i32, f32, vp, i32, vp, i64, vp, vp,
-                                            i32]
+                                            i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, i64, vp,
+                                            vp, i32]
     lib.oracle_decode_attention.restype = i32
     lib.oracle_decode_partials.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, i32, vp, i32, i32,
-                                           i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp, vp,
-                                           i32]
+                                           i32, i32, i32, i32, i32, f32, i32, vp, i32, i32, vp, vp,
+                                           vp, i32]
     lib.oracle_decode_partials.restype = i32
     lib.oracle_splitk_merge.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp, vp]
     lib.oracle_splitk_merge.restype = i32
@@ -120,10 +120,27 @@ def _common(q, k, v, page_table, valid_length, sink, depth_v, max_seq_len):
                                                            max_pages)
 
 
+def _ragged(q, q_offsets):
+    """Ragged q [total, H, D] with offsets [B+1] -> (q as [1, total, H, D] for the shape
+    checks, offsets, B, T = most tokens of a sequence)."""
+    if q_offsets is None:
+        return q, None, None, None
+    qo = np.ascontiguousarray(q_offsets, dtype=np.uint32)
+    q = np.asarray(q)
+    if q.ndim != 3 or qo.ndim != 1 or qo.shape[0] < 1 or int(qo[-1]) != q.shape[0]:
+        raise ValueError("ragged q must be [total, H, D] with offsets [B+1] ending at total")
+    B = qo.shape[0] - 1
+    T = max(1, int(np.max(np.diff(qo.astype(np.int64)))) if B else 1)
+    return q.reshape(1, *q.shape), qo, B, T
+
+
 def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=None,
               causal=False, depth_v=None, max_seq_len=None, rows=None, threads=0, lib=None,
-              k_scale=1.0, v_scale=1.0):
+              k_scale=1.0, v_scale=1.0, q_offsets=None):
     """Reference attention.  Returns (out, lse) as float64.
+
+    q_offsets: ragged q -- q is [total, H, D] and the tokens of sequence b are rows
+    q_offsets[b] .. q_offsets[b+1]; out is then [total, H, Dv], lse [total, H].
 
     k_scale / v_scale: the real key (value) is the scale times the stored element
     (meant for e4m3 k / v; the value slice of MLA, v=None, uses k_scale).
@@ -132,44 +149,54 @@ def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=N
     (b*T + t)*H + h): out [len(rows), Dv], lse [len(rows)].
     """
     lib = lib or load_library()
+    q, qo, rB, rT = _ragged(q, q_offsets)
     q, k, v, page_table, valid_length, sink, code, dims = _common(
         q, k, v, page_table, valid_length, sink, depth_v, max_seq_len)
     B, T, H, KVH, D, Dv, S, page_size, max_pages = dims
+    total = q.shape[0] * q.shape[1]
+    if qo is not None:
+        B, T = rB, rT
     if rows is not None:
         rows = np.ascontiguousarray(rows, dtype=np.int64)
         n = rows.shape[0]
     else:
-        n = B * T * H
+        n = total * H
     out = np.zeros((n, Dv), np.float64)
     lse = np.zeros((n,), np.float64)
     rc = lib.oracle_decode_attention(_ptr(q), _ptr(k), _ptr(v), code, float(k_scale),
                                      float(v_scale), _ptr(page_table), page_size,
                                      max_pages, _ptr(valid_length), B, T, H, KVH, D, Dv, S,
-                                     float(scale), _ptr(sink), int(bool(causal)), _ptr(rows),
-                                     n, _ptr(out), _ptr(lse), int(threads))
+                                     float(scale), _ptr(sink), int(bool(causal)), _ptr(qo),
+                                     _ptr(rows), n, _ptr(out), _ptr(lse), int(threads))
     if rc != 0:
         raise RuntimeError(f"oracle_decode_attention failed ({rc})")
     if rows is None:
+        if qo is not None:
+            return out.reshape(total, H, Dv), lse.reshape(total, H)
         return out.reshape(B, T, H, Dv), lse.reshape(B, T, H)
     return out, lse
 
 
 def partials(q, k, v=None, *, scale, num_partitions, keys_per_partition, page_table=None,
              valid_length=None, causal=False, depth_v=None, max_seq_len=None, threads=0,
-             lib=None, k_scale=1.0, v_scale=1.0):
-    """Split-K partials.  Returns (O_p [P, B*T*H, Dv], m_p [P, B*T*H], l_p [P, B*T*H])."""
+             lib=None, k_scale=1.0, v_scale=1.0, q_offsets=None):
+    """Split-K partials.  Returns (O_p [P, rows, Dv], m_p [P, rows], l_p [P, rows]) with
+    rows = (q tokens) * H."""
     lib = lib or load_library()
+    q, qo, rB, rT = _ragged(q, q_offsets)
     q, k, v, page_table, valid_length, _, code, dims = _common(
         q, k, v, page_table, valid_length, None, depth_v, max_seq_len)
     B, T, H, KVH, D, Dv, S, page_size, max_pages = dims
-    rows = B * T * H
+    if qo is not None:
+        B, T = rB, rT
+    rows = q.shape[0] * q.shape[1] * H
     po = np.zeros((num_partitions, rows, Dv), np.float64)
     pm = np.zeros((num_partitions, rows), np.float64)
     pl = np.zeros((num_partitions, rows), np.float64)
     rc = lib.oracle_decode_partials(_ptr(q), _ptr(k), _ptr(v), code, float(k_scale),
                                     float(v_scale), _ptr(page_table), page_size,
                                     max_pages, _ptr(valid_length), B, T, H, KVH, D, Dv, S,
-                                    float(scale), int(bool(causal)), int(num_partitions),
+                                    float(scale), int(bool(causal)), _ptr(qo), int(num_partitions),
                                     int(keys_per_partition), _ptr(po), _ptr(pm), _ptr(pl),
                                     int(threads))
     if rc != 0:

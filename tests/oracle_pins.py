@@ -466,6 +466,64 @@ def pin_splitk_single_nonempty(lib):
 
 
 # --------------------------------------------------------------------------
+# Ragged q: per-sequence token counts from cumulative offsets
+# --------------------------------------------------------------------------
+
+def _ragged_case(rng, dtype="f32"):
+    B, H, KVH, D, S = 4, 4, 2, 16, 23
+    tokens = np.array([2, 0, 3, 1])
+    qo = np.concatenate([[0], np.cumsum(tokens)]).astype(np.uint32)
+    q = _randn(rng, (int(qo[-1]), H, D), dtype)
+    k = _randn(rng, (B, S, KVH, D), dtype)
+    v = _randn(rng, (B, S, KVH, D), dtype)
+    lens = np.array([23, 9, 5, 17], np.uint32)
+    return q, qo, k, v, lens, tokens
+
+
+def pin_ragged_q_equals_sequence_by_sequence(lib):
+    """Each sequence of a ragged call equals a one-sequence call with T = its own
+    token count (causal and not, with a sink)."""
+    rng = _rng(50)
+    q, qo, k, v, lens, tokens = _ragged_case(rng)
+    sink = rng.standard_normal(q.shape[1]).astype(np.float32)
+    for causal in (False, True):
+        out, lse = O.attention(q, k, v, scale=0.3, valid_length=lens, sink=sink, causal=causal,
+                               q_offsets=qo, lib=lib)
+        for b, T in enumerate(tokens):
+            if T == 0:
+                continue
+            r = slice(int(qo[b]), int(qo[b + 1]))
+            o1, l1 = O.attention(q[r][None], k[b:b + 1], v[b:b + 1], scale=0.3,
+                                 valid_length=lens[b:b + 1], sink=sink, causal=causal, lib=lib)
+            _close(out[r], o1[0], tol=0, what=f"seq {b} out")
+            _close(lse[r], l1[0], tol=0, what=f"seq {b} lse")
+
+
+def pin_sdpa_ragged_q_causal(lib):
+    """Ragged causal q against fp64 SDPA with explicit masks: token t of the T_b
+    tokens of sequence b sees keys j <= N_b - T_b + t."""
+    rng = _rng(51)
+    q, qo, k, v, lens, tokens = _ragged_case(rng, "bf16")
+    H, KVH = q.shape[1], k.shape[2]
+    scale = float(np.float32(0.35))
+    out, lse = O.attention(q, k, v, scale=scale, valid_length=lens, causal=True, q_offsets=qo,
+                           lib=lib)
+    for b, T in enumerate(tokens):
+        if T == 0:
+            continue
+        r = slice(int(qo[b]), int(qo[b + 1]))
+        S = k.shape[1]
+        j = np.arange(S)[None, :]
+        lim = int(lens[b]) - int(T) + np.arange(T)[:, None] + 1
+        allowed = np.broadcast_to((j < np.minimum(lim, int(lens[b])))[None, None],
+                                  (1, H, T, S)).copy()
+        ro, rl = _sdpa(q[r][None], _expand_heads(k[b:b + 1], H // KVH),
+                       _expand_heads(v[b:b + 1], H // KVH), scale, allowed=allowed)
+        _close(out[r], ro[0], what=f"seq {b} out")
+        _close(lse[r], rl[0], what=f"seq {b} lse")
+
+
+# --------------------------------------------------------------------------
 # 8-bit e4m3 keys / values with per-tensor scales
 # --------------------------------------------------------------------------
 

@@ -17,8 +17,9 @@ SRC = os.path.join(os.path.dirname(O.__file__), "decode_oracle.c")
 # (name, exact text in the source, replacement)
 MUTANTS = [
     ("kv_head_modulo", "int g = h / (p->H / p->KVH);", "int g = h % p->KVH;"),
-    ("causal_off_by_one", "int lim = n - p->T + t + 1;", "int lim = n - p->T + t;"),
-    ("causal_top_left", "int lim = n - p->T + t + 1;", "int lim = t + 1;"),
+    ("causal_off_by_one", "int lim = n - seq_tokens(p, b) + t + 1;",
+     "int lim = n - seq_tokens(p, b) + t;"),
+    ("causal_top_left", "int lim = n - seq_tokens(p, b) + t + 1;", "int lim = t + 1;"),
     ("scale_dropped", "s[j - lo] = p->scale * dot;", "s[j - lo] = dot;"),
     ("scale_squared", "s[j - lo] = p->scale * dot;", "s[j - lo] = p->scale * p->scale * dot;"),
     ("valid_length_ignored", "int n = p->valid_length ? (int)p->valid_length[b] : p->S;",
@@ -49,8 +50,14 @@ MUTANTS = [
     ("v_scale_dropped", "return p->v_scale * elem(p->v,", "return elem(p->v,"),
     ("cache_layout_head_major", "return (row * p->KVH + (size_t)g) * (size_t)width + (size_t)d;",
      "return ((size_t)g * ((size_t)p->B * p->S + 1) + row) * (size_t)width + (size_t)d;"),
-    ("q_layout_head_token_swapped", "size_t qbase = (((size_t)b * p->T + t) * p->H + h) * (size_t)p->D;",
+    ("q_layout_head_token_swapped",
+     "size_t qbase = ((first_token(p, b) + (size_t)t) * p->H + h) * (size_t)p->D;",
      "size_t qbase = (((size_t)b * p->H + h) * p->T + t) * (size_t)p->D;"),
+    # ragged q (tokens per sequence from q_offsets)
+    ("ragged_causal_uses_most_tokens",
+     "return p->q_offsets ? (int)(p->q_offsets[b + 1] - p->q_offsets[b]) : p->T;", "return p->T;"),
+    ("ragged_boundary_token_misplaced", "(int64_t)p->q_offsets[s + 1] <= token) ++s;",
+     "(int64_t)p->q_offsets[s + 1] < token) ++s;"),
     ("max_not_subtracted_in_lse", "double w = exp(s[j] - m);", "double w = exp(s[j]);"),
     ("empty_row_lse_zero", "lse[i] = (l > 0.0) ? m + log(l) : -INFINITY;",
      "lse[i] = (l > 0.0) ? m + log(l) : 0.0;"),
@@ -82,7 +89,8 @@ def test_mutant_is_caught(tmp_path, name, old, new):
     path = tmp_path / f"oracle_{name}.c"
     path.write_text(mutated)
     lib_path = O.build(force=True, src=str(path), out=str(tmp_path / f"lib_{name}.so"),
-                       extra_flags=("-Wno-unused-variable", "-Wno-unused-but-set-variable"))
+                       extra_flags=("-Wno-unused-variable", "-Wno-unused-but-set-variable",
+                                    "-Wno-unused-function"))
     lib = O.load_library(lib_path)
     caught = oracle_pins.failing_pins(lib)
     assert caught, f"planted mistake {name!r} passed every pin"

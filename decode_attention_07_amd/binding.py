@@ -25,8 +25,8 @@ MLA_DEPTH, MLA_DEPTH_V = 576, 512
 
 EXPORTS = ("decode_attention_status_string", "decode_num_partitions", "decode_workspace_size",
            "decode_workspace_o_offset", "decode_workspace_max_offset",
-           "decode_workspace_sum_offset", "decode_attention", "decode_attention_fp8kv",
-           "decode_attention_fp8kv_partials",
+           "decode_workspace_sum_offset", "decode_attention", "decode_attention_ragged",
+           "decode_attention_fp8kv", "decode_attention_fp8kv_partials", "mla_decode_ragged",
            "decode_attention_partials", "mla_decode", "mla_decode_partials", "splitk_reduce")
 
 _lock = threading.Lock()
@@ -55,6 +55,13 @@ def _declare(lib):
     lib.decode_attention_partials.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32,
                                               i32, i32, f32, i32, i32, i32, vp, sz, vp]
     lib.decode_attention_partials.restype = i32
+    lib.decode_attention_ragged.argtypes = [vp, vp, i32, i32, vp, vp, vp, i32, i32, vp, i32, i32,
+                                            i32, i32, i32, f32, i32, vp, i32, i32, vp, vp, vp, sz,
+                                            vp]
+    lib.decode_attention_ragged.restype = i32
+    lib.mla_decode_ragged.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, vp, i32, i32, i32, f32,
+                                      i32, vp, i32, vp, vp, vp, sz, vp]
+    lib.mla_decode_ragged.restype = i32
     lib.decode_attention_fp8kv.argtypes = [vp, vp, vp, f32, f32, vp, i32, i32, vp, i32, i32, i32,
                                            i32, i32, i32, f32, i32, vp, i32, vp, vp, vp, sz, vp]
     lib.decode_attention_fp8kv.restype = i32
@@ -188,7 +195,7 @@ def workspace_views(workspace: torch.Tensor, num_partitions, batch, q_len, num_q
     return po, pm, ps
 
 
-def _cache_geometry(q, k, page_table, max_seq_len):
+def _cache_geometry(q, k, page_table, max_seq_len, batch=None):
     if page_table is not None:
         _need(page_table, "page_table", 2, _U32)
         page_size, max_pages = k.shape[1], page_table.shape[1]
@@ -198,7 +205,7 @@ def _cache_geometry(q, k, page_table, max_seq_len):
         S = k.shape[1]
         if max_seq_len is not None and int(max_seq_len) != S:
             raise ValueError("dense cache: max_seq_len must equal k.shape[1]")
-        if k.shape[0] != q.shape[0]:
+        if k.shape[0] != (q.shape[0] if batch is None else batch):
             raise ValueError("dense cache batch must match q")
     return page_size, max_pages, S
 
@@ -274,6 +281,81 @@ def decode_attention_partials(q, k, v, *, group, scale, num_partitions, page_tab
             _stream(stream))
     return _finish(library().decode_attention_partials, args, "decode_attention_partials",
                    workspace, (q, k, v, page_table, valid_length, workspace), prepare)
+
+
+def _ragged_q(q, q_offsets, max_q_len):
+    _need(q, "q", 3)
+    _need(q_offsets, "q_offsets", 1, _U32)
+    if q_offsets is None or q_offsets.shape[0] < 1:
+        raise ValueError("q_offsets [batch + 1] is required")
+    if max_q_len is None or int(max_q_len) < 1:
+        raise ValueError("max_q_len (an upper bound of every sequence's tokens) is required")
+    return q_offsets.shape[0] - 1, int(max_q_len)
+
+
+def decode_attention_ragged(q, q_offsets, k, v, *, max_q_len, group, scale, page_table=None,
+                            valid_length=None, max_seq_len=None, num_partitions=0,
+                            sink_weights=None, causal=False, out=None, lse=None, workspace=None,
+                            stream=None, want_lse=True, prepare=False):
+    """GQA/MHA decode with a ragged q [total, H, D]: the tokens of sequence b are rows
+    q_offsets[b] .. q_offsets[b+1].  Returns (out [total, H, D], lse [total, H])."""
+    B, Tm = _ragged_q(q, q_offsets, max_q_len)
+    _need(k, "k", 4)
+    _need(v, "v", 4)
+    _need(valid_length, "valid_length", 1, _U32)
+    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    total, H, D = q.shape
+    if k.shape[3] != D or v.shape[3] != D or k.shape[2] * group != H:
+        raise ValueError("k/v shape does not match q and group")
+    page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len, batch=B)
+    P = _resolve_partitions(num_partitions, B, Tm, H, H // group, D, D, S,
+                            valid_length is not None)
+    if out is None:
+        out = torch.empty((total, H, D), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((total, H), dtype=torch.float32, device=q.device)
+    workspace, wbytes = _workspace(workspace, P, 1, total, H, D, q.device)
+    args = (_ptr(q), _ptr(q_offsets), total, Tm, _ptr(k), _ptr(v), _ptr(page_table), page_size,
+            max_pages, _ptr(valid_length), B, H, group, D, S, float(scale), P,
+            _ptr(sink_weights), DA_MASK_CAUSAL if causal else DA_MASK_NONE, dt, _ptr(out),
+            _ptr(lse), _ptr(workspace), wbytes, _stream(stream))
+    return _finish(library().decode_attention_ragged, args, "decode_attention_ragged",
+                   (out, lse), (q, q_offsets, k, v, page_table, valid_length, sink_weights, out,
+                                lse, workspace), prepare)
+
+
+def mla_decode_ragged(q, q_offsets, kv, *, max_q_len, scale, page_table=None,
+                      valid_length=None, max_seq_len=None, num_partitions=0, sink_weights=None,
+                      causal=False, out=None, lse=None, workspace=None, stream=None,
+                      want_lse=True, prepare=False):
+    """MLA decode with a ragged q [total, H, 576].  Returns (out [total, H, 512],
+    lse [total, H])."""
+    B, Tm = _ragged_q(q, q_offsets, max_q_len)
+    _need(q, "q", 3, (torch.bfloat16,))
+    _need(kv, "kv", 4, (torch.bfloat16,))
+    _need(valid_length, "valid_length", 1, _U32)
+    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    total, H, D = q.shape
+    if D != MLA_DEPTH or kv.shape[3] != MLA_DEPTH or kv.shape[2] != 1:
+        raise ValueError("MLA needs q [..., 576] and kv [..., 1, 576]")
+    page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len, batch=B)
+    P = _resolve_partitions(num_partitions, B, Tm, H, 1, MLA_DEPTH, MLA_DEPTH_V, S,
+                            valid_length is not None)
+    if out is None:
+        out = torch.empty((total, H, MLA_DEPTH_V), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((total, H), dtype=torch.float32, device=q.device)
+    workspace, wbytes = _workspace(workspace, P, 1, total, H, MLA_DEPTH_V, q.device)
+    args = (_ptr(q), _ptr(q_offsets), total, Tm, _ptr(kv), _ptr(page_table), page_size,
+            max_pages, _ptr(valid_length), B, H, S, float(scale), P, _ptr(sink_weights),
+            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(out), _ptr(lse), _ptr(workspace),
+            wbytes, _stream(stream))
+    return _finish(library().mla_decode_ragged, args, "mla_decode_ragged", (out, lse),
+                   (q, q_offsets, kv, page_table, valid_length, sink_weights, out, lse,
+                    workspace), prepare)
 
 
 _FP8 = (torch.uint8, torch.float8_e4m3fn)

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
@@ -142,11 +143,22 @@ struct Common {
   const uint32_t* valid_length;
   int batch, q_len, num_q_heads, max_seq_len, mask;
   float scale;
+  // Ragged q: cumulative token offsets [batch + 1] (q_len bounds every
+  // sequence's tokens) and the total token count; nullptr / 0 otherwise.
+  const uint32_t* q_offsets = nullptr;
+  int total_q_tokens = 0;
 };
+
+// q / out rows of a call (tokens x heads).
+size_t call_rows(const Common& c) {
+  const size_t tokens = c.q_offsets ? (size_t)c.total_q_tokens : (size_t)c.batch * c.q_len;
+  return tokens * c.num_q_heads;
+}
 
 int check_common(const Common& c) {
   if (c.batch < 0 || c.q_len < 1 || c.num_q_heads < 1 || c.max_seq_len < 0)
     return DA_ERR_INVALID_ARG;
+  if (c.total_q_tokens < 0) return DA_ERR_INVALID_ARG;
   if (c.mask != DA_MASK_NONE && c.mask != DA_MASK_CAUSAL) return DA_ERR_INVALID_ARG;
   if (!std::isfinite(c.scale)) return DA_ERR_INVALID_ARG;
   if (c.page_table) {
@@ -178,6 +190,8 @@ da::DecodeParams base_params(const Common& c, const void* q, const void* k, cons
   p.causal = c.mask == DA_MASK_CAUSAL;
   p.scale_log2 = c.scale * 1.4426950408889634f;
   p.v_scale = 1.f;
+  p.q_offsets = c.q_offsets;
+  p.rows_total = (int)call_rows(c);
   return p;
 }
 
@@ -219,8 +233,9 @@ const char* variant_name(Variant v) {
 int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int num_partitions,
         bool partials_only, const float* sink, void* out, float* lse, void* workspace,
         size_t workspace_bytes, void* stream) {
-  const size_t rows = (size_t)c.batch * c.q_len * c.num_q_heads;
+  const size_t rows = call_rows(c);
   if (rows == 0) return DA_OK;  // empty batch: nothing to enqueue
+  if (rows > (size_t)INT32_MAX) return DA_ERR_INVALID_ARG;
   int P = num_partitions;
   if (P == 0) {
     P = decode_num_partitions(c.batch, c.q_len, c.num_q_heads, p.num_kv_heads, p.depth,
@@ -231,7 +246,8 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
   if (P > 1 && !da::splitk_reduce_supported(p.depth_v, P)) return DA_ERR_UNSUPPORTED;
   const bool split = partials_only || P > 1;
   if (split) {
-    const size_t need = decode_workspace_size(P, c.batch, c.q_len, c.num_q_heads, p.depth_v);
+    const size_t need = decode_workspace_size(P, 1, (int)(rows / c.num_q_heads), c.num_q_heads,
+                                              p.depth_v);
     if (!workspace || workspace_bytes < need) return DA_ERR_WORKSPACE;
   }
 
@@ -414,6 +430,50 @@ int decode_attention_partials(const void* q, const void* k, const void* v,
   const da::DecodeParams p = base_params(c, q, k, v, kv_heads, group, depth, depth);
   return run(c, p, plan_mha(q_len, group, bf16), bf16, num_partitions, true, nullptr, nullptr,
              nullptr, workspace, workspace_bytes, stream);
+}
+
+int decode_attention_ragged(const void* q, const uint32_t* q_offsets, int total_q_tokens,
+                            int max_q_len, const void* k, const void* v,
+                            const uint32_t* page_table, int page_size, int max_pages_per_seq,
+                            const uint32_t* valid_length, int batch, int num_q_heads, int group,
+                            int depth, int max_seq_len, float scale, int num_partitions,
+                            const float* sink_weights, int mask, int dtype, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+           max_q_len,  num_q_heads, max_seq_len, mask, scale};
+  c.q_offsets = q_offsets;
+  c.total_q_tokens = total_q_tokens;
+  if (!q_offsets) return DA_ERR_INVALID_ARG;
+  int rc = check_mha(c, q, k, v, group, depth, dtype);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  const bool bf16 = dtype == DA_BF16;
+  const int kv_heads = num_q_heads / group;
+  const da::DecodeParams p = base_params(c, q, k, v, kv_heads, group, depth, depth);
+  return run(c, p, plan_mha(max_q_len, group, bf16), bf16, num_partitions, false, sink_weights,
+             out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_ragged(const void* q, const uint32_t* q_offsets, int total_q_tokens,
+                      int max_q_len, const void* kv, const uint32_t* page_table, int page_size,
+                      int max_pages_per_seq, const uint32_t* valid_length, int batch,
+                      int num_q_heads, int max_seq_len, float scale, int num_partitions,
+                      const float* sink_weights, int mask, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+           max_q_len,  num_q_heads, max_seq_len, mask, scale};
+  c.q_offsets = q_offsets;
+  c.total_q_tokens = total_q_tokens;
+  if (!q_offsets) return DA_ERR_INVALID_ARG;
+  int rc = check_mla(c, q, kv);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  const da::DecodeParams p =
+      base_params(c, q, kv, kv, 1, num_q_heads, kMlaDepth, kMlaDepthV);
+  return run(c, p, plan_mla(max_q_len, num_q_heads), true, num_partitions, false, sink_weights,
+             out, lse, workspace, workspace_bytes, stream);
 }
 
 int decode_attention_fp8kv(const void* q, const void* k, const void* v, float k_scale,

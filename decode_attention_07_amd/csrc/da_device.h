@@ -112,7 +112,7 @@ __device__ __forceinline__ int visible_keys(const DecodeParams& p, int b, int t)
   int n = p.valid_length ? (int)p.valid_length[b] : p.max_seq_len;
   if (n > p.max_seq_len) n = p.max_seq_len;
   if (p.causal) {
-    int lim = n - p.q_len + t + 1;
+    int lim = n - seq_tokens(p, b) + t + 1;
     n = lim < n ? lim : n;
   }
   return n < 0 ? 0 : n;

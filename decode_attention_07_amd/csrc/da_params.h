@@ -34,10 +34,32 @@ struct DecodeParams {
   // blocks done; zero between calls.
   unsigned long long* queue;
   int queue_blocks;             // persistent blocks launched when queue is set
+  // Ragged q: the q_len_b tokens of sequence b are q / out rows q_offsets[b] ..
+  // q_offsets[b+1] (q_len is then an upper bound of q_len_b); nullptr: q_len
+  // tokens per sequence.
+  const uint32_t* q_offsets;
+  int rows_total;               // q / out rows (tokens x heads): one partition's partial rows
 };
 
 // Row-block geometry of a (batch, KV head): T*group rows (token-major:
 // row = t*group + i is query head kv*group + i of token t).
 __host__ __device__ inline int fold_rows(const DecodeParams& p) { return p.q_len * p.group; }
+
+// Query tokens of sequence b (at most q_len) and the q / out row of its first
+// token.  The offsets are read through the scalar cache: b is uniform and the
+// table is constant during the call.
+__device__ inline int seq_tokens(const DecodeParams& p, int b) {
+  if (!p.q_offsets) return p.q_len;
+  const __attribute__((address_space(4))) uint32_t* qo =
+      (const __attribute__((address_space(4))) uint32_t*)p.q_offsets;
+  const int n = (int)(qo[b + 1] - qo[b]);
+  return n < p.q_len ? n : p.q_len;
+}
+__device__ inline size_t seq_row0(const DecodeParams& p, int b) {
+  if (!p.q_offsets) return (size_t)b * p.q_len;
+  const __attribute__((address_space(4))) uint32_t* qo =
+      (const __attribute__((address_space(4))) uint32_t*)p.q_offsets;
+  return (size_t)qo[b];
+}
 
 }  // namespace da

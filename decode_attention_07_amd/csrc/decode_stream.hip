@@ -182,7 +182,8 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
   const int c16 = lane & 15, g16 = lane >> 4;
 
   // This lane's query row (16 rows per block: rows of the token-major fold).
-  const int nrows = fold_rows(p);
+  const int nrows = seq_tokens(p, b) * p.group;  // this sequence's fold
+  const size_t row0q = seq_row0(p, b);
   const int rr = rb * 16 + c16;
   const bool row_ok = rr < nrows;
   const int tok = row_ok ? rr / p.group : 0;
@@ -203,7 +204,7 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
   // Q^T operand: k-slot (g16, j) of depth step s <-> depth 32 s + 8 g16 + j.
   bf16x8_t qf[C::KS];
   const uint16_t* qrow =
-      (const uint16_t*)p.q + (((size_t)b * p.q_len + tok) * p.num_q_heads + head) * (size_t)D;
+      (const uint16_t*)p.q + ((row0q + tok) * p.num_q_heads + head) * (size_t)D;
 #pragma unroll
   for (int s = 0; s < C::KS; ++s)  // rows past the fold read row (b, 0, g * group): zeroed later
     qf[s] = *(const bf16x8_t*)(qrow + s * 32 + g16 * 8);
@@ -310,9 +311,9 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
       Lr += f * sr[w * 16 + r];
       O += f * so[(w * 16 + r) * (D + 3) + d];
     }
-    const size_t row = ((size_t)b * p.q_len + tt) * p.num_q_heads + h;
+    const size_t row = (row0q + tt) * p.num_q_heads + h;
     if (p.write_partials) {
-      const size_t prow = (size_t)pidx * ((size_t)p.batch * p.q_len * p.num_q_heads) + row;
+      const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
       const bool any = L > 0.f;
       p.part_o[prow * D + d] = any ? O / Lr : 0.f;
       if (d == 0) {

@@ -198,7 +198,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   const int b = id % p.batch; id /= p.batch;
   const int pidx = id;
 
-  const int nrows = fold_rows(p);
+  const int nrows = seq_tokens(p, b) * p.group;  // this sequence's fold
+  const size_t row0q = seq_row0(p, b);
   const int k_lo = pidx * p.keys_per_partition;
   int hi[R];
   bool row_ok[R];
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
   uint4 qv[R][C::NV];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const size_t qoff = (((size_t)b * p.q_len + tok[r]) * p.num_q_heads + head[r]) * (size_t)D;
+    const size_t qoff = ((row0q + tok[r]) * p.num_q_heads + head[r]) * (size_t)D;
 #pragma unroll
     for (int vv = 0; vv < C::NV; ++vv) {
       if (row_ok[r])
@@ -325,9 +326,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
       Lsum += f * sm_l[w][r];
       O += f * sm_o[w][r][d];
     }
-    const size_t row = ((size_t)b * p.q_len + t) * p.num_q_heads + h;
+    const size_t row = (row0q + t) * p.num_q_heads + h;
     if (p.write_partials) {
-      const size_t prow = (size_t)pidx * ((size_t)p.batch * p.q_len * p.num_q_heads) + row;
+      const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
       const bool any = Lsum > 0.f;
       p.part_o[prow * D + d] = any ? O / Lsum : 0.f;
       if (d == 0) {

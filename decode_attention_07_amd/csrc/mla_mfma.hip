@@ -115,7 +115,12 @@ __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage,
   } else {
     row0 = (size_t)b * p.max_seq_len + j0;
   }
-  const char* base = (const char*)p.k + row0 * kRowBytes;
+  // Uniform by construction; pinned to scalar registers (the loads take a
+  // scalar base) even where it reaches here through a phi after a divergent branch.
+  const size_t off0 = row0 * kRowBytes;
+  const size_t off = ((size_t)__builtin_amdgcn_readfirstlane((uint32_t)(off0 >> 32)) << 32) |
+                     (size_t)__builtin_amdgcn_readfirstlane((uint32_t)off0);
+  const char* base = (const char*)p.k + off;
   const int nvalid = kend - j0;
   const uint4 t0 = *(const uint4*)tab;
   const uint4 t1 = *(const uint4*)(tab + 4);
@@ -378,7 +383,9 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c32 = lane & 31, g = lane >> 5;
   const int H = p.num_q_heads;
-  const int nrows = p.q_len * H;
+  const int nrows = seq_tokens(p, b) * H;  // this sequence's token x head rows
+  if (mb * kRows >= nrows) return;  // ragged q: none of this block's rows exist (no barrier yet)
+  const size_t row0q = seq_row0(p, b);
 
   const int rr = mb * kRows + wave * kWaveRows + c32;
   const bool row_ok = rr < nrows;
@@ -397,7 +404,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   // Q^T operand: k-slot (g, j) of depth step st <-> depth 16*st + 8*g + j.
   bf16x8_t qf[kKS];
   const uint16_t* qrow =
-      (const uint16_t*)p.q + (((size_t)b * p.q_len + tok) * H + head) * (size_t)kD;
+      (const uint16_t*)p.q + ((row0q + tok) * H + head) * (size_t)kD;
 #pragma unroll
   for (int s = 0; s < kKS; ++s)  // rows past the fold read row (b, 0, 0) and are zeroed later
     qf[s] = *(const bf16x8_t*)(qrow + s * 16 + g * 8);
@@ -523,10 +530,10 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   lsum = sum_xor32(lsum);
   lsr = sum_xor32(lsr);
   if (!row_ok) return;
-  const size_t row = ((size_t)b * p.q_len + tok) * H + head;
+  const size_t row = (row0q + tok) * H + head;
   // Lane holds O^T[d = 32*dt + 8*(j/4) + 4*g + j%4][row]: 4 consecutive d per j/4.
   if (p.write_partials) {
-    const size_t prow = (size_t)pidx * ((size_t)p.batch * nrows) + row;
+    const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
     const bool any = lsum > 0.f;
     const float inv = any ? 1.f / lsr : 0.f;
     float* dst = p.part_o + prow * kDv;

@@ -169,6 +169,39 @@ int decode_attention_partials(const void* q, const void* k, const void* v,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode attention with a ragged q ("flare_mla_decoding_dispatch", Parameters
+ * `ragged` and Args `valid_length`: a rank-3 q whose rows are located by
+ * cumulative per-sequence offsets): q is [total_q_tokens, num_q_heads, depth]
+ * and the q_len_b tokens of sequence b are its rows q_offsets[b] ..
+ * q_offsets[b+1] (device uint32 [batch + 1], non-decreasing, q_offsets[batch] =
+ * total_q_tokens, every q_len_b <= max_q_len; tokens past max_q_len are not
+ * computed).  out is [total_q_tokens, num_q_heads, depth] and lse
+ * [total_q_tokens, num_q_heads].  valid_length keeps its meaning (keys of
+ * sequence b, its current tokens included); with DA_MASK_CAUSAL token t of
+ * sequence b sees keys j <= N_b - q_len_b + t.  The split-K workspace is sized
+ * for rows = total_q_tokens * num_q_heads: decode_workspace_size(P, 1,
+ * total_q_tokens, num_q_heads, depth_v).  Other arguments as for
+ * decode_attention(); num_partitions = 0 uses decode_num_partitions() with
+ * q_len = max_q_len.
+ */
+int decode_attention_ragged(const void* q, const uint32_t* q_offsets, int total_q_tokens,
+                            int max_q_len, const void* k, const void* v,
+                            const uint32_t* page_table, int page_size, int max_pages_per_seq,
+                            const uint32_t* valid_length, int batch, int num_q_heads, int group,
+                            int depth, int max_seq_len, float scale, int num_partitions,
+                            const float* sink_weights, int mask, int dtype, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* MLA decode with a ragged q (layouts as for decode_attention_ragged(), depth 576
+ * in, 512 out; other arguments as for mla_decode()). */
+int mla_decode_ragged(const void* q, const uint32_t* q_offsets, int total_q_tokens,
+                      int max_q_len, const void* kv, const uint32_t* page_table, int page_size,
+                      int max_pages_per_seq, const uint32_t* valid_length, int batch,
+                      int num_q_heads, int max_seq_len, float scale, int num_partitions,
+                      const float* sink_weights, int mask, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode attention with an 8-bit KV cache: q bf16, k and v one byte per element
  * in the e4m3 format (the OCP FP8 E4M3 encoding: bias 7, subnormals, no
  * infinity, S.1111.111 is NaN), out bf16.  The pages admit float8_e4m3fn

@@ -37,7 +37,7 @@ ROTATE_BYTES = 2 << 30  # >= 8x the last-level cache
 
 WORKLOADS = {"tiny": W.TINY_MHA, "gqa": W.GQA, "paged": W.PAGED, "mla": W.MLA,
              "mla_mtp": W.MLA_MTP, "long": W.LONG, "gqa_fp8": W.GQA_FP8,
-             "paged_fp8": W.PAGED_FP8}
+             "paged_fp8": W.PAGED_FP8, "gqa_ragged_q": W.GQA_RAGGED_Q}
 
 CSRC = os.path.join(ROOT, "decode_attention_07_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -161,13 +161,22 @@ def cpu_baseline(inp: W.Inputs, budget_s: float):
     from oracle import oracle as O
     wl = inp.wl
     threads = O.num_threads()
+    tokens = W.ragged_q_tokens(wl)
+
+    def oracle_call(smp):
+        kw = dict(scale=wl.softmax_scale, page_table=smp.page_table,
+                  valid_length=smp.valid_length, sink=smp.sink, causal=wl.causal,
+                  depth_v=wl.dv, max_seq_len=wl.max_seq_len, k_scale=wl.k_scale,
+                  v_scale=wl.v_scale)
+        if tokens is None:
+            return O.attention(smp.q, smp.k, smp.v, **kw)
+        q, qo = W.pack_ragged_q(smp, tokens[:smp.wl.batch])
+        return O.attention(q, smp.k, smp.v, q_offsets=qo, **kw)
+
     # Size the sample from one short probe run on one sequence.
     probe = sample_inputs(inp, 1)
     t0 = time.perf_counter()
-    O.attention(probe.q, probe.k, probe.v, scale=wl.softmax_scale, page_table=probe.page_table,
-                valid_length=probe.valid_length, sink=probe.sink, causal=wl.causal,
-                depth_v=wl.dv, max_seq_len=wl.max_seq_len, k_scale=wl.k_scale,
-                v_scale=wl.v_scale)
+    oracle_call(probe)
     per_seq = max(time.perf_counter() - t0, 1e-4)
     nb = int(max(1, min(wl.batch, budget_s / 3 / per_seq)))
     smp = sample_inputs(inp, nb)
@@ -175,10 +184,7 @@ def cpu_baseline(inp: W.Inputs, budget_s: float):
     t_start = time.perf_counter()
     while len(times) < 3 or (len(times) < 5 and time.perf_counter() - t_start < budget_s / 2):
         t0 = time.perf_counter()
-        O.attention(smp.q, smp.k, smp.v, scale=wl.softmax_scale, page_table=smp.page_table,
-                    valid_length=smp.valid_length, sink=smp.sink, causal=wl.causal,
-                    depth_v=wl.dv, max_seq_len=wl.max_seq_len,
-                    k_scale=wl.k_scale, v_scale=wl.v_scale)
+        oracle_call(smp)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     gbs = smp.kv_bytes() / t / 1e9
@@ -219,16 +225,27 @@ def main():
         dev_sets.append(dict(q=DA.to_device(inp.q), k=DA.to_device(inp.k),
                              v=DA.to_device(inp.v), table=DA.to_device(inp.page_table),
                              valid=DA.to_device(inp.valid_length), sink=DA.to_device(inp.sink)))
+    ragged_q = W.ragged_q_tokens(wl)
+    if ragged_q is not None:  # q rows packed per sequence (its first tokens[b] tokens)
+        for inp, d in zip(host_sets, dev_sets):
+            q, qo = W.pack_ragged_q(inp, ragged_q)
+            d["q"], d["q_offsets"] = DA.to_device(q), DA.to_device(qo)
+        log(f"ragged q: {int(ragged_q.sum())} tokens, {int(ragged_q.min())}..{int(ragged_q.max())} "
+            f"per sequence")
     kv_bytes = footprint
     S = wl.max_seq_len
     B, T, H = wl.batch, wl.q_len, wl.num_heads
     P = args.partitions or DA.num_partitions(B, T, H, wl.kv_heads, wl.depth, wl.dv, S,
                                              ragged=first.valid_length is not None)
-    split = P > 1
+    split = P > 1 and ragged_q is None  # a ragged-q call is timed as one full call
     ws = torch.zeros(DA.decode_workspace_size(P, B, T, H, wl.dv), dtype=torch.uint8,
                      device="cuda")  # zero-filled once: the work-queue word starts at 0
     out = torch.empty((B, T, H, wl.dv), dtype=dev_sets[0]["q"].dtype, device="cuda")
     lse = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+    if ragged_q is not None:
+        n_tok = int(ragged_q.sum())
+        out = torch.empty((n_tok, H, wl.dv), dtype=dev_sets[0]["q"].dtype, device="cuda")
+        lse = torch.empty((n_tok, H), dtype=torch.float32, device="cuda")
     po, pm, ps = DA.workspace_views(ws, P, B, T, H, wl.dv)
 
     # Each launch is marshalled once (binding BoundCall): a timed step costs the host
@@ -256,6 +273,9 @@ def main():
         kw = dict(scale=wl.softmax_scale, page_table=d["table"], valid_length=d["valid"],
                   max_seq_len=S, num_partitions=P, sink_weights=d["sink"], causal=wl.causal,
                   out=out, lse=lse, workspace=ws, prepare=True)
+        if ragged_q is not None:
+            return DA.decode_attention_ragged(d["q"], d["q_offsets"], d["k"], d["v"],
+                                              max_q_len=T, group=wl.group, **kw)
         if wl.mla:
             return DA.mla_decode(d["q"], d["k"], **kw)
         if wl.kv_type == "e4m3":

@@ -156,7 +156,30 @@ GQA_FP8 = GQA.with_(name="gqa_fp8_b32_h32_kv8_d128_s4096", kv_dtype="e4m3", k_sc
 PAGED_FP8 = PAGED.with_(name="paged_ragged_fp8_b64_h64_kv8_d128_s32768_p128", kv_dtype="e4m3",
                         k_scale=0.125, v_scale=0.125)
 
-ALL = {w.name: w for w in (TINY_MHA, GQA, PAGED, MLA, MLA_MTP, LONG, GQA_FP8, PAGED_FP8)}
+# Speculative-decode shape of the GQA problem: each sequence brings 1..4 new
+# tokens (seeded), causal; q is ragged (rows packed per sequence).
+GQA_RAGGED_Q = GQA.with_(name="gqa_ragged_q_b32_h32_kv8_d128_s4096_t1to4", q_len=4, causal=True,
+                         extra={"q_tokens": (1, 4)})
+
+ALL = {w.name: w for w in (TINY_MHA, GQA, PAGED, MLA, MLA_MTP, LONG, GQA_FP8, PAGED_FP8,
+                           GQA_RAGGED_Q)}
+
+
+def ragged_q_tokens(wl: Workload):
+    """Per-sequence token counts of a ragged-q workload (seeded), or None."""
+    rq = wl.extra.get("q_tokens")
+    if rq is None:
+        return None
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 77])))
+    return rng.integers(rq[0], rq[1], size=wl.batch, endpoint=True).astype(np.int64)
+
+
+def pack_ragged_q(inp: Inputs, tokens):
+    """Ragged q [total, H, D] and offsets [B+1]: the first tokens[b] tokens of each
+    sequence of the padded q [B, T, H, D]."""
+    qo = np.concatenate([[0], np.cumsum(tokens)]).astype(np.uint32)
+    q = np.concatenate([inp.q[b, :int(t)] for b, t in enumerate(tokens)], axis=0)
+    return np.ascontiguousarray(q), qo
 
 
 @dataclass

@@ -143,3 +143,70 @@ def test_mla_and_reduce_argument_checks():
     assert lib.splitk_reduce(None, 1, 1, 2, 4, 2, 128, None, 1, 1, None, None) == \
         DA.DA_ERR_INVALID_ARG
     assert lib.splitk_reduce(1, 1, 1, 2, 0, 2, 128, None, 1, 1, None, None) == DA.DA_OK
+
+
+def _call_fp8(**over):
+    a = dict(q=1, k=1, v=1, k_scale=1.0, v_scale=1.0, page_table=None, page_size=0, max_pages=0,
+             valid_length=None, batch=1, q_len=1, num_q_heads=8, group=1, depth=128,
+             max_seq_len=256, scale=0.1, num_partitions=0, sink=None, mask=0, out=1, lse=None,
+             workspace=None, wbytes=0, stream=None)
+    a.update(over)
+    return DA.library().decode_attention_fp8kv(
+        a["q"], a["k"], a["v"], a["k_scale"], a["v_scale"], a["page_table"], a["page_size"],
+        a["max_pages"], a["valid_length"], a["batch"], a["q_len"], a["num_q_heads"], a["group"],
+        a["depth"], a["max_seq_len"], a["scale"], a["num_partitions"], a["sink"], a["mask"],
+        a["out"], a["lse"], a["workspace"], a["wbytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=None), DA.DA_ERR_INVALID_ARG),
+    (dict(out=None), DA.DA_ERR_INVALID_ARG),
+    (dict(depth=64), DA.DA_ERR_UNSUPPORTED),      # the 8-bit kernel is built for depth 128
+    (dict(k_scale=float("inf")), DA.DA_ERR_INVALID_ARG),
+    (dict(v_scale=float("nan")), DA.DA_ERR_INVALID_ARG),
+    (dict(scale=1e30, k_scale=1e30), DA.DA_ERR_INVALID_ARG),   # scale * k_scale overflows
+    (dict(group=3), DA.DA_ERR_INVALID_ARG),
+    (dict(num_partitions=4), DA.DA_ERR_WORKSPACE),
+    (dict(batch=0), DA.DA_OK),
+])
+def test_fp8kv_argument_checks(over, code):
+    assert _call_fp8(**over) == code
+
+
+def _call_ragged(**over):
+    a = dict(q=1, q_offsets=1, total=3, max_q_len=2, k=1, v=1, page_table=None, page_size=0,
+             max_pages=0, valid_length=None, batch=2, num_q_heads=8, group=2, depth=128,
+             max_seq_len=256, scale=0.1, num_partitions=0, sink=None, mask=1, dtype=1, out=1,
+             lse=None, workspace=None, wbytes=0, stream=None)
+    a.update(over)
+    return DA.library().decode_attention_ragged(
+        a["q"], a["q_offsets"], a["total"], a["max_q_len"], a["k"], a["v"], a["page_table"],
+        a["page_size"], a["max_pages"], a["valid_length"], a["batch"], a["num_q_heads"],
+        a["group"], a["depth"], a["max_seq_len"], a["scale"], a["num_partitions"], a["sink"],
+        a["mask"], a["dtype"], a["out"], a["lse"], a["workspace"], a["wbytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q_offsets=None), DA.DA_ERR_INVALID_ARG),
+    (dict(total=-1), DA.DA_ERR_INVALID_ARG),
+    (dict(max_q_len=0), DA.DA_ERR_INVALID_ARG),
+    (dict(group=3), DA.DA_ERR_INVALID_ARG),
+    (dict(depth=96), DA.DA_ERR_UNSUPPORTED),
+    # workspace sized for rows = total * H: 3 tokens x 8 heads at P = 4
+    (dict(num_partitions=4, workspace=1, wbytes=16), DA.DA_ERR_WORKSPACE),
+    (dict(total=0), DA.DA_OK),                     # no tokens: nothing launched
+])
+def test_ragged_argument_checks(over, code):
+    assert _call_ragged(**over) == code
+
+
+def test_mla_ragged_argument_checks():
+    lib = DA.library()
+    # mla_decode_ragged(q, q_offsets, total, max_q_len, kv, table, ps, max_pages, valid, B, H,
+    #                   S, scale, P, sink, mask, out, lse, ws, wbytes, stream)
+    assert lib.mla_decode_ragged(1, None, 4, 2, 1, None, 0, 0, None, 2, 128, 64, 0.1, 1, None,
+                                 1, 1, None, None, 0, None) == DA.DA_ERR_INVALID_ARG
+    assert lib.mla_decode_ragged(1, 1, 4, 0, 1, None, 0, 0, None, 2, 128, 64, 0.1, 1, None,
+                                 1, 1, None, None, 0, None) == DA.DA_ERR_INVALID_ARG
+    assert lib.mla_decode_ragged(1, 1, 0, 2, 1, None, 0, 0, None, 2, 128, 64, 0.1, 1, None,
+                                 1, 1, None, None, 0, None) == DA.DA_OK

@@ -32,6 +32,15 @@
  *     score sigma_h and a zero value row), not multiplied by `scale`.
  *   - LSE = m + ln(l) of the full denominator, sink included.
  *   - A row with no visible key and no sink: out = 0, LSE = -inf.
+ *   - Sparse top-k ("flare_mla_decoding_dispatch", Parameters `sparse`; Args
+ *     `d_indices`, `indices_stride`, `topk_lengths`): the keys of sequence b
+ *     are the cache rows indices[b * indices_stride + i] for i <
+ *     topk_lengths[b] of a pool [pool_rows, KVH, D] (a gather at page size 1).
+ *     Every query token and head of the sequence attends to that one list; no
+ *     mask applies (the selection is the mask, and a row index carries no
+ *     position), so a causal mask together with indices is rejected.  A count
+ *     outside [0, indices_stride] or a counted index outside [0, pool_rows) is
+ *     an invalid call.  Partition p covers list positions [p*C, (p+1)*C).
  *   - Split-K ("mha_decoding_single_batch_pipelined", description: the keys
  *     are cut into consecutive ranges, one per block, whose max and exp-sum a
  *     separate merge pass combines): partition p covers
@@ -97,6 +106,10 @@ typedef struct {
   const uint32_t* q_offsets;  /* ragged q: [B+1] cumulative token offsets, the tokens of
                                  sequence b being rows q_offsets[b]..q_offsets[b+1] of a
                                  [total, H, D] q; NULL: T tokens per sequence  */
+  const int32_t* indices;     /* sparse: [B, indices_stride] pool rows, or NULL       */
+  int indices_stride;
+  const int32_t* topk_lengths;/* sparse: [B] listed keys of each sequence           */
+  int64_t pool_rows;          /* sparse: rows of the pool k (and v) is               */
 } problem_t;
 
 /* Query tokens of sequence b, and the q row of its first token. */
@@ -126,7 +139,9 @@ static void locate_token(const problem_t* p, int64_t token, int* b, int* t) {
  * in a cache whose rows hold `width` elements. */
 static size_t kv_index(const problem_t* p, int b, int j, int g, int d, int width) {
   size_t row;
-  if (p->page_table) {
+  if (p->indices) {
+    row = (size_t)p->indices[(size_t)b * p->indices_stride + (size_t)j];
+  } else if (p->page_table) {
     uint32_t phys = p->page_table[(size_t)b * p->max_pages + (size_t)(j / p->page_size)];
     row = (size_t)phys * p->page_size + (size_t)(j % p->page_size);
   } else {
@@ -146,6 +161,7 @@ static double value_elem(const problem_t* p, int b, int j, int g, int d) {
 
 /* Number of keys visible to row (b, t). */
 static int visible_keys(const problem_t* p, int b, int t) {
+  if (p->indices) return p->topk_lengths[b]; /* sparse: the listed keys, no mask */
   int n = p->valid_length ? (int)p->valid_length[b] : p->S;
   if (p->causal) {
     int lim = n - seq_tokens(p, b) + t + 1;
@@ -204,9 +220,13 @@ static problem_t make_problem(const void* q, const void* k, const void* v, int d
                               float k_scale, float v_scale, const uint32_t* page_table,
                               int page_size, int max_pages, const uint32_t* valid_length, int B,
                               int T, int H, int KVH, int D, int Dv, int S, float scale,
-                              const float* sink, int causal, const uint32_t* q_offsets) {
+                              const float* sink, int causal, const uint32_t* q_offsets,
+                              const int32_t* indices, int indices_stride,
+                              const int32_t* topk_lengths, int64_t pool_rows) {
   problem_t p;
   p.q_offsets = q_offsets;
+  p.indices = indices; p.indices_stride = indices_stride;
+  p.topk_lengths = topk_lengths; p.pool_rows = pool_rows;
   p.q = q; p.k = k; p.v = v;
   p.q_dtype = (dtype == ORACLE_BF16_Q_E4M3_KV) ? ORACLE_BF16 : dtype;
   p.kv_dtype = (dtype == ORACLE_BF16_Q_E4M3_KV) ? ORACLE_E4M3 : dtype;
@@ -229,11 +249,23 @@ static int check_problem(const problem_t* p) {
   if (p->H % p->KVH != 0) return -1;
   if (p->v == NULL && p->Dv > p->D) return -1;
   if (p->page_table && (p->page_size < 1 || p->max_pages < 1)) return -1;
+  if (p->indices) {
+    if (p->causal || p->page_table || !p->topk_lengths || p->indices_stride < 0) return -1;
+    for (int b = 0; b < p->B; ++b) {
+      int n = p->topk_lengths[b];
+      if (n < 0 || n > p->indices_stride) return -1;
+      for (int j = 0; j < n; ++j) {
+        int32_t r = p->indices[(size_t)b * p->indices_stride + (size_t)j];
+        if (r < 0 || (int64_t)r >= p->pool_rows) return -1;
+      }
+    }
+  }
   return 0;
 }
 
 static int longest_cache(const problem_t* p) {
   int s = p->S;
+  if (p->indices && p->indices_stride > s) s = p->indices_stride;
   if (p->valid_length)
     for (int b = 0; b < p->B; ++b)
       if ((int)p->valid_length[b] > s) s = (int)p->valid_length[b];
@@ -249,11 +281,13 @@ int oracle_decode_attention(const void* q, const void* k, const void* v, int dty
                             float k_scale, float v_scale, const uint32_t* page_table, int page_size, int max_pages,
                             const uint32_t* valid_length, int B, int T, int H, int KVH, int D,
                             int Dv, int S, float scale, const float* sink, int causal,
-                            const uint32_t* q_offsets, const int64_t* rows, int64_t num_rows,
+                            const uint32_t* q_offsets, const int32_t* indices,
+                            int indices_stride, const int32_t* topk_lengths, int64_t pool_rows,
+                            const int64_t* rows, int64_t num_rows,
                             double* out, double* lse, int num_threads) {
   problem_t p = make_problem(q, k, v, dtype, k_scale, v_scale, page_table, page_size, max_pages,
                              valid_length, B, T, H, KVH, D, Dv, S, scale, sink, causal,
-                             q_offsets);
+                             q_offsets, indices, indices_stride, topk_lengths, pool_rows);
   if (check_problem(&p)) return -1;
   int64_t n_rows = rows ? num_rows : total_tokens(&p) * H;
   int smax = longest_cache(&p);
@@ -294,11 +328,12 @@ int oracle_decode_partials(const void* q, const void* k, const void* v, int dtyp
                            float k_scale, float v_scale, const uint32_t* page_table, int page_size, int max_pages,
                            const uint32_t* valid_length, int B, int T, int H, int KVH, int D,
                            int Dv, int S, float scale, int causal, const uint32_t* q_offsets,
-                           int num_partitions, int keys_per_partition, double* part_o,
+                           const int32_t* indices, int indices_stride,
+                           const int32_t* topk_lengths, int64_t pool_rows, int num_partitions, int keys_per_partition, double* part_o,
                            double* part_m, double* part_l, int num_threads) {
   problem_t p = make_problem(q, k, v, dtype, k_scale, v_scale, page_table, page_size, max_pages,
                              valid_length, B, T, H, KVH, D, Dv, S, scale, NULL, causal,
-                             q_offsets);
+                             q_offsets, indices, indices_stride, topk_lengths, pool_rows);
   if (check_problem(&p) || num_partitions < 1 || keys_per_partition < 1) return -1;
   int64_t n_rows = total_tokens(&p) * H;
   int64_t n_items = n_rows * num_partitions;

@@ -11,6 +11,10 @@ Array conventions (numpy, C-contiguous):
     [num_pages, page_size, KVH, D]; v: same layout with Dv, or None meaning
     V = K[..., :Dv] (the MLA case, "flare_mla_decoding_dispatch", Args ``k``).
   * page_table: uint32 [B, max_pages]; valid_length: uint32 [B]; sink: float32 [H].
+  * sparse top-k: k (and v) is a pool [pool_rows, KVH, D]; indices int32 [B, stride]
+    lists the pool rows of each sequence's keys, topk_lengths int32 [B] how many
+    of them count ("flare_mla_decoding_dispatch", Args ``d_indices``,
+    ``indices_stride``, ``topk_lengths``).
 
 Every routine returns float64 results.  The meaning of each argument and the
 readings taken where the pages are silent are stated in decode_oracle.c.
@@ -44,12 +48,12 @@ def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH, extra_flag
 def _bind(lib):
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.oracle_decode_attention.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, i32, vp, i32, i32,
-                                            i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, i64, vp,
-                                            vp, i32]
+                                            i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, i32, vp,
+                                            i64, vp, i64, vp, vp, i32]
     lib.oracle_decode_attention.restype = i32
     lib.oracle_decode_partials.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, i32, vp, i32, i32,
-                                           i32, i32, i32, i32, i32, f32, i32, vp, i32, i32, vp, vp,
-                                           vp, i32]
+                                           i32, i32, i32, i32, i32, f32, i32, vp, vp, i32, vp, i64,
+                                           i32, i32, vp, vp, vp, i32]
     lib.oracle_decode_partials.restype = i32
     lib.oracle_splitk_merge.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp, vp]
     lib.oracle_splitk_merge.restype = i32
@@ -134,9 +138,29 @@ def _ragged(q, q_offsets):
     return q.reshape(1, *q.shape), qo, B, T
 
 
+def _sparse(k, v, indices, topk_lengths, batch):
+    """Sparse top-k: the pool [rows, KVH, D] as [rows, 1, KVH, D] for the shape checks,
+    the index list [B, stride], the counts [B], stride and pool rows."""
+    if indices is None:
+        if topk_lengths is not None:
+            raise ValueError("topk_lengths needs indices")
+        return k, v, None, None, 0, 0
+    k = np.asarray(k)
+    if k.ndim != 3 or (v is not None and np.asarray(v).ndim != 3):
+        raise ValueError("sparse: k (and v) must be pools [rows, KVH, D]")
+    idx = np.ascontiguousarray(indices, dtype=np.int32)
+    tl = np.ascontiguousarray(topk_lengths, dtype=np.int32)
+    if idx.ndim != 2 or idx.shape[0] != batch or tl.shape != (batch,):
+        raise ValueError("sparse: indices must be [B, stride] and topk_lengths [B]")
+    k4 = k.reshape(k.shape[0], 1, *k.shape[1:])
+    v4 = None if v is None else np.asarray(v).reshape(np.asarray(v).shape[0], 1,
+                                                      *np.asarray(v).shape[1:])
+    return k4, v4, idx, tl, idx.shape[1], k.shape[0]
+
+
 def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=None,
               causal=False, depth_v=None, max_seq_len=None, rows=None, threads=0, lib=None,
-              k_scale=1.0, v_scale=1.0, q_offsets=None):
+              k_scale=1.0, v_scale=1.0, q_offsets=None, indices=None, topk_lengths=None):
     """Reference attention.  Returns (out, lse) as float64.
 
     q_offsets: ragged q -- q is [total, H, D] and the tokens of sequence b are rows
@@ -145,14 +169,21 @@ def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=N
     k_scale / v_scale: the real key (value) is the scale times the stored element
     (meant for e4m3 k / v; the value slice of MLA, v=None, uses k_scale).
 
+    indices / topk_lengths: sparse top-k -- k (and v) is a pool [pool_rows, KVH, D] and
+    the keys of sequence b are its rows indices[b, :topk_lengths[b]] (no mask).
+
     With rows=None: out [B, T, H, Dv], lse [B, T, H].  With rows (int64 row ids
     (b*T + t)*H + h): out [len(rows), Dv], lse [len(rows)].
     """
     lib = lib or load_library()
     q, qo, rB, rT = _ragged(q, q_offsets)
+    k, v, idx, tl, stride, pool_rows = _sparse(k, v, indices, topk_lengths,
+                                               rB if qo is not None else np.shape(q)[0])
     q, k, v, page_table, valid_length, sink, code, dims = _common(
         q, k, v, page_table, valid_length, sink, depth_v, max_seq_len)
     B, T, H, KVH, D, Dv, S, page_size, max_pages = dims
+    if idx is not None:
+        S = stride
     total = q.shape[0] * q.shape[1]
     if qo is not None:
         B, T = rB, rT
@@ -167,7 +198,8 @@ def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=N
                                      float(v_scale), _ptr(page_table), page_size,
                                      max_pages, _ptr(valid_length), B, T, H, KVH, D, Dv, S,
                                      float(scale), _ptr(sink), int(bool(causal)), _ptr(qo),
-                                     _ptr(rows), n, _ptr(out), _ptr(lse), int(threads))
+                                     _ptr(idx), stride, _ptr(tl), pool_rows, _ptr(rows), n,
+                                     _ptr(out), _ptr(lse), int(threads))
     if rc != 0:
         raise RuntimeError(f"oracle_decode_attention failed ({rc})")
     if rows is None:
@@ -179,14 +211,19 @@ def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=N
 
 def partials(q, k, v=None, *, scale, num_partitions, keys_per_partition, page_table=None,
              valid_length=None, causal=False, depth_v=None, max_seq_len=None, threads=0,
-             lib=None, k_scale=1.0, v_scale=1.0, q_offsets=None):
+             lib=None, k_scale=1.0, v_scale=1.0, q_offsets=None, indices=None,
+             topk_lengths=None):
     """Split-K partials.  Returns (O_p [P, rows, Dv], m_p [P, rows], l_p [P, rows]) with
-    rows = (q tokens) * H."""
+    rows = (q tokens) * H.  Sparse: partition p covers list positions [p*C, (p+1)*C)."""
     lib = lib or load_library()
     q, qo, rB, rT = _ragged(q, q_offsets)
+    k, v, idx, tl, stride, pool_rows = _sparse(k, v, indices, topk_lengths,
+                                               rB if qo is not None else np.shape(q)[0])
     q, k, v, page_table, valid_length, _, code, dims = _common(
         q, k, v, page_table, valid_length, None, depth_v, max_seq_len)
     B, T, H, KVH, D, Dv, S, page_size, max_pages = dims
+    if idx is not None:
+        S = stride
     if qo is not None:
         B, T = rB, rT
     rows = q.shape[0] * q.shape[1] * H
@@ -196,7 +233,8 @@ def partials(q, k, v=None, *, scale, num_partitions, keys_per_partition, page_ta
     rc = lib.oracle_decode_partials(_ptr(q), _ptr(k), _ptr(v), code, float(k_scale),
                                     float(v_scale), _ptr(page_table), page_size,
                                     max_pages, _ptr(valid_length), B, T, H, KVH, D, Dv, S,
-                                    float(scale), int(bool(causal)), _ptr(qo), int(num_partitions),
+                                    float(scale), int(bool(causal)), _ptr(qo), _ptr(idx), stride,
+                                    _ptr(tl), pool_rows, int(num_partitions),
                                     int(keys_per_partition), _ptr(po), _ptr(pm), _ptr(pl),
                                     int(threads))
     if rc != 0:

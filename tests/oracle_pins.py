@@ -575,6 +575,126 @@ def pin_sdpa_e4m3_scaled_kv(lib):
     _close(lse, rl, what="lse")
 
 
+# --------------------------------------------------------------------------
+# Sparse top-k: each sequence's keys are listed pool rows
+# --------------------------------------------------------------------------
+
+def _sparse_case(rng, B, T, H, D, R, stride, lens, dtype="f32"):
+    q = _randn(rng, (B, T, H, D), dtype)
+    pool = _randn(rng, (R, 1, D), dtype)
+    idx = rng.integers(0, R, size=(B, stride)).astype(np.int32)
+    return q, pool, idx, np.asarray(lens, np.int32)
+
+
+def pin_sparse_identity_list_equals_dense(lib):
+    """Listing rows b*S .. b*S + N_b - 1 of the dense cache (read as a pool) gives the
+    dense result with valid_length N_b; list entries past the count name a NaN row
+    and are never read."""
+    rng = _rng(40)
+    B, T, H, D, Dv, S = 3, 2, 4, 24, 16, 19
+    q, kv = _randn(rng, (B, T, H, D), "bf16"), _randn(rng, (B, S, 1, D), "bf16")
+    lens = np.array([19, 7, 0], np.uint32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    ref = O.attention(q, kv, None, depth_v=Dv, scale=0.3, valid_length=lens, sink=sink, lib=lib)
+    pool = np.concatenate([kv.reshape(B * S, 1, D), np.full((1, 1, D), 0x7FC0, np.uint16)])
+    idx = np.full((B, S + 2), B * S, np.int32)
+    for b in range(B):
+        idx[b, :lens[b]] = b * S + np.arange(lens[b])
+    got = O.attention(q, pool, None, depth_v=Dv, scale=0.3, sink=sink,
+                      indices=idx, topk_lengths=lens.astype(np.int32), lib=lib)
+    _close(got[0], ref[0], tol=1e-12, what="out")
+    _close(got[1], ref[1], tol=1e-12, what="lse")
+
+
+def pin_sdpa_sparse_gather(lib):
+    """torch fp64 SDPA over the gathered rows (a repeated index counts twice, a zero
+    count leaves only the sink), MLA value slice, sink as a virtual key."""
+    rng = _rng(41)
+    B, T, H, D, Dv, R, stride = 3, 2, 4, 20, 12, 40, 9
+    q, pool, idx, lens = _sparse_case(rng, B, T, H, D, R, stride, [9, 4, 0])
+    idx[0, 3] = idx[0, 5]
+    vis = np.arange(stride)[None, :] < lens[:, None]
+    idx[~vis] = R                                                      # a NaN row, never read
+    pool = np.concatenate([pool, np.full((1, 1, D), np.nan, np.float32)])
+    sink = rng.standard_normal(H).astype(np.float32)
+    out, lse = O.attention(q, pool, None, depth_v=Dv, scale=0.4, sink=sink, indices=idx,
+                           topk_lengths=lens, lib=lib)
+    kg = pool[np.where(vis, idx, 0)][:, :, 0]                          # [B, stride, D]
+    kx = np.concatenate([np.repeat(kg[:, :, None], H, axis=2),
+                         np.zeros((B, 1, H, D), np.float32)], axis=1)  # + sink key
+    vis = np.concatenate([vis, np.ones((B, 1), bool)], axis=1)
+    allowed = np.broadcast_to(vis[:, None, None, :], (B, H, T, stride + 1)).copy()
+    bias = np.zeros((B, H, T, stride + 1))
+    bias[..., stride] = sink.astype(np.float64)[None, :, None]
+    ro, rl = _sdpa(q, kx, kx[..., :Dv].copy(), float(np.float32(0.4)), allowed=allowed,
+                   bias=bias)
+    _close(out, ro, what="out")
+    _close(lse, rl, what="lse")
+
+
+def pin_sparse_list_order(lib):
+    """The keys form a set: reordering a sequence's listed rows changes nothing."""
+    rng = _rng(42)
+    B, T, H, D, R, stride = 2, 1, 3, 16, 30, 11
+    q, pool, idx, lens = _sparse_case(rng, B, T, H, D, R, stride, [11, 6])
+    a = O.attention(q, pool, pool, scale=0.5, indices=idx, topk_lengths=lens, lib=lib)
+    idx2 = idx.copy()
+    for b in range(B):
+        idx2[b, :lens[b]] = idx[b, rng.permutation(lens[b])]
+    b_ = O.attention(q, pool, pool, scale=0.5, indices=idx2, topk_lengths=lens, lib=lib)
+    _close(a[0], b_[0], tol=1e-12, what="out")
+    _close(a[1], b_[1], tol=1e-12, what="lse")
+
+
+def pin_sparse_paged_list(lib):
+    """A page table expanded into one row per key (page size 1) gives the paged result;
+    the pool's unused pages are NaN, so a wrong row shows."""
+    rng = _rng(43)
+    B, H, KVH, D, S, ps = 3, 4, 2, 8, 30, 4
+    q, k, v = (_randn(rng, (B, 1, H, D)), _randn(rng, (B, S, KVH, D)),
+               _randn(rng, (B, S, KVH, D)))
+    lens = np.array([30, 13, 1], np.uint32)
+    kp, vp, table = _paged_from_contiguous(rng, k, v, lens, ps)
+    ref = O.attention(q, kp, vp, scale=0.5, valid_length=lens, page_table=table, max_seq_len=S,
+                      lib=lib)
+    j = np.arange(S)
+    idx = (table[:, j // ps].astype(np.int64) * ps + j % ps).astype(np.int32)
+    got = O.attention(q, kp.reshape(-1, KVH, D), vp.reshape(-1, KVH, D), scale=0.5,
+                      indices=idx, topk_lengths=lens.astype(np.int32), lib=lib)
+    _close(got[0], ref[0], tol=1e-12, what="out")
+    _close(got[1], ref[1], tol=1e-12, what="lse")
+
+
+def pin_sparse_partials(lib):
+    """Sparse partitions cover list positions: each partial is SDPA over its slice of the
+    list, and the merge gives the full result."""
+    rng = _rng(44)
+    B, T, H, D, Dv, R, stride, C = 2, 2, 2, 12, 8, 25, 13, 4
+    q, pool, idx, lens = _sparse_case(rng, B, T, H, D, R, stride, [13, 6])
+    sink = rng.standard_normal(H).astype(np.float32)
+    ref = O.attention(q, pool, None, depth_v=Dv, scale=0.6, sink=sink, indices=idx,
+                      topk_lengths=lens, lib=lib)
+    P = -(-stride // C)
+    po, pm, pl = O.partials(q, pool, None, depth_v=Dv, scale=0.6, num_partitions=P,
+                            keys_per_partition=C, indices=idx, topk_lengths=lens, lib=lib)
+    out, lse = O.merge(po, pm, pl, num_heads=H, sink=sink, lib=lib)
+    _close(out.reshape(ref[0].shape), ref[0], tol=1e-12, what="merged out")
+    _close(lse.reshape(ref[1].shape), ref[1], tol=1e-12, what="merged lse")
+    po = po.reshape(P, B, T, H, Dv)
+    ml = (pm + np.log(np.where(pl > 0, pl, 1.0))).reshape(P, B, T, H)
+    for p in range(P):
+        for b in range(B):
+            lo, hi = p * C, min((p + 1) * C, int(lens[b]))
+            if hi <= lo:
+                assert np.all(pl.reshape(P, B, T, H)[p, b] == 0), "empty partition"
+                continue
+            kg = pool[idx[b, lo:hi]][:, 0]
+            kk = np.repeat(kg[None, :, None], H, axis=2)
+            ro, rl = _sdpa(q[b:b + 1], kk, kk[..., :Dv].copy(), float(np.float32(0.6)))
+            _close(po[p, b], ro[0], what=f"O_p p={p} b={b}")
+            _close(ml[p, b], rl[0], what=f"m_p + ln l_p p={p} b={b}")
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}
 
 

@@ -58,6 +58,17 @@ MUTANTS = [
      "return p->q_offsets ? (int)(p->q_offsets[b + 1] - p->q_offsets[b]) : p->T;", "return p->T;"),
     ("ragged_boundary_token_misplaced", "(int64_t)p->q_offsets[s + 1] <= token) ++s;",
      "(int64_t)p->q_offsets[s + 1] < token) ++s;"),
+    # sparse top-k lists
+    ("sparse_list_row_stride", "row = (size_t)p->indices[(size_t)b * p->indices_stride + (size_t)j];",
+     "row = (size_t)p->indices[(size_t)b * p->topk_lengths[0] + (size_t)j];"),
+    ("sparse_list_ignores_batch", "row = (size_t)p->indices[(size_t)b * p->indices_stride + (size_t)j];",
+     "row = (size_t)p->indices[(size_t)j];"),
+    ("sparse_position_as_row", "row = (size_t)p->indices[(size_t)b * p->indices_stride + (size_t)j];",
+     "row = (size_t)b * p->indices_stride + (size_t)j;"),
+    ("sparse_count_off_by_one", "if (p->indices) return p->topk_lengths[b];",
+     "if (p->indices) return p->topk_lengths[b] - (p->topk_lengths[b] > 0);"),
+    ("sparse_count_is_stride", "if (p->indices) return p->topk_lengths[b];",
+     "if (p->indices) return p->indices_stride;"),
     ("max_not_subtracted_in_lse", "double w = exp(s[j] - m);", "double w = exp(s[j]);"),
     ("empty_row_lse_zero", "lse[i] = (l > 0.0) ? m + log(l) : -INFINITY;",
      "lse[i] = (l > 0.0) ? m + log(l) : 0.0;"),

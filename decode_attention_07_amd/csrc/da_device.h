@@ -96,6 +96,17 @@ __device__ __forceinline__ int wave_id_uniform() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
+// A wave-uniform 64-bit value (an address or byte offset) pinned to scalar
+// registers, so that a load can take it as its scalar base even where it reaches
+// the load through a phi after a divergent branch.  The readfirstlane builtin
+// returns int: each half goes back through uint32_t, or a low half with bit 31
+// set would be sign-extended into the high half.
+__device__ __forceinline__ uint64_t pin_uniform_u64(uint64_t x) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
 // ---- online-softmax state merge (log2 domain) ----------------------------------
 // Combines (mA, lA) with (mB, lB); returns the scale factors for A and B.
 __device__ __forceinline__ void merge_factors(float mA, float mB, float& m, float& fa,

@@ -82,9 +82,7 @@ __device__ __forceinline__ void stream_issue(const DecodeParams& p, int b, int g
   // keeps it in scalar registers (the loads take a scalar base) even where it
   // reaches here through a phi after a divergent branch.
   const size_t head_off0 = (row0 * p.num_kv_heads + g) * (size_t)C::ROW;
-  const size_t head_off =
-      ((size_t)__builtin_amdgcn_readfirstlane((uint32_t)(head_off0 >> 32)) << 32) |
-      (size_t)__builtin_amdgcn_readfirstlane((uint32_t)head_off0);
+  const size_t head_off = pin_uniform_u64(head_off0);
   const char* kb = (const char*)p.k + head_off;
   const char* vb = (const char*)p.v + head_off;
   const uint32_t rs = (uint32_t)p.num_kv_heads * C::ROW;  // bytes between keys of a head

@@ -118,8 +118,7 @@ __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage,
   // Uniform by construction; pinned to scalar registers (the loads take a
   // scalar base) even where it reaches here through a phi after a divergent branch.
   const size_t off0 = row0 * kRowBytes;
-  const size_t off = ((size_t)__builtin_amdgcn_readfirstlane((uint32_t)(off0 >> 32)) << 32) |
-                     (size_t)__builtin_amdgcn_readfirstlane((uint32_t)off0);
+  const size_t off = pin_uniform_u64(off0);
   const char* base = (const char*)p.k + off;
   const int nvalid = kend - j0;
   const uint4 t0 = *(const uint4*)tab;
@@ -137,6 +136,86 @@ __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage,
       if (key >= nvalid) off -= (uint32_t)key * kRowBytes;
       dma16(base, off, dst + i * kWaves * 1024);
     }
+  }
+}
+
+// Sparse top-k lists ("flare_mla_decoding_dispatch", Parameters `sparse`, Args
+// `d_indices`, `indices_stride`, `topk_lengths`): the 32 keys of a tile are
+// arbitrary pool rows, a gather at page size 1.  The stage layout stays the
+// same; only the loads change.  Wave w fills keys 8w .. 8w + 7 of the tile: its
+// load i (0..8) writes stage chunks 64 (9w + i) + lane, which is chunk position
+// q = (64 i + lane) % 72 of key 8w + (64 i + lane) / 72.  One load spans at
+// most two keys, sp_lo(i) below lane sp_split(i) and sp_lo(i) + 1 from it on;
+// the byte offsets of the wave's 8 rows are uniform scalars, so a lane's
+// offset is one of two scalars plus its fixed offset inside the row (in the
+// table).  Offsets are 32-bit from the pool base: the pool holds at most
+// 2^32 / 1152 rows, and each row index is clamped to the pool.
+// The 8 row indices of a tile are copied to LDS two tiles ahead of the tile's
+// loads (lanes 0..7, 4 bytes each), into a ring of 4 slots per wave; the waits
+// that let a tile's loads land cover them.
+constexpr int kSpSlots = 4;
+
+__device__ __forceinline__ constexpr int sp_lo(int i) { return (64 * i) / 72; }
+__device__ __forceinline__ constexpr int sp_split(int i) { return 72 * (sp_lo(i) + 1) - 64 * i; }
+
+__device__ __forceinline__ void dma_table_init_sparse(uint32_t* tab, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int cr = 64 * i + lane;  // chunk within the wave's 8 keys
+    const int key = 8 * wave + cr / 72;
+    const int q = cr % 72;
+    tab[i] = 16u * (uint32_t)((q & ~7) | ((q & 7) ^ swz(key)));
+  }
+}
+
+// 4 bytes per lane from base + voff into LDS at lds_base + 4 * lane
+// (global_load_lds_dword).
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dword %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds_base)
+               : "memory");
+}
+
+// Requests the row indices of tile t (keys k_lo + 32 t ..) of this wave into
+// its slot.  Keys at or past kend take the partition's first key (a listed
+// row, finite data; masked out of the softmax), so that the index reads stay
+// inside the list.
+__device__ __forceinline__ void sp_rows_issue(const DecodeParams& p, int b, int t, int k_lo,
+                                              int kend, int wave, int lane, uint32_t slot) {
+  const int key = k_lo + t * kBN + 8 * wave + (lane & 7);
+  const int src = key < kend ? key : k_lo;
+  // the list's base is uniform: pinned to scalar registers for the load
+  const uint64_t base = pin_uniform_u64((uint64_t)(p.indices + (size_t)b * p.max_seq_len));
+  if (lane < 8) dma4((const void*)base, 4u * (uint32_t)src, slot);
+}
+
+// Requests tile t of a sparse list into one LDS stage (and the indices of
+// tile t + 2 into their slot): kDmaPerWave + 1 loads per wave.
+__device__ __forceinline__ void mla_issue_sparse(const DecodeParams& p, uint32_t stage, int b,
+                                                 int t, int k_lo, int kend, int wave, int lane,
+                                                 const uint32_t* tab, const int32_t* slots,
+                                                 uint32_t slots_lds) {
+  const int32_t* mine = slots + ((t & (kSpSlots - 1)) * kWaves + wave) * 8;
+  const int4 ra = *(const int4*)mine;
+  const int4 rb = *(const int4*)(mine + 4);
+  const int rw[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+  const uint32_t last = p.pool_rows - 1u;
+  uint32_t off[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t r = (uint32_t)__builtin_amdgcn_readfirstlane(rw[e]);
+    off[e] = (r < last ? r : last) * (uint32_t)kRowBytes;
+  }
+  sp_rows_issue(p, b, t + 2, k_lo, kend, wave, lane,
+                slots_lds + (uint32_t)((((t + 2) & (kSpSlots - 1)) * kWaves + wave) * 32));
+  const uint4 t0 = *(const uint4*)tab;
+  const uint4 t1 = *(const uint4*)(tab + 4);
+  const uint32_t e[kDmaPerWave] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w, tab[8]};
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + wave * (kDmaPerWave * 1024));
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int lo = sp_lo(i);
+    const uint32_t row = (lo == 7 || lane < sp_split(i)) ? off[lo] : off[lo + 1];
+    dma16(p.k, row + e[i], dst + i * 1024);
   }
 }
 
@@ -365,8 +444,13 @@ struct BoolTag {
   static constexpr bool value = V;
 };
 
+// SPARSE: keys from a top-k list of pool rows (p.indices) instead of the
+// contiguous or paged cache.
+template <bool SPARSE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
+  // loads per wave per tile request
+  constexpr int kIssue = kDmaPerWave + (SPARSE ? 1 : 0);
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
   // XCD-aware decode of the block id: blocks i and i + 8 share an XCD; the
   // n_mblocks row blocks of one (partition, sequence) get ids 8 apart.
@@ -437,12 +521,37 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   __shared__ __attribute__((aligned(16))) int votes[2][kWaves];
   __shared__ __attribute__((aligned(16))) uint32_t dma_tab[kThreads * kTabPerLane];
   const uint32_t* tab = dma_tab + threadIdx.x * kTabPerLane;  // this lane's own entries
-  dma_table_init(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
+  if constexpr (SPARSE)
+    dma_table_init_sparse(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
+  else
+    dma_table_init(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
+  // Sparse lists: row indices of tiles t, t + 1 sit in slots t % 4, (t + 1) % 4
+  // when tile t is requested.
+  __shared__ __attribute__((aligned(16))) int32_t sp_slots[kSpSlots * kWaves * 8];
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const uint32_t stage = lds0 + (uint32_t)((t & (kStages - 1)) * kTileBytes);
+    if constexpr (SPARSE)
+      mla_issue_sparse(p, stage, b, t, k_lo, hmax, wave, lane, tab, sp_slots,
+                       (uint32_t)(uintptr_t)sp_slots);
+    else
+      mla_issue(p, stage, b, k_lo + t * kBN, hmax, wave, tab);
+  };
+  // Sparse lists: the indices of tiles 0 and 1, waited for before tile 0 is
+  // requested.
+  auto prime = [&]() __attribute__((always_inline)) {
+    if constexpr (SPARSE) {
+      for (int t = 0; t < 2; ++t)
+        sp_rows_issue(p, b, t, k_lo, hmax, wave, lane,
+                      (uint32_t)(uintptr_t)sp_slots + (uint32_t)((t * kWaves + wave) * 32));
+      wait_vm_lgkm0<0>();
+    }
+  };
   if (n_tot > 0) {
     // Tile 0 is requested while the Q loads are in flight; both are waited for
     // before anything else is issued, so that only tile requests are counted
     // below.
-    mla_issue(p, lds0, b, k_lo, hmax, wave, tab);
+    prime();
+    issue(0);
     wait_vm_lgkm0<0>();
     // Rows outside the fold get Q = 0; a negative scale flips Q's sign (exact).
     const uint32_t qx = p.scale_log2 < 0.f ? 0x80008000u : 0u;
@@ -457,8 +566,8 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     for (;;) {  // one pass over the partition; repeated only after a restart
       // tile 0 is requested on entry; tile 1 now; wait for tile 0
       if (n_tot > 1) {
-        mla_issue(p, lds0 + kTileBytes, b, k_lo + kBN, hmax, wave, tab);
-        wait_vm_lgkm0<kDmaPerWave>();
+        issue(1);
+        wait_vm_lgkm0<kIssue>();
       } else {
         wait_vm_lgkm0<0>();
       }
@@ -476,9 +585,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         int4 prev = make_int4(0, 0, 0, 0);
         if (PV) prev = *(const int4*)votes[(i - 1) & 1];
         const bool ahead = i + 2 < n_tot;
-        if (ahead)  // into the stage of tile i - 2, last read a barrier ago
-          mla_issue(p, lds0 + ((i + 2) & (kStages - 1)) * kTileBytes, b, k_lo + (i + 2) * kBN,
-                    hmax, wave, tab);
+        if (ahead) issue(i + 2);  // into the stage of tile i - 2, last read a barrier ago
         f32x16_t s0, s1;
         mla_scores(smem + (i & (kStages - 1)) * kTileBytes, qf, kofs, s0, s1);
         bool need = false;
@@ -492,7 +599,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         if (lane == 0) votes[i & 1][wave] = __builtin_amdgcn_ballot_w64(need) != 0;
         // tile i + 1 must have landed: tile i + 2 may stay in flight
         if (ahead)
-          wait_vm_lgkm0<kDmaPerWave>();
+          wait_vm_lgkm0<kIssue>();
         else
           wait_vm_lgkm0<0>();
         __syncthreads();
@@ -522,7 +629,8 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       lsum = 0.f;
       lsr = 0.f;
       __syncthreads();  // every wave has read the votes before the next pass writes them
-      mla_issue(p, lds0, b, k_lo, hmax, wave, tab);  // tile 0 of the next pass
+      prime();
+      issue(0);  // tile 0 of the next pass
     }
   }
 
@@ -582,7 +690,12 @@ hipError_t launch_mla(const DecodeParams& p, hipStream_t s) {
   const int n_mblocks = p.row_blocks;
   const int n_work = p.num_partitions * p.batch;
   const int grid = ((n_work + 7) / 8) * 8 * n_mblocks;
-  hipLaunchKernelGGL(mla_decode_kernel, dim3(grid), dim3(kThreads), 0, s, p, n_mblocks, n_work);
+  if (p.indices)
+    hipLaunchKernelGGL(mla_decode_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p, n_mblocks,
+                       n_work);
+  else
+    hipLaunchKernelGGL(mla_decode_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p, n_mblocks,
+                       n_work);
   return hipGetLastError();
 }
 

@@ -37,7 +37,8 @@ ROTATE_BYTES = 2 << 30  # >= 8x the last-level cache
 
 WORKLOADS = {"tiny": W.TINY_MHA, "gqa": W.GQA, "paged": W.PAGED, "mla": W.MLA,
              "mla_mtp": W.MLA_MTP, "long": W.LONG, "gqa_fp8": W.GQA_FP8,
-             "paged_fp8": W.PAGED_FP8, "gqa_ragged_q": W.GQA_RAGGED_Q}
+             "paged_fp8": W.PAGED_FP8, "gqa_ragged_q": W.GQA_RAGGED_Q,
+             "mla_sparse": W.MLA_SPARSE}
 
 CSRC = os.path.join(ROOT, "decode_attention_07_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -147,8 +148,11 @@ def parse():
 
 
 def sample_inputs(inp: W.Inputs, nb: int) -> W.Inputs:
-    """The first nb sequences of an instance (same cache pool when paged)."""
+    """The first nb sequences of an instance (same cache pool when paged or sparse)."""
     wl = inp.wl.with_(batch=nb)
+    if inp.indices is not None:
+        return W.Inputs(wl, inp.q[:nb], inp.k, None, None, None, inp.sink,
+                        indices=inp.indices[:nb], topk_lengths=inp.topk_lengths[:nb])
     k = inp.k if inp.page_table is not None else inp.k[:nb]
     v = None if inp.v is None else (inp.v if inp.page_table is not None else inp.v[:nb])
     return W.Inputs(wl, inp.q[:nb], k, v,
@@ -164,6 +168,10 @@ def cpu_baseline(inp: W.Inputs, budget_s: float):
     tokens = W.ragged_q_tokens(wl)
 
     def oracle_call(smp):
+        if smp.indices is not None:
+            return O.attention(smp.q, smp.k, None, scale=wl.softmax_scale, sink=smp.sink,
+                               depth_v=wl.dv, indices=smp.indices,
+                               topk_lengths=smp.topk_lengths)
         kw = dict(scale=wl.softmax_scale, page_table=smp.page_table,
                   valid_length=smp.valid_length, sink=smp.sink, causal=wl.causal,
                   depth_v=wl.dv, max_seq_len=wl.max_seq_len, k_scale=wl.k_scale,
@@ -224,7 +232,9 @@ def main():
     for inp in host_sets:
         dev_sets.append(dict(q=DA.to_device(inp.q), k=DA.to_device(inp.k),
                              v=DA.to_device(inp.v), table=DA.to_device(inp.page_table),
-                             valid=DA.to_device(inp.valid_length), sink=DA.to_device(inp.sink)))
+                             valid=DA.to_device(inp.valid_length), sink=DA.to_device(inp.sink),
+                             indices=DA.to_device(inp.indices),
+                             topk=DA.to_device(inp.topk_lengths)))
     ragged_q = W.ragged_q_tokens(wl)
     if ragged_q is not None:  # q rows packed per sequence (its first tokens[b] tokens)
         for inp, d in zip(host_sets, dev_sets):
@@ -235,8 +245,11 @@ def main():
     kv_bytes = footprint
     S = wl.max_seq_len
     B, T, H = wl.batch, wl.q_len, wl.num_heads
-    P = args.partitions or DA.num_partitions(B, T, H, wl.kv_heads, wl.depth, wl.dv, S,
-                                             ragged=first.valid_length is not None)
+    if wl.topk:
+        P = args.partitions or DA.mla_sparse_num_partitions(B, T, H, wl.topk)
+    else:
+        P = args.partitions or DA.num_partitions(B, T, H, wl.kv_heads, wl.depth, wl.dv, S,
+                                                 ragged=first.valid_length is not None)
     split = P > 1 and ragged_q is None  # a ragged-q call is timed as one full call
     ws = torch.zeros(DA.decode_workspace_size(P, B, T, H, wl.dv), dtype=torch.uint8,
                      device="cuda")  # zero-filled once: the work-queue word starts at 0
@@ -252,6 +265,10 @@ def main():
     # one ctypes call per kernel, far less than the kernel itself, so the device
     # never waits for the host.
     def partition_call(d):
+        if wl.topk:
+            return DA.mla_decode_sparse_partials(d["q"], d["k"], d["indices"], d["topk"],
+                                                 scale=wl.softmax_scale, num_partitions=P,
+                                                 workspace=ws, prepare=True)
         if wl.mla:
             return DA.mla_decode_partials(d["q"], d["k"], scale=wl.softmax_scale,
                                           num_partitions=P, page_table=d["table"],
@@ -270,6 +287,11 @@ def main():
                                 out=out.view(-1, wl.dv), lse=lse.view(-1), prepare=True)
 
     def full_call(d):
+        if wl.topk:
+            return DA.mla_decode_sparse(d["q"], d["k"], d["indices"], d["topk"],
+                                        scale=wl.softmax_scale, num_partitions=P,
+                                        sink_weights=d["sink"], out=out, lse=lse, workspace=ws,
+                                        prepare=True)
         kw = dict(scale=wl.softmax_scale, page_table=d["table"], valid_length=d["valid"],
                   max_seq_len=S, num_partitions=P, sink_weights=d["sink"], causal=wl.causal,
                   out=out, lse=lse, workspace=ws, prepare=True)
@@ -355,6 +377,7 @@ def main():
         "config": {"workload": wl.name, "batch": B, "q_len": T, "num_q_heads": H,
                    "num_kv_heads": wl.kv_heads, "depth": wl.depth, "depth_v": wl.dv,
                    "max_seq_len": S, "page_size": wl.page_size, "partitions": P,
+                   **({"topk": wl.topk} if wl.topk else {}),
                    "kv_bytes_per_step": kv_bytes, "input_sets": R},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

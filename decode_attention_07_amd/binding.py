@@ -27,7 +27,8 @@ EXPORTS = ("decode_attention_status_string", "decode_num_partitions", "decode_wo
            "decode_workspace_o_offset", "decode_workspace_max_offset",
            "decode_workspace_sum_offset", "decode_attention", "decode_attention_ragged",
            "decode_attention_fp8kv", "decode_attention_fp8kv_partials", "mla_decode_ragged",
-           "decode_attention_partials", "mla_decode", "mla_decode_partials", "splitk_reduce")
+           "decode_attention_partials", "mla_decode", "mla_decode_partials", "mla_decode_sparse",
+           "mla_decode_sparse_partials", "mla_sparse_num_partitions", "splitk_reduce")
 
 _lock = threading.Lock()
 _lib = None
@@ -75,6 +76,15 @@ def _declare(lib):
     lib.mla_decode_partials.argtypes = [vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, f32, i32,
                                         i32, vp, sz, vp]
     lib.mla_decode_partials.restype = i32
+    i64 = ctypes.c_longlong
+    lib.mla_decode_sparse.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32, vp, vp,
+                                      vp, vp, sz, vp]
+    lib.mla_decode_sparse.restype = i32
+    lib.mla_decode_sparse_partials.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32,
+                                               i32, vp, sz, vp]
+    lib.mla_decode_sparse_partials.restype = i32
+    lib.mla_sparse_num_partitions.argtypes = [i32] * 5
+    lib.mla_sparse_num_partitions.restype = i32
     lib.splitk_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, vp, vp]
     lib.splitk_reduce.restype = i32
     return lib
@@ -459,6 +469,60 @@ def mla_decode_partials(q, kv, *, scale, num_partitions, page_table=None, valid_
             wbytes, _stream(stream))
     return _finish(library().mla_decode_partials, args, "mla_decode_partials", workspace,
                    (q, kv, page_table, valid_length, workspace), prepare)
+
+
+def mla_sparse_num_partitions(batch, q_len, num_q_heads, topk, num_cus=0) -> int:
+    p = library().mla_sparse_num_partitions(batch, q_len, num_q_heads, topk, num_cus)
+    if p < 1:
+        raise DecodeAttentionError(p, "mla_sparse_num_partitions")
+    return p
+
+
+def _sparse_args(q, kv, indices, topk_lengths):
+    _need(q, "q", 4, (torch.bfloat16,))
+    _need(kv, "kv", 3, (torch.bfloat16,))
+    _need(indices, "indices", 2, (torch.int32,))
+    _need(topk_lengths, "topk_lengths", 1, (torch.int32,))
+    B, T, H, D = q.shape
+    if D != MLA_DEPTH or kv.shape[1] != 1 or kv.shape[2] != MLA_DEPTH:
+        raise ValueError("sparse MLA needs q [..., 576] and a pool kv [rows, 1, 576]")
+    if indices.shape[0] != B or topk_lengths.shape[0] != B:
+        raise ValueError("indices [B, stride] and topk_lengths [B] must match q's batch")
+    return B, T, H, kv.shape[0], indices.shape[1]
+
+
+def mla_decode_sparse(q, kv, indices, topk_lengths, *, scale, num_partitions=0,
+                      sink_weights=None, out=None, lse=None, workspace=None, stream=None,
+                      want_lse=True, prepare=False):
+    """Sparse top-k MLA: sequence b attends to pool rows indices[b, :topk_lengths[b]]
+    of kv [pool_rows, 1, 576].  Returns (out [B,T,H,512], lse [B,T,H]), or with
+    prepare=True a BoundCall."""
+    B, T, H, R, stride = _sparse_args(q, kv, indices, topk_lengths)
+    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    P = int(num_partitions) or (mla_sparse_num_partitions(B, T, H, stride) if B else 1)
+    if out is None:
+        out = torch.empty((B, T, H, MLA_DEPTH_V), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device)
+    args = (_ptr(q), _ptr(kv), R, _ptr(indices), stride, _ptr(topk_lengths), B, T, H,
+            float(scale), P, _ptr(sink_weights), _ptr(out), _ptr(lse), _ptr(workspace), wbytes,
+            _stream(stream))
+    return _finish(library().mla_decode_sparse, args, "mla_decode_sparse", (out, lse),
+                   (q, kv, indices, topk_lengths, sink_weights, out, lse, workspace), prepare)
+
+
+def mla_decode_sparse_partials(q, kv, indices, topk_lengths, *, scale, num_partitions,
+                               workspace=None, stream=None, prepare=False):
+    """Partition pass of mla_decode_sparse() alone.  Returns the workspace, or with
+    prepare=True a BoundCall."""
+    B, T, H, R, stride = _sparse_args(q, kv, indices, topk_lengths)
+    P = int(num_partitions)
+    workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device, always=True)
+    args = (_ptr(q), _ptr(kv), R, _ptr(indices), stride, _ptr(topk_lengths), B, T, H,
+            float(scale), P, _ptr(workspace), wbytes, _stream(stream))
+    return _finish(library().mla_decode_sparse_partials, args, "mla_decode_sparse_partials",
+                   workspace, (q, kv, indices, topk_lengths, workspace), prepare)
 
 
 def splitk_reduce(part_o, part_max, part_sum, *, num_q_heads, sink_weights=None,

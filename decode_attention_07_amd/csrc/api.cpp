@@ -335,6 +335,56 @@ int check_mla(const Common& c, const void* q, const void* kv) {
   return check_common(c);
 }
 
+// Sparse top-k MLA: the kernel addresses a row by a 32-bit byte offset from
+// the pool base, and a list entry by a 32-bit byte offset from its list.
+constexpr long long kMaxSparsePoolRows = (1ll << 32) / (kMlaDepth * 2);
+constexpr int kMaxTopk = 1 << 28;
+
+// The list's keys per partition: long enough that a block's partial write-back
+// (128 rows x 2 KB) stays below its share of the gathered rows, short enough
+// that a batch of a few dozen sequences fills the chip.
+constexpr int kSparseMinKeys = 512;
+
+int sparse_partitions(int batch, int q_len, int num_q_heads, int topk, int num_cus) {
+  if (num_cus <= 0) num_cus = device_cus();
+  const Plan pl = plan_mla(q_len, num_q_heads);
+  return heuristic_partitions(batch * pl.row_blocks, topk, num_cus, 1, kSparseMinKeys);
+}
+
+int check_sparse(const void* q, const void* kv, long long pool_rows, const int32_t* indices,
+                 int indices_stride, const int32_t* topk_lengths, int batch, int q_len,
+                 int num_q_heads, float scale) {
+  if (!q || !kv || !indices || !topk_lengths) return DA_ERR_INVALID_ARG;
+  if (batch < 0 || q_len < 1 || num_q_heads < 1 || indices_stride < 0 || pool_rows < 1)
+    return DA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return DA_ERR_INVALID_ARG;
+  if (pool_rows > kMaxSparsePoolRows || indices_stride > kMaxTopk) return DA_ERR_UNSUPPORTED;
+  return DA_OK;
+}
+
+// The partition pass and, for P > 1, the merge over the listed pool rows: the
+// counts take the place of the valid lengths and the list stride that of the
+// cache length.
+int run_sparse(const void* q, const void* kv, long long pool_rows, const int32_t* indices,
+               int indices_stride, const int32_t* topk_lengths, int batch, int q_len,
+               int num_q_heads, float scale, int num_partitions, bool partials_only,
+               const float* sink, void* out, float* lse, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const Common c{nullptr,        0,     0,           (const uint32_t*)topk_lengths,
+                 batch,          q_len, num_q_heads, indices_stride,
+                 DA_MASK_NONE,   scale};
+  int P = num_partitions;
+  if (P == 0) {
+    if (batch == 0) return DA_OK;
+    P = sparse_partitions(batch, q_len, num_q_heads, indices_stride, 0);
+  }
+  da::DecodeParams p = base_params(c, q, kv, kv, 1, num_q_heads, kMlaDepth, kMlaDepthV);
+  p.indices = indices;
+  p.pool_rows = (uint32_t)pool_rows;
+  return run(c, p, plan_mla(q_len, num_q_heads), true, P, partials_only, sink, out, lse,
+             workspace, workspace_bytes, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -539,6 +589,40 @@ int mla_decode_partials(const void* q, const void* kv, const uint32_t* page_tabl
       base_params(c, q, kv, kv, 1, num_q_heads, kMlaDepth, kMlaDepthV);
   return run(c, p, plan_mla(q_len, num_q_heads), true, num_partitions, true, nullptr, nullptr,
              nullptr, workspace, workspace_bytes, stream);
+}
+
+int mla_sparse_num_partitions(int batch, int q_len, int num_q_heads, int topk, int num_cus) {
+  if (batch < 1 || q_len < 1 || num_q_heads < 1 || topk < 0) return DA_ERR_INVALID_ARG;
+  return sparse_partitions(batch, q_len, num_q_heads, topk, num_cus);
+}
+
+int mla_decode_sparse(const void* q, const void* kv, long long pool_rows, const int32_t* indices,
+                      int indices_stride, const int32_t* topk_lengths, int batch, int q_len,
+                      int num_q_heads, float scale, int num_partitions,
+                      const float* sink_weights, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int rc = check_sparse(q, kv, pool_rows, indices, indices_stride, topk_lengths, batch, q_len,
+                        num_q_heads, scale);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  return run_sparse(q, kv, pool_rows, indices, indices_stride, topk_lengths, batch, q_len,
+                    num_q_heads, scale, num_partitions, false, sink_weights, out, lse, workspace,
+                    workspace_bytes, stream);
+}
+
+int mla_decode_sparse_partials(const void* q, const void* kv, long long pool_rows,
+                               const int32_t* indices, int indices_stride,
+                               const int32_t* topk_lengths, int batch, int q_len,
+                               int num_q_heads, float scale, int num_partitions, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  int rc = check_sparse(q, kv, pool_rows, indices, indices_stride, topk_lengths, batch, q_len,
+                        num_q_heads, scale);
+  if (rc) return rc;
+  if (num_partitions < 1 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  return run_sparse(q, kv, pool_rows, indices, indices_stride, topk_lengths, batch, q_len,
+                    num_q_heads, scale, num_partitions, true, nullptr, nullptr, nullptr,
+                    workspace, workspace_bytes, stream);
 }
 
 int splitk_reduce(const float* part_o, const float* part_max, const float* part_sum,

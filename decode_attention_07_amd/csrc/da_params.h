@@ -39,6 +39,11 @@ struct DecodeParams {
   // tokens per sequence.
   const uint32_t* q_offsets;
   int rows_total;               // q / out rows (tokens x heads): one partition's partial rows
+  // Sparse top-k (MLA): key i of sequence b is row indices[b * max_seq_len + i] of
+  // the pool k [pool_rows, 1, D], for i < valid_length[b] (the top-k counts);
+  // nullptr: keys from the contiguous or paged cache.
+  const int32_t* indices;
+  uint32_t pool_rows;
 };
 
 // Row-block geometry of a (batch, KV head): T*group rows (token-major:

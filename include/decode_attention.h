@@ -255,6 +255,56 @@ int mla_decode_partials(const void* q, const void* kv, const uint32_t* page_tabl
                         void* stream);
 
 /*
+ * Sparse top-k MLA ("flare_mla_decoding_dispatch", Parameters `sparse`; Args
+ * `d_indices`, `indices_stride`, `topk_lengths`): the keys of sequence b are
+ * not a prefix of its cache but a list of rows of a shared pool, a gather at
+ * page size 1.  Every query token and head of sequence b attends to the rows
+ *     indices[b * indices_stride + i],   0 <= i < topk_lengths[b]
+ * of the pool, with no mask (the list is the selection; a row index carries no
+ * position).  Reading of the pages: one list per sequence, shared by its
+ * q_len tokens; the counts play the part of valid_length and indices_stride
+ * (the allocation stride, the largest top-k) that of max_seq_len.
+ *   q             bf16 [batch, q_len, num_q_heads, 576] (the MTP token fold as
+ *                 for mla_decode())
+ *   kv            bf16 pool [pool_rows, 1, 576]; V = the first 512 columns
+ *   pool_rows     1 .. 3728270 (the pool is at most 4 GiB: rows are addressed
+ *                 by 32-bit byte offsets); larger pools are DA_ERR_UNSUPPORTED
+ *   indices       int32 [batch, indices_stride]; entries at or past a
+ *                 sequence's count are never read
+ *   topk_lengths  int32 [batch]; a count below 0 is 0, above indices_stride is
+ *                 indices_stride
+ *   out           bf16 [batch, q_len, num_q_heads, 512]; lse fp32 [batch, q_len,
+ *                 num_q_heads] or NULL; sink_weights as for decode_attention()
+ * The caller keeps every counted index inside [0, pool_rows).  The kernel
+ * clamps each one into that range before the load, so that a call with a bad
+ * index still reads only the pool (the value of such a row is then that of
+ * row min(index as unsigned, pool_rows - 1)).  Partition p covers list
+ * positions [p*C, (p+1)*C).  num_partitions = 0 selects
+ * mla_sparse_num_partitions(); the workspace is sized as for mla_decode() with
+ * the same batch, q_len and num_q_heads.
+ */
+int mla_decode_sparse(const void* q, const void* kv, long long pool_rows, const int32_t* indices,
+                      int indices_stride, const int32_t* topk_lengths, int batch, int q_len,
+                      int num_q_heads, float scale, int num_partitions,
+                      const float* sink_weights, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* The partition pass of mla_decode_sparse() alone (see decode_attention_partials()). */
+int mla_decode_sparse_partials(const void* q, const void* kv, long long pool_rows,
+                               const int32_t* indices, int indices_stride,
+                               const int32_t* topk_lengths, int batch, int q_len,
+                               int num_q_heads, float scale, int num_partitions, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * Partition count of mla_decode_sparse() with num_partitions = 0: enough
+ * (batch x row block x partition) blocks for one per compute unit, each
+ * partition keeping at least 512 list positions.  num_cus <= 0 queries the
+ * current device.  Returns P >= 1, or a negative status.
+ */
+int mla_sparse_num_partitions(int batch, int q_len, int num_q_heads, int topk, int num_cus);
+
+/*
  * Log-sum-exp merge of split-K partials ("mha_splitk_reduce"; "mla_splitk_reduce").
  *   part_o    fp32 [num_partitions, rows, depth_v]  normalised partial outputs
  *   part_max  fp32 [num_partitions, rows]           natural-log partial max

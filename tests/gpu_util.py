@@ -25,11 +25,16 @@ def device_inputs(inp: W.Inputs):
     return dict(q=DA.to_device(inp.q), k=DA.to_device(inp.k), v=DA.to_device(inp.v),
                 page_table=DA.to_device(inp.page_table),
                 valid_length=DA.to_device(inp.valid_length),
-                sink=DA.to_device(inp.sink))
+                sink=DA.to_device(inp.sink), indices=DA.to_device(inp.indices),
+                topk_lengths=DA.to_device(inp.topk_lengths))
 
 
 def run_gpu(wl: W.Workload, dev: dict, num_partitions=None, **kw):
     P = wl.num_partitions if num_partitions is None else num_partitions
+    if wl.topk:
+        return DA.mla_decode_sparse(dev["q"], dev["k"], dev["indices"], dev["topk_lengths"],
+                                    scale=wl.softmax_scale, num_partitions=P,
+                                    sink_weights=dev["sink"], **kw)
     common = dict(scale=wl.softmax_scale, page_table=dev["page_table"],
                   valid_length=dev["valid_length"], max_seq_len=wl.max_seq_len,
                   num_partitions=P, sink_weights=dev["sink"], causal=wl.causal)
@@ -43,6 +48,10 @@ def run_gpu(wl: W.Workload, dev: dict, num_partitions=None, **kw):
 
 
 def run_oracle(wl: W.Workload, inp: W.Inputs, rows=None):
+    if wl.topk:
+        return O.attention(inp.q, inp.k, None, scale=wl.softmax_scale, sink=inp.sink,
+                           depth_v=wl.dv, rows=rows, indices=inp.indices,
+                           topk_lengths=inp.topk_lengths)
     return O.attention(inp.q, inp.k, inp.v, scale=wl.softmax_scale, page_table=inp.page_table,
                        valid_length=inp.valid_length, sink=inp.sink, causal=wl.causal,
                        depth_v=wl.dv, max_seq_len=wl.max_seq_len, rows=rows,

@@ -20,7 +20,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     lib = ctypes.CDLL(DA.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
@@ -210,3 +210,48 @@ def test_mla_ragged_argument_checks():
                                  1, 1, None, None, 0, None) == DA.DA_ERR_INVALID_ARG
     assert lib.mla_decode_ragged(1, 1, 0, 2, 1, None, 0, 0, None, 2, 128, 64, 0.1, 1, None,
                                  1, 1, None, None, 0, None) == DA.DA_OK
+
+
+def _call_sparse(**over):
+    a = dict(q=1, kv=1, pool_rows=1000, indices=1, stride=64, topk=1, batch=2, q_len=1,
+             num_q_heads=128, scale=0.1, num_partitions=1, sink=None, out=1, lse=None,
+             workspace=None, wbytes=0, stream=None)
+    a.update(over)
+    return DA.library().mla_decode_sparse(
+        a["q"], a["kv"], a["pool_rows"], a["indices"], a["stride"], a["topk"], a["batch"],
+        a["q_len"], a["num_q_heads"], a["scale"], a["num_partitions"], a["sink"], a["out"],
+        a["lse"], a["workspace"], a["wbytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(indices=None), DA.DA_ERR_INVALID_ARG),
+    (dict(topk=None), DA.DA_ERR_INVALID_ARG),
+    (dict(kv=None), DA.DA_ERR_INVALID_ARG),
+    (dict(out=None), DA.DA_ERR_INVALID_ARG),
+    (dict(pool_rows=0), DA.DA_ERR_INVALID_ARG),
+    (dict(stride=-1), DA.DA_ERR_INVALID_ARG),
+    (dict(q_len=0), DA.DA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), DA.DA_ERR_INVALID_ARG),
+    (dict(num_partitions=-1), DA.DA_ERR_INVALID_ARG),
+    # rows are addressed by 32-bit byte offsets: at most 2^32 / 1152 of them
+    (dict(pool_rows=(1 << 32) // 1152 + 1), DA.DA_ERR_UNSUPPORTED),
+    (dict(num_partitions=3), DA.DA_ERR_WORKSPACE),
+    (dict(batch=0), DA.DA_OK),
+    (dict(batch=0, num_partitions=0), DA.DA_OK),
+])
+def test_sparse_argument_checks(over, code):
+    assert _call_sparse(**over) == code
+
+
+def test_sparse_partials_and_heuristic_checks():
+    lib = DA.library()
+    # mla_decode_sparse_partials(q, kv, R, idx, stride, topk, B, T, H, scale, P, ws, wbytes, s)
+    assert lib.mla_decode_sparse_partials(1, 1, 10, 1, 8, 1, 2, 1, 128, 0.1, 0, None, 0,
+                                          None) == DA.DA_ERR_INVALID_ARG
+    assert lib.mla_decode_sparse_partials(1, 1, 10, 1, 8, 1, 2, 1, 128, 0.1, 2, None, 0,
+                                          None) == DA.DA_ERR_WORKSPACE
+    assert DA.mla_sparse_num_partitions(64, 1, 128, 2048, num_cus=256) == 4
+    assert DA.mla_sparse_num_partitions(64, 2, 128, 2048, num_cus=256) == 2
+    assert DA.mla_sparse_num_partitions(1, 1, 128, 2048, num_cus=256) == 4
+    assert DA.mla_sparse_num_partitions(8, 1, 128, 100, num_cus=256) == 1
+    assert lib.mla_sparse_num_partitions(0, 1, 128, 2048, 256) == DA.DA_ERR_INVALID_ARG

@@ -113,6 +113,7 @@ class Workload:
     kv_dtype: str | None = None  # None -> dtype; 'e4m3' -> 8-bit K / V bits (q and out bf16)
     k_scale: float = 1.0      # 8-bit cache: real key = k_scale * stored key
     v_scale: float = 1.0      # 8-bit cache: real value = v_scale * stored value
+    topk: int = 0             # sparse top-k MLA: list stride (0 -> keys from the cache)
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -161,8 +162,14 @@ PAGED_FP8 = PAGED.with_(name="paged_ragged_fp8_b64_h64_kv8_d128_s32768_p128", kv
 GQA_RAGGED_Q = GQA.with_(name="gqa_ragged_q_b32_h32_kv8_d128_s4096_t1to4", q_len=4, causal=True,
                          extra={"q_tokens": (1, 4)})
 
+# Sparse top-k MLA (a DeepSeek-style selection of 2048 of each sequence's 8192 cached
+# rows): the same 64 sequences and heads as the MLA problem, each attending to its
+# own list of 2048 pool rows.
+MLA_SPARSE = MLA.with_(name="mla_sparse_bf16_b64_h128_d576_dv512_topk2048_s8192", seed=7006,
+                       topk=2048)
+
 ALL = {w.name: w for w in (TINY_MHA, GQA, PAGED, MLA, MLA_MTP, LONG, GQA_FP8, PAGED_FP8,
-                           GQA_RAGGED_Q)}
+                           GQA_RAGGED_Q, MLA_SPARSE)}
 
 
 def ragged_q_tokens(wl: Workload):
@@ -192,8 +199,12 @@ class Inputs:
     valid_length: np.ndarray | None
     page_table: np.ndarray | None
     sink: np.ndarray | None
+    indices: np.ndarray | None = None       # sparse: int32 [B, topk] pool rows
+    topk_lengths: np.ndarray | None = None  # sparse: int32 [B] listed keys
 
     def lengths(self) -> np.ndarray:
+        if self.topk_lengths is not None:
+            return self.topk_lengths.astype(np.int64)
         if self.valid_length is not None:
             return self.valid_length.astype(np.int64)
         return np.full(self.wl.batch, self.wl.max_seq_len, np.int64)
@@ -239,6 +250,28 @@ def _poison(arr: np.ndarray, dtype: str):
         arr[...] = np.float32(np.nan)
 
 
+def _sparse_inputs(wl: Workload, st, q, ctx, sink, poison: bool) -> Inputs:
+    """Sparse top-k: a pool of B*S rows (sequence b's context is rows b*S ..
+    b*S + N_b - 1) and one NaN row; sequence b lists min(topk, N_b) distinct rows of
+    its context, drawn without replacement in random order (a top-k selection
+    keeps no position order); list entries past the count name the NaN row, and so
+    do context rows past N_b."""
+    B, S, D = wl.batch, wl.max_seq_len, wl.depth
+    lens = ctx.astype(np.int64) if ctx is not None else np.full(B, S, np.int64)
+    k = _kv_tensor(st["k"], (B * S + 1, wl.kv_heads, D), wl.kv_type)
+    nan_row = B * S
+    rng = np.random.Generator(np.random.PCG64(st["pages"]))
+    tl = np.minimum(lens, wl.topk).astype(np.int32)
+    idx = np.full((B, wl.topk), nan_row, np.int32)
+    for b in range(B):
+        idx[b, :tl[b]] = b * S + rng.choice(int(lens[b]), size=int(tl[b]), replace=False)
+    if poison:
+        _poison(k[nan_row], wl.kv_type)
+        for b in range(B):
+            _poison(k[b * S + int(lens[b]):(b + 1) * S], wl.kv_type)
+    return Inputs(wl, q, k, None, None, None, sink, indices=idx, topk_lengths=tl)
+
+
 def make_inputs(wl: Workload, variant: int = 0, poison: bool = True) -> Inputs:
     """Draw one seeded instance of ``wl``."""
     st = _streams(wl, variant)
@@ -258,6 +291,8 @@ def make_inputs(wl: Workload, variant: int = 0, poison: bool = True) -> Inputs:
     if wl.sink:
         rng = np.random.Generator(np.random.PCG64(st["sink"]))
         sink = rng.standard_normal(H, dtype=np.float32)
+    if wl.topk:
+        return _sparse_inputs(wl, st, q, valid, sink, poison)
 
     page_table = None
     if wl.page_size:

@@ -39,7 +39,7 @@ ROTATE_BYTES = 2 << 30  # >= 8x the last-level cache
 WORKLOADS = {"tiny": W.TINY_MHA, "gqa": W.GQA, "paged": W.PAGED, "mla": W.MLA,
              "mla_mtp": W.MLA_MTP, "long": W.LONG, "gqa_fp8": W.GQA_FP8,
              "paged_fp8": W.PAGED_FP8, "gqa_ragged_q": W.GQA_RAGGED_Q,
-             "mla_sparse": W.MLA_SPARSE}
+             "mla_sparse": W.MLA_SPARSE, "mla_fp8": W.MLA_FP8}
 
 CSRC = os.path.join(ROOT, "decode_attention_07_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -286,6 +286,12 @@ def main():
             return DA.mla_decode_sparse_partials(d["q"], d["k"], d["indices"], d["topk"],
                                                  scale=wl.softmax_scale, num_partitions=P,
                                                  workspace=ws, prepare=True)
+        if wl.mla and wl.kv_type == "e4m3":
+            return DA.mla_decode_fp8kv_partials(d["q"], d["k"], k_scale=wl.k_scale,
+                                                scale=wl.softmax_scale, num_partitions=P,
+                                                page_table=d["table"], valid_length=d["valid"],
+                                                max_seq_len=S, causal=wl.causal, workspace=ws,
+                                                prepare=True)
         if wl.mla:
             return DA.mla_decode_partials(d["q"], d["k"], scale=wl.softmax_scale,
                                           num_partitions=P, page_table=d["table"],
@@ -315,6 +321,8 @@ def main():
         if ragged_q is not None:
             return DA.decode_attention_ragged(d["q"], d["q_offsets"], d["k"], d["v"],
                                               max_q_len=T, group=wl.group, **kw)
+        if wl.mla and wl.kv_type == "e4m3":
+            return DA.mla_decode_fp8kv(d["q"], d["k"], k_scale=wl.k_scale, **kw)
         if wl.mla:
             return DA.mla_decode(d["q"], d["k"], **kw)
         if wl.kv_type == "e4m3":

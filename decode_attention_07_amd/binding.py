@@ -27,7 +27,8 @@ EXPORTS = ("decode_attention_status_string", "decode_num_partitions", "decode_wo
            "decode_workspace_o_offset", "decode_workspace_max_offset",
            "decode_workspace_sum_offset", "decode_attention", "decode_attention_ragged",
            "decode_attention_fp8kv", "decode_attention_fp8kv_partials", "mla_decode_ragged",
-           "decode_attention_partials", "mla_decode", "mla_decode_partials", "mla_decode_sparse",
+           "decode_attention_partials", "mla_decode", "mla_decode_partials", "mla_decode_fp8kv",
+           "mla_decode_fp8kv_partials", "mla_decode_sparse",
            "mla_decode_sparse_partials", "mla_sparse_num_partitions", "splitk_reduce")
 
 _lock = threading.Lock()
@@ -76,6 +77,12 @@ def _declare(lib):
     lib.mla_decode_partials.argtypes = [vp, vp, vp, i32, i32, vp, i32, i32, i32, i32, f32, i32,
                                         i32, vp, sz, vp]
     lib.mla_decode_partials.restype = i32
+    lib.mla_decode_fp8kv.argtypes = [vp, vp, f32, vp, i32, i32, vp, i32, i32, i32, i32, f32,
+                                     i32, vp, i32, vp, vp, vp, sz, vp]
+    lib.mla_decode_fp8kv.restype = i32
+    lib.mla_decode_fp8kv_partials.argtypes = [vp, vp, f32, vp, i32, i32, vp, i32, i32, i32, i32,
+                                              f32, i32, i32, vp, sz, vp]
+    lib.mla_decode_fp8kv_partials.restype = i32
     i64 = ctypes.c_longlong
     lib.mla_decode_sparse.argtypes = [vp, vp, i64, vp, i32, vp, i32, i32, i32, f32, i32, vp, vp,
                                       vp, vp, sz, vp]
@@ -469,6 +476,54 @@ def mla_decode_partials(q, kv, *, scale, num_partitions, page_table=None, valid_
             wbytes, _stream(stream))
     return _finish(library().mla_decode_partials, args, "mla_decode_partials", workspace,
                    (q, kv, page_table, valid_length, workspace), prepare)
+
+
+def mla_decode_fp8kv(q, kv, *, k_scale, scale, page_table=None, valid_length=None,
+                     max_seq_len=None, num_partitions=0, sink_weights=None, causal=False,
+                     out=None, lse=None, workspace=None, stream=None, want_lse=True,
+                     prepare=False):
+    """MLA over an 8-bit e4m3 cache (uint8 / float8_e4m3fn [..., 1, 576]; real element =
+    k_scale x stored) with bf16 q.  Returns (out, lse), or with prepare=True a BoundCall."""
+    _need(q, "q", 4, (torch.bfloat16,))
+    _need(kv, "kv", 4, _FP8)
+    _need(valid_length, "valid_length", 1, _U32)
+    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    B, T, H, D = q.shape
+    if D != MLA_DEPTH or kv.shape[3] != MLA_DEPTH or kv.shape[2] != 1:
+        raise ValueError("MLA needs q [..., 576] and kv [..., 1, 576]")
+    page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len)
+    P = _resolve_partitions(num_partitions, B, T, H, 1, MLA_DEPTH, MLA_DEPTH_V, S,
+                            valid_length is not None)
+    if out is None:
+        out = torch.empty((B, T, H, MLA_DEPTH_V), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device)
+    args = (_ptr(q), _ptr(kv), float(k_scale), _ptr(page_table), page_size, max_pages,
+            _ptr(valid_length), B, T, H, S, float(scale), P, _ptr(sink_weights),
+            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(out), _ptr(lse), _ptr(workspace),
+            wbytes, _stream(stream))
+    return _finish(library().mla_decode_fp8kv, args, "mla_decode_fp8kv", (out, lse),
+                   (q, kv, page_table, valid_length, sink_weights, out, lse, workspace), prepare)
+
+
+def mla_decode_fp8kv_partials(q, kv, *, k_scale, scale, num_partitions, page_table=None,
+                              valid_length=None, max_seq_len=None, causal=False, workspace=None,
+                              stream=None, prepare=False):
+    """Partition pass of mla_decode_fp8kv() alone.  Returns the workspace, or with
+    prepare=True a BoundCall."""
+    _need(q, "q", 4, (torch.bfloat16,))
+    _need(kv, "kv", 4, _FP8)
+    _need(valid_length, "valid_length", 1, _U32)
+    B, T, H, D = q.shape
+    page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len)
+    P = int(num_partitions)
+    workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device, always=True)
+    args = (_ptr(q), _ptr(kv), float(k_scale), _ptr(page_table), page_size, max_pages,
+            _ptr(valid_length), B, T, H, S, float(scale), P,
+            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(workspace), wbytes, _stream(stream))
+    return _finish(library().mla_decode_fp8kv_partials, args, "mla_decode_fp8kv_partials",
+                   workspace, (q, kv, page_table, valid_length, workspace), prepare)
 
 
 def mla_sparse_num_partitions(batch, q_len, num_q_heads, topk, num_cus=0) -> int:

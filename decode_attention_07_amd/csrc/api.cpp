@@ -26,6 +26,7 @@ int stream_rows_per_block();
 hipError_t launch_decode_stream_fp8(const DecodeParams& p, hipStream_t s);
 int stream_fp8_step_keys();
 hipError_t launch_mla(const DecodeParams& p, hipStream_t s);
+hipError_t launch_mla_fp8(const DecodeParams& p, hipStream_t s);
 int mla_step_keys(int q_len);
 int mla_rows_per_block(int q_len, int num_q_heads);
 bool splitk_reduce_supported(int depth_v, int P);
@@ -74,7 +75,7 @@ int log2i(int x) {
 }
 
 // Which partition kernel runs, and its tiling.
-enum Variant { kValu = 0, kStream = 1, kMla = 2, kStreamFp8 = 3 };
+enum Variant { kValu = 0, kStream = 1, kMla = 2, kStreamFp8 = 3, kMlaFp8 = 4 };
 
 struct Plan {
   Variant variant;
@@ -216,6 +217,7 @@ hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16
     case kValu: return da::launch_decode_valu(p, s);
     case kStream: return da::launch_decode_stream(p, s);
     case kStreamFp8: return da::launch_decode_stream_fp8(p, s);
+    case kMlaFp8: return da::launch_mla_fp8(p, s);
     default: return da::launch_mla(p, s);
   }
 }
@@ -225,6 +227,7 @@ const char* variant_name(Variant v) {
     case kValu: return "valu";
     case kStream: return "stream";
     case kStreamFp8: return "stream_fp8";
+    case kMlaFp8: return "mla_fp8";
     default: return "mla";
   }
 }
@@ -333,6 +336,27 @@ int run_fp8kv(const Common& c, const void* q, const void* k, const void* v, floa
 int check_mla(const Common& c, const void* q, const void* kv) {
   if (!q || !kv) return DA_ERR_INVALID_ARG;
   return check_common(c);
+}
+
+// MLA over an 8-bit e4m3 cache: k_scale joins the softmax scale, and the value
+// slice (the same stored numbers) is scaled by it in the output.
+int check_mla_fp8(const Common& c, const void* q, const void* kv, float k_scale) {
+  int rc = check_mla(c, q, kv);
+  if (rc) return rc;
+  if (!std::isfinite(k_scale) || !std::isfinite(c.scale * k_scale)) return DA_ERR_INVALID_ARG;
+  return DA_OK;
+}
+
+int run_mla_fp8(const Common& c, const void* q, const void* kv, float k_scale,
+                int num_partitions, bool partials_only, const float* sink, void* out, float* lse,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  da::DecodeParams p = base_params(c, q, kv, kv, 1, c.num_q_heads, kMlaDepth, kMlaDepthV);
+  p.scale_log2 = c.scale * k_scale * 1.4426950408889634f;
+  p.v_scale = k_scale;
+  Plan pl = plan_mla(c.q_len, c.num_q_heads);
+  pl.variant = kMlaFp8;
+  return run(c, p, pl, true, num_partitions, partials_only, sink, out, lse, workspace,
+             workspace_bytes, stream);
 }
 
 // Sparse top-k MLA: the kernel addresses a row by a 32-bit byte offset from
@@ -589,6 +613,35 @@ int mla_decode_partials(const void* q, const void* kv, const uint32_t* page_tabl
       base_params(c, q, kv, kv, 1, num_q_heads, kMlaDepth, kMlaDepthV);
   return run(c, p, plan_mla(q_len, num_q_heads), true, num_partitions, true, nullptr, nullptr,
              nullptr, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_fp8kv(const void* q, const void* kv, float k_scale, const uint32_t* page_table,
+                     int page_size, int max_pages_per_seq, const uint32_t* valid_length,
+                     int batch, int q_len, int num_q_heads, int max_seq_len, float scale,
+                     int num_partitions, const float* sink_weights, int mask, void* out,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  const Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+                 q_len,      num_q_heads, max_seq_len, mask, scale};
+  int rc = check_mla_fp8(c, q, kv, k_scale);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  return run_mla_fp8(c, q, kv, k_scale, num_partitions, false, sink_weights, out, lse,
+                     workspace, workspace_bytes, stream);
+}
+
+int mla_decode_fp8kv_partials(const void* q, const void* kv, float k_scale,
+                              const uint32_t* page_table, int page_size, int max_pages_per_seq,
+                              const uint32_t* valid_length, int batch, int q_len,
+                              int num_q_heads, int max_seq_len, float scale, int num_partitions,
+                              int mask, void* workspace, size_t workspace_bytes, void* stream) {
+  const Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+                 q_len,      num_q_heads, max_seq_len, mask, scale};
+  int rc = check_mla_fp8(c, q, kv, k_scale);
+  if (rc) return rc;
+  if (num_partitions < 1 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  return run_mla_fp8(c, q, kv, k_scale, num_partitions, true, nullptr, nullptr, nullptr,
+                     workspace, workspace_bytes, stream);
 }
 
 int mla_sparse_num_partitions(int batch, int q_len, int num_q_heads, int topk, int num_cus) {

@@ -92,6 +92,20 @@ __device__ __forceinline__ bf16x8_t concat_bf16x8(uint2 lo, uint2 hi) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
+// Eight e4m3 bytes (two dwords) -> eight bf16 (exact: every finite e4m3 value is a
+// bf16 value; v_cvt_scalef32_pk_bf16_fp8 with scale 1).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  // whole 32-bit words only: element-wise access of the pairs is miscompiled
+  return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, a),
+                                                 __builtin_bit_cast(uint32_t, b),
+                                                 __builtin_bit_cast(uint32_t, c),
+                                                 __builtin_bit_cast(uint32_t, d)));
+}
+
 __device__ __forceinline__ int wave_id_uniform() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

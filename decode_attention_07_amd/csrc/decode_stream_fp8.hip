@@ -76,19 +76,6 @@ __device__ __forceinline__ constexpr int pv_key(int G, int b) {
   return b < 4 ? 4 * G + b : 16 + 4 * G + (b - 4);
 }
 
-// Eight e4m3 bytes (two dwords) -> eight bf16 (exact).
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-  // whole 32-bit words only: element-wise access of the pairs is miscompiled
-  return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint32_t, a),
-                                                 __builtin_bit_cast(uint32_t, b),
-                                                 __builtin_bit_cast(uint32_t, c),
-                                                 __builtin_bit_cast(uint32_t, d)));
-}
-
 __device__ __forceinline__ uint2 lds_read_tr8(const void* p) {
   typedef int v2i __attribute__((ext_vector_type(2)));
   const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(

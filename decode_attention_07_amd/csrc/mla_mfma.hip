@@ -100,21 +100,28 @@ __device__ __forceinline__ void dma_table_init(uint32_t* tab, int wave, int lane
   }
 }
 
+// First cache row of the tile at key j0 (a tile never straddles a page).  The
+// page-table entry is read through the scalar cache (uniform index, table constant
+// during the call); its address is pinned to scalar registers first, or the
+// compiler, keeping it in vector registers under register pressure, would make the
+// read a vector load, whose wait would also wait for every tile load in flight.
+__device__ __forceinline__ size_t mla_row0(const DecodeParams& p, int b, int j0) {
+  if (p.page_table) {
+    const uint64_t a = pin_uniform_u64(
+        (uint64_t)(p.page_table + (size_t)b * p.max_pages + (size_t)(j0 >> p.page_shift)));
+    const uint32_t phys = *(const __attribute__((address_space(4))) uint32_t*)a;
+    return ((size_t)phys << p.page_shift) + (size_t)(j0 & ((1 << p.page_shift) - 1));
+  }
+  return (size_t)b * p.max_seq_len + j0;
+}
+
 // Requests the 32-key tile starting at key j0 into one LDS stage.  Keys at or
 // past `kend` fetch the same chunk of the tile's first key instead (finite data;
 // those keys are masked out of the softmax), so every wave issues exactly
 // kDmaPerWave instructions.
 __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage, int b, int j0,
                                           int kend, int wave, const uint32_t* tab) {
-  size_t row0;
-  if (p.page_table) {  // uniform index, table constant during the call: scalar cache
-    const __attribute__((address_space(4))) uint32_t* pt =
-        (const __attribute__((address_space(4))) uint32_t*)p.page_table;
-    const uint32_t phys = pt[(size_t)b * p.max_pages + (j0 >> p.page_shift)];
-    row0 = ((size_t)phys << p.page_shift) + (size_t)(j0 & ((1 << p.page_shift) - 1));
-  } else {
-    row0 = (size_t)b * p.max_seq_len + j0;
-  }
+  const size_t row0 = mla_row0(p, b, j0);
   // Uniform by construction; pinned to scalar registers (the loads take a
   // scalar base) even where it reaches here through a phi after a divergent branch.
   const size_t off0 = row0 * kRowBytes;
@@ -219,6 +226,84 @@ __device__ __forceinline__ void mla_issue_sparse(const DecodeParams& p, uint32_t
   }
 }
 
+// 8-bit e4m3 cache with bf16 q ("flare_mla_decoding_dispatch", Parameters
+// `dtype`, Args `output`): a cache row is 576 bytes.  A tile's rows reach LDS in
+// a 2-slot staging ring of 18 KB, each wave loading its own 8 keys (18 loads of
+// 256 bytes); after its P.V each wave converts those same bytes into the bf16
+// stage layout above (a 3-slot ring here), so the scores, the softmax and P.V
+// run unchanged.  A wave converts only what it loaded itself, so its own vmcnt
+// wait orders the conversion after the loads, and the tile's barrier makes the
+// converted stage visible to the other waves.
+constexpr int kF8Row = kD;                           // bytes per cache row
+constexpr int kF8Tile = kF8Row * kBN;                // 18 KB
+constexpr int kF8WaveBytes = kF8Tile / kWaves;       // keys 8w .. 8w + 7 of a tile
+constexpr int kF8DmaPerWave = kF8WaveBytes / 256;    // 18
+constexpr int kF8Pieces = kF8WaveBytes / (64 * 8);   // 9 eight-byte pieces per lane
+constexpr int kBStagesF8 = 3;
+constexpr int kF8Ring0 = kBStagesF8 * kTileBytes;    // the staging ring follows the bf16 stages
+static_assert(kF8Ring0 + 2 * kF8Tile <= kStages * kTileBytes, "8-bit rings fit the stage array");
+static_assert(kF8Pieces <= kTabPerLane, "conversion table fits");
+
+// 4 bytes per lane from base + voff into LDS at lds_base + 4 * lane, non-temporal.
+// (No immediate offset: on these loads it would move the LDS destination too.)
+__device__ __forceinline__ void dma4_nt(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dword %0, %1 nt" : : "v"(voff), "s"(base), "{m0}"(lds_base)
+               : "memory");
+}
+
+// bf16-stage byte offset of the 8 elements that 8-byte piece j (byte 512 j + 8 lane
+// of the wave's 8 keys) converts to: chunk c of key k at position c ^ swz(k).
+__device__ __forceinline__ void f8_table_init(uint32_t* tab, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < kF8Pieces; ++j) {
+    const int o = 512 * j + 8 * lane;
+    const int key = 8 * wave + o / kF8Row;
+    const int c = (o % kF8Row) / 8;
+    tab[j] = (uint32_t)(key * kRowBytes + 16 * ((c & ~7) | ((c & 7) ^ swz(key))));
+  }
+}
+
+// Requests this wave's 8 keys of the 32-key tile at j0 into a staging slot.  Keys
+// at or past kend load the tile's first key instead (finite data, masked out of
+// the softmax), so every wave issues exactly kF8DmaPerWave loads.
+__device__ __forceinline__ void mla_issue_fp8(const DecodeParams& p, uint32_t fstage, int b,
+                                              int j0, int kend, int wave, int lane) {
+  const char* base = (const char*)p.k + pin_uniform_u64(mla_row0(p, b, j0) * kF8Row);
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(fstage + wave * kF8WaveBytes);
+  const uint32_t o0 = (uint32_t)(kF8WaveBytes * wave) + 4u * (uint32_t)lane;
+  const int nvalid = kend - j0;
+  if (nvalid >= kBN) {  // whole tile (uniform branch): one offset register, the base moves
+#pragma unroll
+    for (int i = 0; i < kF8DmaPerWave; ++i) dma4_nt(base + 256 * i, o0, dst + 256u * i);
+  } else {
+    // The lane's offsets are recomputed here from an opaque copy of o0, so that
+    // the compiler does not keep all 18 (and their keys) live across the loop.
+    uint32_t oq;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(oq) : "v"(o0));
+#pragma unroll
+    for (int i = 0; i < kF8DmaPerWave; ++i) {
+      uint32_t o = oq + 256u * i;
+      const uint32_t key = o / (uint32_t)kF8Row;
+      if ((int)key >= nvalid) o -= key * (uint32_t)kF8Row;
+      dma4_nt(base, o, dst + 256u * i);
+    }
+  }
+}
+
+// This wave's 8 keys of a staged 8-bit tile -> the bf16 stage (exact conversion).
+__device__ __forceinline__ void mla_convert_fp8(const char* fst, char* bst, int wave, int lane,
+                                                const uint32_t* tab) {
+  const char* src = fst + kF8WaveBytes * wave + 8 * lane;
+  const uint4 t0 = *(const uint4*)tab;
+  const uint4 t1 = *(const uint4*)(tab + 4);
+  const uint32_t e[kF8Pieces] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w, tab[8]};
+#pragma unroll
+  for (int j = 0; j < kF8Pieces; ++j) {
+    const uint2 w = *(const uint2*)(src + 512 * j);
+    *(bf16x8_t*)(bst + e[j]) = fp8x8_to_bf16(w.x, w.y);
+  }
+}
+
 // The MFMAs are written as inline asm so that the register classes are fixed:
 // the O^T accumulator in the 256 accumulation registers, Q^T and the score
 // tiles in arch VGPRs (left to itself the compiler puts the score accumulators
@@ -275,13 +360,13 @@ __device__ __forceinline__ constexpr int c32_row(int j, int g) {
 // (the swizzle only touches bits 4..6 of the offset).  Two accumulation chains
 // (even / odd st); the K fragments come from a ring kPf pairs deep so that their
 // LDS latency hides behind the MFMAs in flight.
+template <int kPf>
 __device__ __forceinline__ void mla_scores(const char* buf, const bf16x8_t (&qf)[kKS],
                                            uint32_t kofs, f32x16_t& s0, f32x16_t& s1) {
   auto kfrag = [&](int st) {
     return *(const bf16x8_t*)(buf + ((kofs ^ (32u * (st % 4))) + 128u * (st / 4)));
   };
   constexpr int kPairs = kKS / 2;
-  constexpr int kPf = 4;
   bf16x8_t ra[kPf], rb[kPf];
 #pragma unroll
   for (int q = 0; q < kPf; ++q) {
@@ -445,12 +530,15 @@ struct BoolTag {
 };
 
 // SPARSE: keys from a top-k list of pool rows (p.indices) instead of the
-// contiguous or paged cache.
-template <bool SPARSE>
+// contiguous or paged cache.  FP8: the cache holds e4m3 elements (real value =
+// k_scale x stored; k_scale is folded into scale_log2, and v_scale, the same
+// factor for the value slice, multiplies the output).
+template <bool SPARSE, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
+  static_assert(!(SPARSE && FP8), "no sparse 8-bit form");
   // loads per wave per tile request
-  constexpr int kIssue = kDmaPerWave + (SPARSE ? 1 : 0);
+  constexpr int kIssue = FP8 ? kF8DmaPerWave : kDmaPerWave + (SPARSE ? 1 : 0);
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
   // XCD-aware decode of the block id: blocks i and i + 8 share an XCD; the
   // n_mblocks row blocks of one (partition, sequence) get ids 8 apart.
@@ -523,14 +611,32 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   const uint32_t* tab = dma_tab + threadIdx.x * kTabPerLane;  // this lane's own entries
   if constexpr (SPARSE)
     dma_table_init_sparse(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
+  else if constexpr (FP8)
+    f8_table_init(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
   else
     dma_table_init(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
+  // bf16 stage of tile t: a 4-slot ring, or 3 slots when the 8-bit staging ring
+  // takes the rest of the array.
+  // (The 3-slot index passes through an empty asm: left visible, the compiler
+  // keeps per-slot copies of the operand offsets live and spills the Q operand.)
+  auto bstage = [&](int t) __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      int st = __builtin_amdgcn_readfirstlane(t % kBStagesF8);
+      asm volatile("" : "+s"(st));
+      return st;
+    } else {
+      return t & (kStages - 1);
+    }
+  };
   // Sparse lists: row indices of tiles t, t + 1 sit in slots t % 4, (t + 1) % 4
   // when tile t is requested.
   __shared__ __attribute__((aligned(16))) int32_t sp_slots[kSpSlots * kWaves * 8];
   auto issue = [&](int t) __attribute__((always_inline)) {
     const uint32_t stage = lds0 + (uint32_t)((t & (kStages - 1)) * kTileBytes);
-    if constexpr (SPARSE)
+    if constexpr (FP8)
+      mla_issue_fp8(p, lds0 + (uint32_t)(kF8Ring0 + (t & 1) * kF8Tile), b, k_lo + t * kBN,
+                    hmax, wave, lane);
+    else if constexpr (SPARSE)
       mla_issue_sparse(p, stage, b, t, k_lo, hmax, wave, lane, tab, sp_slots,
                        (uint32_t)(uintptr_t)sp_slots);
     else
@@ -546,13 +652,35 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       wait_vm_lgkm0<0>();
     }
   };
+  // 8-bit cache: this wave's keys of staged tile t -> bf16 stage of tile t.
+  auto convert = [&](int t) __attribute__((always_inline)) {
+    if constexpr (FP8)
+      mla_convert_fp8(smem + kF8Ring0 + (t & 1) * kF8Tile, smem + bstage(t) * kTileBytes, wave,
+                      lane, tab);
+  };
+  // Start of a pass: tile 0 requested (8-bit: tiles 0 and 1 requested and tile 0
+  // converted once landed).
+  auto start_pass = [&]() __attribute__((always_inline)) {
+    if constexpr (FP8) {
+      issue(0);
+      if (n_tot > 1) {
+        issue(1);
+        wait_vm_lgkm0<kIssue>();
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+      convert(0);
+    } else {
+      prime();
+      issue(0);
+    }
+  };
   if (n_tot > 0) {
     // Tile 0 is requested while the Q loads are in flight; both are waited for
     // before anything else is issued, so that only tile requests are counted
     // below.
-    prime();
-    issue(0);
-    wait_vm_lgkm0<0>();
+    start_pass();
+    if constexpr (!FP8) wait_vm_lgkm0<0>();
     // Rows outside the fold get Q = 0; a negative scale flips Q's sign (exact).
     const uint32_t qx = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
@@ -564,12 +692,15 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     const float sl = fabsf(p.scale_log2);
     bf16x8_t pb_prev[2];
     for (;;) {  // one pass over the partition; repeated only after a restart
-      // tile 0 is requested on entry; tile 1 now; wait for tile 0
-      if (n_tot > 1) {
-        issue(1);
-        wait_vm_lgkm0<kIssue>();
-      } else {
-        wait_vm_lgkm0<0>();
+      // tile 0 is requested on entry; tile 1 now; wait for tile 0 (8-bit: done
+      // by start_pass)
+      if constexpr (!FP8) {
+        if (n_tot > 1) {
+          issue(1);
+          wait_vm_lgkm0<kIssue>();
+        } else {
+          wait_vm_lgkm0<0>();
+        }
       }
       __syncthreads();
       // One tile: returns true when the votes of the tile before it ask for a
@@ -587,21 +718,28 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         const bool ahead = i + 2 < n_tot;
         if (ahead) issue(i + 2);  // into the stage of tile i - 2, last read a barrier ago
         f32x16_t s0, s1;
-        mla_scores(smem + (i & (kStages - 1)) * kTileBytes, qf, kofs, s0, s1);
+        // K fragments ring: 4 pairs deep, 3 in the 8-bit form (its staging needs
+        // registers of its own)
+        mla_scores<FP8 ? 3 : 4>(smem + bstage(i) * kTileBytes, qf, kofs, s0, s1);
         bool need = false;
         bf16x8_t pb[2];
         MlaPV pv;
-        if (PV) pv.start(smem + ((i - 1) & (kStages - 1)) * kTileBytes, vofs0, vofs1);
+        if (PV) pv.start(smem + bstage(i - 1) * kTileBytes, vofs0, vofs1);
         mla_softmax_pv<PV, MASKED>(s0, s1, pv, pb_prev, pb, acc, m, lsum, lsr, k_lo + i * kBN,
                                    hi, sl, need);
         pb_prev[0] = pb[0];
         pb_prev[1] = pb[1];
         if (lane == 0) votes[i & 1][wave] = __builtin_amdgcn_ballot_w64(need) != 0;
-        // tile i + 1 must have landed: tile i + 2 may stay in flight
+        // tile i + 1 must have landed: tile i + 2 may stay in flight (8-bit: this
+        // wave's part of staged tile i + 1, converted into the bf16 stage tile i - 2
+        // left, last read a barrier ago)
         if (ahead)
           wait_vm_lgkm0<kIssue>();
         else
           wait_vm_lgkm0<0>();
+        if constexpr (FP8) {
+          if (i + 1 < n_tot) convert(i + 1);
+        }
         __syncthreads();
         return (prev.x | prev.y | prev.z | prev.w) != 0;  // same votes in every wave
       };
@@ -614,7 +752,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         if (!(last.x | last.y | last.z | last.w)) {
           // the last tile's P.V (its stage is no longer written)
           MlaPV pv;
-          pv.start(smem + ((n_tot - 1) & (kStages - 1)) * kTileBytes, vofs0, vofs1);
+          pv.start(smem + bstage(n_tot - 1) * kTileBytes, vofs0, vofs1);
           pv.step<true>(0, acc, pb_prev);
           pv.step<true>(1, acc, pb_prev);
 #pragma unroll
@@ -629,8 +767,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       lsum = 0.f;
       lsr = 0.f;
       __syncthreads();  // every wave has read the votes before the next pass writes them
-      prime();
-      issue(0);  // tile 0 of the next pass
+      start_pass();  // tile 0 of the next pass
     }
   }
 
@@ -643,7 +780,8 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   if (p.write_partials) {
     const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
     const bool any = lsum > 0.f;
-    const float inv = any ? 1.f / lsr : 0.f;
+    float inv = any ? 1.f / lsr : 0.f;
+    if constexpr (FP8) inv *= p.v_scale;
     float* dst = p.part_o + prow * kDv;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
@@ -668,7 +806,8 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       M = M2;
     }
     const bool any = L > 0.f;
-    const float inv = any ? c / Lr : 0.f;
+    float inv = any ? c / Lr : 0.f;
+    if constexpr (FP8) inv *= p.v_scale;
     uint16_t* dst = (uint16_t*)p.out + row * kDv;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
@@ -691,11 +830,20 @@ hipError_t launch_mla(const DecodeParams& p, hipStream_t s) {
   const int n_work = p.num_partitions * p.batch;
   const int grid = ((n_work + 7) / 8) * 8 * n_mblocks;
   if (p.indices)
-    hipLaunchKernelGGL(mla_decode_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p, n_mblocks,
-                       n_work);
+    hipLaunchKernelGGL((mla_decode_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, p,
+                       n_mblocks, n_work);
   else
-    hipLaunchKernelGGL(mla_decode_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p, n_mblocks,
-                       n_work);
+    hipLaunchKernelGGL((mla_decode_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, p,
+                       n_mblocks, n_work);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_fp8(const DecodeParams& p, hipStream_t s) {
+  const int n_mblocks = p.row_blocks;
+  const int n_work = p.num_partitions * p.batch;
+  const int grid = ((n_work + 7) / 8) * 8 * n_mblocks;
+  hipLaunchKernelGGL((mla_decode_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, p,
+                     n_mblocks, n_work);
   return hipGetLastError();
 }
 

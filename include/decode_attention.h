@@ -255,6 +255,31 @@ int mla_decode_partials(const void* q, const void* kv, const uint32_t* page_tabl
                         void* stream);
 
 /*
+ * MLA over an 8-bit cache ("flare_mla_decoding_dispatch", Parameters `dtype`: q
+ * of a half type or float8_e4m3fn; Args `output`: a bfloat16 output when the
+ * inputs are 8-bit).  Reading of the pages: bf16 q over an e4m3 cache (OCP FP8
+ * E4M3, the elements of float8_e4m3fn) with one fp32 scale for the tensor: the
+ * real cache element is k_scale x stored, for the keys and for their value
+ * slice alike (V is the first 512 columns of the same stored rows).
+ *   kv  uint8 e4m3 bit patterns, dense [batch, max_seq_len, 1, 576] or pool
+ *       [num_pages, page_size, 1, 576]
+ *   q, out, lse and every other argument as for mla_decode().
+ * k_scale and scale * k_scale must be finite (else DA_ERR_INVALID_ARG).
+ */
+int mla_decode_fp8kv(const void* q, const void* kv, float k_scale, const uint32_t* page_table,
+                     int page_size, int max_pages_per_seq, const uint32_t* valid_length,
+                     int batch, int q_len, int num_q_heads, int max_seq_len, float scale,
+                     int num_partitions, const float* sink_weights, int mask, void* out,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The partition pass of mla_decode_fp8kv() alone (see decode_attention_partials()). */
+int mla_decode_fp8kv_partials(const void* q, const void* kv, float k_scale,
+                              const uint32_t* page_table, int page_size, int max_pages_per_seq,
+                              const uint32_t* valid_length, int batch, int q_len,
+                              int num_q_heads, int max_seq_len, float scale, int num_partitions,
+                              int mask, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Sparse top-k MLA ("flare_mla_decoding_dispatch", Parameters `sparse`; Args
  * `d_indices`, `indices_stride`, `topk_lengths`): the keys of sequence b are
  * not a prefix of its cache but a list of rows of a shared pool, a gather at

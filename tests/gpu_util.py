@@ -39,6 +39,8 @@ def run_gpu(wl: W.Workload, dev: dict, num_partitions=None, **kw):
                   valid_length=dev["valid_length"], max_seq_len=wl.max_seq_len,
                   num_partitions=P, sink_weights=dev["sink"], causal=wl.causal)
     common.update(kw)
+    if wl.mla and wl.kv_type == "e4m3":
+        return DA.mla_decode_fp8kv(dev["q"], dev["k"], k_scale=wl.k_scale, **common)
     if wl.mla:
         return DA.mla_decode(dev["q"], dev["k"], **common)
     if wl.kv_type == "e4m3":

@@ -20,7 +20,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     lib = ctypes.CDLL(DA.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
@@ -255,3 +255,28 @@ def test_sparse_partials_and_heuristic_checks():
     assert DA.mla_sparse_num_partitions(1, 1, 128, 2048, num_cus=256) == 4
     assert DA.mla_sparse_num_partitions(8, 1, 128, 100, num_cus=256) == 1
     assert lib.mla_sparse_num_partitions(0, 1, 128, 2048, 256) == DA.DA_ERR_INVALID_ARG
+
+
+def test_mla_fp8kv_argument_checks():
+    lib = DA.library()
+    # mla_decode_fp8kv(q, kv, k_scale, table, ps, max_pages, valid, B, T, H, S, scale, P, sink,
+    #                  mask, out, lse, ws, wbytes, stream)
+    ok = [1, 1, 0.125, None, 0, 0, None, 1, 1, 128, 64, 0.1, 1, None, 0, 1, None, None, 0, None]
+    for i, v, code in [(0, None, DA.DA_ERR_INVALID_ARG), (1, None, DA.DA_ERR_INVALID_ARG),
+                       (2, float("nan"), DA.DA_ERR_INVALID_ARG),
+                       (2, 1e30, DA.DA_ERR_INVALID_ARG),        # scale x k_scale overflows
+                       (11, float("inf"), DA.DA_ERR_INVALID_ARG), (14, 5, DA.DA_ERR_INVALID_ARG),
+                       (15, None, DA.DA_ERR_INVALID_ARG), (12, 3, DA.DA_ERR_WORKSPACE)]:
+        a = list(ok)
+        a[i] = v
+        if i == 2 and v == 1e30:
+            a[11] = 1e10
+        assert lib.mla_decode_fp8kv(*a) == code, (i, v)
+    a = list(ok)
+    a[7] = 0
+    assert lib.mla_decode_fp8kv(*a) == DA.DA_OK   # empty batch: nothing launched
+    # partials: P must be >= 1 and the workspace given
+    assert lib.mla_decode_fp8kv_partials(1, 1, 0.125, None, 0, 0, None, 1, 1, 128, 64, 0.1, 0,
+                                         0, None, 0, None) == DA.DA_ERR_INVALID_ARG
+    assert lib.mla_decode_fp8kv_partials(1, 1, 0.125, None, 0, 0, None, 1, 1, 128, 64, 0.1, 2,
+                                         0, None, 0, None) == DA.DA_ERR_WORKSPACE

@@ -162,6 +162,11 @@ PAGED_FP8 = PAGED.with_(name="paged_ragged_fp8_b64_h64_kv8_d128_s32768_p128", kv
 GQA_RAGGED_Q = GQA.with_(name="gqa_ragged_q_b32_h32_kv8_d128_s4096_t1to4", q_len=4, causal=True,
                          extra={"q_tokens": (1, 4)})
 
+# The MLA problem over an 8-bit e4m3 cache (bf16 q; one scale for the stored rows,
+# whose first 512 columns are V: stored e4m3(8 N(0,1)), k_scale = 1/8).
+MLA_FP8 = MLA.with_(name="mla_fp8_b64_h128_d576_dv512_s8192", kv_dtype="e4m3", k_scale=0.125,
+                    v_scale=0.125)
+
 # Sparse top-k MLA (a DeepSeek-style selection of 2048 of each sequence's 8192 cached
 # rows): the same 64 sequences and heads as the MLA problem, each attending to its
 # own list of 2048 pool rows.
@@ -169,7 +174,7 @@ MLA_SPARSE = MLA.with_(name="mla_sparse_bf16_b64_h128_d576_dv512_topk2048_s8192"
                        topk=2048)
 
 ALL = {w.name: w for w in (TINY_MHA, GQA, PAGED, MLA, MLA_MTP, LONG, GQA_FP8, PAGED_FP8,
-                           GQA_RAGGED_Q, MLA_SPARSE)}
+                           GQA_RAGGED_Q, MLA_SPARSE, MLA_FP8)}
 
 
 def ragged_q_tokens(wl: Workload):

@@ -575,6 +575,27 @@ def pin_sdpa_e4m3_scaled_kv(lib):
     _close(lse, rl, what="lse")
 
 
+def pin_sdpa_e4m3_mla_value_slice(lib):
+    """MLA over an e4m3 cache: V is the first Dv columns of the same stored rows, so
+    it is dequantised with k_scale (a v_scale passed alongside plays no part), causal
+    MTP rows: fp64 SDPA on the rows dequantised by torch."""
+    rng = _rng(45)
+    B, T, H, D, Dv, S = 2, 2, 4, 24, 16, 21
+    q = _randn(rng, (B, T, H, D), "bf16")
+    codes = np.concatenate([np.arange(0, 0x7f), np.arange(0x80, 0xff)]).astype(np.uint8)
+    kv = rng.choice(codes, size=(B, S, 1, D))
+    lens = np.array([21, 6], np.uint32)
+    k_scale = 0.09375
+    scale = float(np.float32(0.3))
+    out, lse = O.attention(q, kv, None, depth_v=Dv, scale=scale, valid_length=lens,
+                           causal=True, k_scale=k_scale, v_scale=7.0, lib=lib)
+    kd = _expand_heads(k_scale * _e4m3_torch(kv), H)
+    allowed = np.broadcast_to(_visible(lens, T, S, True)[:, None], (B, H, T, S)).copy()
+    ro, rl = _sdpa(q, kd, kd[..., :Dv].copy(), scale, allowed=allowed)
+    _close(out, ro, what="out")
+    _close(lse, rl, what="lse")
+
+
 # --------------------------------------------------------------------------
 # Sparse top-k: each sequence's keys are listed pool rows
 # --------------------------------------------------------------------------

@@ -46,6 +46,9 @@ MUTANTS = [
     ("e4m3_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
     ("k_scale_dropped", "return p->k_scale * elem(p->k, kv_index(p, b, j, g, d, p->D), p->kv_dtype);\n}",
      "return elem(p->k, kv_index(p, b, j, g, d, p->D), p->kv_dtype);\n}"),
+    ("mla_value_slice_uses_v_scale",
+     "if (p->v == NULL) return p->k_scale * elem(p->k, kv_index(p, b, j, g, d, p->D), p->kv_dtype);",
+     "if (p->v == NULL) return p->v_scale * elem(p->k, kv_index(p, b, j, g, d, p->D), p->kv_dtype);"),
     ("v_scale_is_k_scale", "return p->v_scale * elem(p->v,", "return p->k_scale * elem(p->v,"),
     ("v_scale_dropped", "return p->v_scale * elem(p->v,", "return elem(p->v,"),
     ("cache_layout_head_major", "return (row * p->KVH + (size_t)g) * (size_t)width + (size_t)d;",

@@ -8,7 +8,7 @@
 // keys, so every cache row of the partition is read from HBM once per 128 rows.
 //
 // Per 32-key tile, shared by the block through a 4-stage LDS ring filled by
-// direct global->LDS loads (no staging registers; three tiles in flight):
+// direct global->LDS loads (no staging registers; tiles requested two ahead):
 //   S^T[32 keys x 32 rows] = K[32 x 576] . Q^T[576 x 32]    36 v_mfma_f32_32x32x16_bf16
 //       A = K from LDS, B = the wave's Q^T kept in registers for the whole
 //       kernel (144 VGPRs).
@@ -36,6 +36,10 @@
 // With two tokens (256 rows) a sequence needs two blocks that read the same
 // tiles; their block ids differ by a multiple of 8 so that both land on the same
 // XCD and the second read of each tile is served by that XCD's L2.
+// Two more forms of the same kernel change only how a tile reaches its stage:
+// the sparse form gathers the tile's 32 keys from a list of pool rows (its row
+// indices reach LDS two tiles ahead), and the 8-bit form stages e4m3 rows in a
+// ring of its own and converts them into the bf16 stage layout.
 #include "da_device.h"
 
 namespace da {

@@ -378,7 +378,8 @@ int sparse_partitions(int batch, int q_len, int num_q_heads, int topk, int num_c
 int check_sparse(const void* q, const void* kv, long long pool_rows, const int32_t* indices,
                  int indices_stride, const int32_t* topk_lengths, int batch, int q_len,
                  int num_q_heads, float scale) {
-  if (!q || !kv || !indices || !topk_lengths) return DA_ERR_INVALID_ARG;
+  if (!q || !kv || !topk_lengths) return DA_ERR_INVALID_ARG;
+  if (!indices && indices_stride > 0) return DA_ERR_INVALID_ARG;  // stride 0: nothing is read
   if (batch < 0 || q_len < 1 || num_q_heads < 1 || indices_stride < 0 || pool_rows < 1)
     return DA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return DA_ERR_INVALID_ARG;

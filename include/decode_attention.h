@@ -295,7 +295,8 @@ int mla_decode_fp8kv_partials(const void* q, const void* kv, float k_scale,
  *   pool_rows     1 .. 3728270 (the pool is at most 4 GiB: rows are addressed
  *                 by 32-bit byte offsets); larger pools are DA_ERR_UNSUPPORTED
  *   indices       int32 [batch, indices_stride]; entries at or past a
- *                 sequence's count are never read
+ *                 sequence's count are never read (NULL allowed when
+ *                 indices_stride is 0)
  *   topk_lengths  int32 [batch]; a count below 0 is 0, above indices_stride is
  *                 indices_stride
  *   out           bf16 [batch, q_len, num_q_heads, 512]; lse fp32 [batch, q_len,

@@ -225,6 +225,7 @@ def _call_sparse(**over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(indices=None), DA.DA_ERR_INVALID_ARG),
+    (dict(indices=None, stride=0, batch=0), DA.DA_OK),   # nothing listed: no list needed
     (dict(topk=None), DA.DA_ERR_INVALID_ARG),
     (dict(kv=None), DA.DA_ERR_INVALID_ARG),
     (dict(out=None), DA.DA_ERR_INVALID_ARG),

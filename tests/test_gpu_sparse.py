@@ -191,3 +191,22 @@ def test_sparse_rejects_bad_shapes():
                                         tl.data_ptr(), 1, 1, 128, 0.1, 1, None, q.data_ptr(),
                                         None, None, 0, None)
     assert rc == DA.DA_ERR_UNSUPPORTED
+
+
+def test_sparse_zero_stride_and_zero_counts():
+    """A list stride of 0 (nothing listed anywhere) and all-zero counts: every row is
+    empty -- out = 0 and lse = -inf, or the sink alone (lse = sigma_h)."""
+    rng = np.random.default_rng(9995)
+    B, H, R = 3, 128, 40
+    q = W.f32_to_bf16_bits(rng.standard_normal((B, 2, H, 576)).astype(np.float32))
+    pool = W.f32_to_bf16_bits(rng.standard_normal((R, 1, 576)).astype(np.float32))
+    sink = rng.standard_normal(H).astype(np.float32)
+    wl = _wl("empty", 0, B, 2, H, 0, 0)
+    for stride in (0, 40):
+        idx = rng.integers(0, R, size=(B, stride)).astype(np.int32)
+        counts = np.zeros(B, np.int32)
+        for s, P in ((None, 1), (sink, 1), (sink, 3)):
+            ref = O.attention(q, pool, None, depth_v=512, scale=SCALE, sink=s, indices=idx,
+                              topk_lengths=counts)
+            out, lse = _explicit(q, pool, idx, counts, s, P)
+            compare(wl, out, lse, *ref, what=f"empty lists stride={stride} sink={s is not None}")

@@ -18,7 +18,9 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 instructions stay off (some of their forms are not trusted)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
+         "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
+         # only the C ABI of include/decode_attention.h is exported
+         "-fvisibility=hidden"]
 # Per-source additions.  The streaming kernels rescale their MFMA accumulators
 # with vector ops: the VGPR form of the MFMAs keeps them out of the
 # accumulation registers and saves a copy in each direction per tile.

@@ -13,7 +13,11 @@
 #include <cstdlib>
 #include <mutex>
 
+// The library is built with hidden visibility: the declarations of the C ABI are
+// the only exported symbols.
+#pragma GCC visibility push(default)
 #include "../../include/decode_attention.h"
+#pragma GCC visibility pop
 #include "da_params.h"
 
 namespace da {

@@ -27,6 +27,21 @@ def test_every_declared_function_is_exported():
     assert sorted(DA.EXPORTS) == names
 
 
+def test_only_declared_functions_are_exported():
+    """The library is built with hidden visibility: its exported functions are exactly
+    the header's declarations (no internal C++ symbol leaks into the ABI)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", DA.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines()
+                      if len(line.split()) == 3 and line.split()[1] == "T")
+    assert exported == header_functions()
+
+
 def test_status_strings():
     for code in (0, -1, -2, -3, -4):
         assert DA.status_string(code) not in ("", "unknown status")

@@ -294,7 +294,8 @@ int mla_decode_fp8kv_partials(const void* q, const void* kv, float k_scale,
  *   kv            bf16 pool [pool_rows, 1, 576]; V = the first 512 columns
  *   pool_rows     1 .. 3728270 (the pool is at most 4 GiB: rows are addressed
  *                 by 32-bit byte offsets); larger pools are DA_ERR_UNSUPPORTED
- *   indices       int32 [batch, indices_stride]; entries at or past a
+ *   indices       int32 [batch, indices_stride], indices_stride 0 .. 2^28
+ *                 (larger is DA_ERR_UNSUPPORTED); entries at or past a
  *                 sequence's count are never read (NULL allowed when
  *                 indices_stride is 0)
  *   topk_lengths  int32 [batch]; a count below 0 is 0, above indices_stride is

@@ -251,6 +251,7 @@ def _call_sparse(**over):
     (dict(num_partitions=-1), DA.DA_ERR_INVALID_ARG),
     # rows are addressed by 32-bit byte offsets: at most 2^32 / 1152 of them
     (dict(pool_rows=(1 << 32) // 1152 + 1), DA.DA_ERR_UNSUPPORTED),
+    (dict(stride=(1 << 28) + 1), DA.DA_ERR_UNSUPPORTED),
     (dict(num_partitions=3), DA.DA_ERR_WORKSPACE),
     (dict(batch=0), DA.DA_OK),
     (dict(batch=0, num_partitions=0), DA.DA_OK),

@@ -5,11 +5,13 @@
 // L = sum_p w_p + exp(sigma - M), out = sum_p w_p * O_p / L, lse = M + ln L
 // ("mha_decoding_single_batch_pipelined", description: the mha_splitk_reduce
 // pass).  One wave per row: lanes take the partitions' (m_p, l_p) 64 at a time,
-// so the row max and the weights need one load round trip and two wave
-// reductions; the weights are then broadcast one partition at a time through
-// scalar lane reads while every lane accumulates its DV/64 consecutive columns
-// of O_p (one coalesced row read per partition, up to 32 partitions in flight).
-// Empty partitions (weight 0) are skipped without loading their row.
+// so the row max and the weights need wave reductions only; the weights are then
+// broadcast one partition at a time through scalar lane reads while every lane
+// accumulates its DV/64 consecutive columns of O_p (one coalesced row read per
+// partition, up to 32 partitions in flight).  With at most 64 partitions the
+// partial rows are requested together with (m_p, l_p), since their addresses do
+// not depend on the weights: one memory round trip per row.  An empty
+// partition's value (weight 0) is dropped by a select, whatever its row holds.
 #pragma once
 
 #include "da_device.h"
@@ -54,6 +56,19 @@ __device__ __forceinline__ MergeCols<EPL> merge_load_cols(const float* p) {
   return c;
 }
 
+// acc += w_u * O_u over a group of partial rows; a zero weight drops its row.
+template <int EPL, int N>
+__device__ __forceinline__ void merge_accumulate(float (&acc)[EPL], const float (&wj)[N],
+                                                 const MergeCols<EPL> (&c)[N]) {
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float t = fmaf(wj[u], c[u].v[e], acc[e]);
+      acc[e] = (wj[u] != 0.f) ? t : acc[e];
+    }
+}
+
 // Merges row `row` (of `rows` per partition) of part_o [P, rows, DV],
 // part_m / part_l [P, rows]; writes out[row, :] (bf16 or fp32) and lse[row]
 // (if lse).  Called by all 64 lanes of one wave; sink (or nullptr) is indexed by
@@ -69,62 +84,83 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
   // Partial rows requested ahead: 64 values per lane in flight (8 rows at
   // DV = 512, 32 at DV <= 128, where a long split of few rows is latency bound).
   constexpr int kInFlight = (64 / EPL) < 32 ? (64 / EPL) : 32;
-  float mx = kNegInf;
-  for (int pp = lane; pp < P; pp += 64) {
-    const float lp = part_l[(size_t)pp * rows + row];
-    if (lp > 0.f) mx = fmaxf(mx, part_m[(size_t)pp * rows + row] * kLog2e);
-  }
-  float M = wave_max(mx);
-  float sig = kNegInf;
-  if (sink) {
-    sig = sink[row % num_heads] * kLog2e;
-    M = fmaxf(M, sig);
-  }
-  const float Ms = (M == kNegInf) ? 0.f : M;
-
+  const float* orow = part_o + (size_t)row * DV + lane * EPL;
+  const size_t pstride = (size_t)rows * DV;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  float lsum = 0.f;
-  const float* orow = part_o + (size_t)row * DV + lane * EPL;
-  const size_t pstride = (size_t)rows * DV;
-  for (int base = 0; base < P; base += 64) {
-    const int pp = base + lane;  // this lane's partition of the chunk and its weight
-    float w = 0.f;
-    if (pp < P) {
-      const float lp = part_l[(size_t)pp * rows + row];
-      if (lp > 0.f) w = lp * fast_exp2(part_m[(size_t)pp * rows + row] * kLog2e - Ms);
-    }
-    lsum += w;
-    const int n = min(64, P - base);
-    // kInFlight partition rows are requested before any is used, without
-    // branches (a branch around each load makes the compiler wait for every
-    // load at the join).  A slot past the end of the chunk or of an empty
-    // partition (weight 0) re-reads the first row of the batch, already in
-    // flight, and a select drops its value (j + u <= 63 for the lane read).
-    for (int j = 0; j < n; j += kInFlight) {
-      float wj[kInFlight];
-      MergeCols<EPL> c[kInFlight];
+  const float sig = sink ? sink[row % num_heads] * kLog2e : kNegInf;
+  float M, lsum;
+
+  if (P <= 64) {
+    // (m_p, l_p) in lane p and the first kInFlight partial rows, requested
+    // together (clamped indices, no branches around the loads)
+    const int pc = lane < P ? lane : 0;
+    const float lp_raw = part_l[(size_t)pc * rows + row];
+    const float mp_raw = part_m[(size_t)pc * rows + row];
+    MergeCols<EPL> c[kInFlight];
 #pragma unroll
-      for (int u = 0; u < kInFlight; ++u) {
-        wj[u] = (j + u < n)
-                    ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u))
-                    : 0.f;
-        const int src = base + j + (wj[u] != 0.f ? u : 0);
-        c[u] = merge_load_cols<EPL>(orow + (size_t)src * pstride);
+    for (int u = 0; u < kInFlight; ++u)
+      c[u] = merge_load_cols<EPL>(orow + (size_t)(u < P ? u : 0) * pstride);
+    const float lp = lane < P ? lp_raw : 0.f;
+    M = fmaxf(wave_max(lp > 0.f ? mp_raw * kLog2e : kNegInf), sig);
+    const float Ms = (M == kNegInf) ? 0.f : M;
+    const float w = lp > 0.f ? lp * fast_exp2(mp_raw * kLog2e - Ms) : 0.f;
+    lsum = w;
+    for (int j = 0; j < P; j += kInFlight) {
+      if (j > 0) {  // more partitions than one group: the next group's rows
+#pragma unroll
+        for (int u = 0; u < kInFlight; ++u)
+          c[u] = merge_load_cols<EPL>(orow + (size_t)(j + u < P ? j + u : j) * pstride);
       }
+      float wj[kInFlight];
 #pragma unroll
       for (int u = 0; u < kInFlight; ++u)
+        wj[u] = (j + u < P) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u))
+                            : 0.f;
+      merge_accumulate(acc, wj, c);
+    }
+  } else {
+    // Longer splits: the row max over every chunk of 64 first, then per chunk the
+    // weights and kInFlight partial rows at a time.  A slot past the end of the
+    // chunk or of an empty partition re-reads the first row of its group (already
+    // in flight), and its value is dropped.
+    float mx = kNegInf;
+    for (int pp = lane; pp < P; pp += 64) {
+      const float lp = part_l[(size_t)pp * rows + row];
+      if (lp > 0.f) mx = fmaxf(mx, part_m[(size_t)pp * rows + row] * kLog2e);
+    }
+    M = fmaxf(wave_max(mx), sig);
+    const float Ms = (M == kNegInf) ? 0.f : M;
+    lsum = 0.f;
+    for (int base = 0; base < P; base += 64) {
+      const int pp = base + lane;  // this lane's partition of the chunk and its weight
+      float w = 0.f;
+      if (pp < P) {
+        const float lp = part_l[(size_t)pp * rows + row];
+        if (lp > 0.f) w = lp * fast_exp2(part_m[(size_t)pp * rows + row] * kLog2e - Ms);
+      }
+      lsum += w;
+      const int n = min(64, P - base);
+      for (int j = 0; j < n; j += kInFlight) {
+        float wj[kInFlight];
+        MergeCols<EPL> c[kInFlight];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float t = fmaf(wj[u], c[u].v[e], acc[e]);
-          acc[e] = (wj[u] != 0.f) ? t : acc[e];
+        for (int u = 0; u < kInFlight; ++u) {
+          wj[u] = (j + u < n)
+                      ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u))
+                      : 0.f;
+          const int src = base + j + (wj[u] != 0.f ? u : 0);
+          c[u] = merge_load_cols<EPL>(orow + (size_t)src * pstride);
         }
+        merge_accumulate(acc, wj, c);
+      }
     }
   }
-  float L = wave_sum(lsum);
-  if (sink) L += fast_exp2(sig - Ms);
 
+  float L = wave_sum(lsum);
+  const float Ms = (M == kNegInf) ? 0.f : M;
+  if (sink) L += fast_exp2(sig - Ms);
   const bool any = L > 0.f;
   const float inv = any ? 1.f / L : 0.f;
   if constexpr (BF16OUT) {

@@ -4,10 +4,10 @@
 // ("mha_decoding_single_batch_pipelined", description; the MLA counterpart in
 // "flare_mla_decoding_dispatch", description), as a launch of its own: for
 // partials from decode_attention_partials() / mla_decode_partials() or any other
-// source.  decode_attention() / mla_decode() merge inside the partition kernel.
+// source, and the second launch of every split call (decode_attention() and
+// mla_decode() with P > 1 and their 8-bit, ragged and sparse forms).
 //
-// The merge arithmetic (one wave per row) lives in da_merge.h, shared with
-// the partition kernels that merge in-kernel.
+// The merge arithmetic (one wave per row) lives in da_merge.h.
 #include "da_merge.h"
 
 namespace da {

@@ -161,9 +161,9 @@ __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage,
 // offset is one of two scalars plus its fixed offset inside the row (in the
 // table).  Offsets are 32-bit from the pool base: the pool holds at most
 // 2^32 / 1152 rows, and each row index is clamped to the pool.
-// The 8 row indices of a tile are copied to LDS two tiles ahead of the tile's
-// loads (lanes 0..7, 4 bytes each), into a ring of 4 slots per wave; the waits
-// that let a tile's loads land cover them.
+// The 8 row indices of a tile are copied to LDS three tile requests ahead of the
+// tile's loads (lanes 0..7, 4 bytes each), into a ring of 4 slots per wave; the
+// waits that let a tile's loads land cover them.
 constexpr int kSpSlots = 4;
 
 __device__ __forceinline__ constexpr int sp_lo(int i) { return (64 * i) / 72; }
@@ -200,7 +200,7 @@ __device__ __forceinline__ void sp_rows_issue(const DecodeParams& p, int b, int 
 }
 
 // Requests tile t of a sparse list into one LDS stage (and the indices of
-// tile t + 2 into their slot): kDmaPerWave + 1 loads per wave.
+// tile t + 3 into their slot): kDmaPerWave + 1 loads per wave.
 __device__ __forceinline__ void mla_issue_sparse(const DecodeParams& p, uint32_t stage, int b,
                                                  int t, int k_lo, int kend, int wave, int lane,
                                                  const uint32_t* tab, const int32_t* slots,
@@ -216,8 +216,8 @@ __device__ __forceinline__ void mla_issue_sparse(const DecodeParams& p, uint32_t
     const uint32_t r = (uint32_t)__builtin_amdgcn_readfirstlane(rw[e]);
     off[e] = (r < last ? r : last) * (uint32_t)kRowBytes;
   }
-  sp_rows_issue(p, b, t + 2, k_lo, kend, wave, lane,
-                slots_lds + (uint32_t)((((t + 2) & (kSpSlots - 1)) * kWaves + wave) * 32));
+  sp_rows_issue(p, b, t + 3, k_lo, kend, wave, lane,
+                slots_lds + (uint32_t)((((t + 3) & (kSpSlots - 1)) * kWaves + wave) * 32));
   const uint4 t0 = *(const uint4*)tab;
   const uint4 t1 = *(const uint4*)(tab + 4);
   const uint32_t e[kDmaPerWave] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w, tab[8]};
@@ -438,10 +438,48 @@ struct MlaPV {
   }
 };
 
-// Softmax of one tile's scores (s0 + s1) into the bf16 weights pb, and, when PV,
-// interleaved with it the P.V contraction of the previous tile (weights pb_prev,
-// V rows in pv's stage): the vector ALU works on this tile while the matrix core
-// works on the last one.
+// Scores of the next tile, one depth step per call of step(st): two
+// accumulation chains (even / odd depth steps), interleaved by the caller with
+// the softmax and the P.V MFMAs of the current tile, so that no score MFMA waits
+// for the one issued just before it.  The K fragments come from a ring kPf deep
+// (same operand layout as mla_scores).
+template <int kPf>
+struct MlaQK {
+  const char* buf;
+  uint32_t kofs;
+  bf16x8_t ring[kPf];
+
+  __device__ __forceinline__ bf16x8_t frag(int st) const {
+    return *(const bf16x8_t*)(buf + ((kofs ^ (32u * (st % 4))) + 128u * (st / 4)));
+  }
+  __device__ __forceinline__ void start(const char* b, uint32_t o) {
+    buf = b;
+    kofs = o;
+#pragma unroll
+    for (int q = 0; q < kPf; ++q) ring[q] = frag(q);
+  }
+  __device__ __forceinline__ void step(int st, f32x16_t& s0, f32x16_t& s1,
+                                       const bf16x8_t (&qf)[kKS]) {
+    const int slot = st % kPf;
+    f32x16_t& s = (st & 1) ? s1 : s0;
+    if (st < 2)
+      mfma_v_first(s, ring[slot], qf[st]);
+    else
+      mfma_v(s, ring[slot], qf[st]);
+    if (st + kPf < kKS) ring[slot] = frag(st + kPf);
+  }
+};
+
+__device__ __forceinline__ void mfma_settle(f32x16_t& s) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+}
+
+// One tile of the loop: the softmax of tile i's scores x into bf16 weights, the
+// P.V contraction of tile i (V rows in vbuf) and, when NEXT, the scores of tile
+// i + 1 (K rows in kbuf), which replace x.  The score MFMAs of tile i + 1 run
+// beside the vector work of the softmax and between the P.V MFMAs, so the matrix
+// core always has independent work queued: the scores form two chains, the P.V
+// MFMAs update 16 different accumulators.
 //
 // Softmax on the accumulator layout: lane l owns row l % 32 and 16 of the 32
 // keys, lane l ^ 32 the other 16.  Each row keeps a fixed reference max, set by
@@ -455,22 +493,26 @@ struct MlaPV {
 // The scale enters once per weight, p = 2^(fma(q.k, sl, -m)) with sl = scale *
 // log2(e) >= 0 (a negative scale was moved into Q by flipping its sign), and the
 // row max is taken over the unscaled scores (sl >= 0 keeps their order).  Only
-// tiles that reach past some row's last visible key (MASKED) compare keys.
-template <bool PV, bool MASKED>
-__device__ __forceinline__ void mla_softmax_pv(const f32x16_t& s0, const f32x16_t& s1, MlaPV& pv,
-                                               const bf16x8_t (&pb_prev)[2], bf16x8_t (&pb)[2],
-                                               f32x16_t (&acc)[kDT], float& m, float& lsum,
-                                               float& lsr, int j0, int hi, float sl,
-                                               bool& restart) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 5;
-  int f = 0;
-  // One P.V MFMA of the previous tile; the scheduling barrier keeps the
-  // compiler from regrouping the interleaved vector and matrix work.
-  auto pv_step = [&]() {
-    if (PV && f < MlaPV::kFrags) {
-      pv.step<false>(f, acc, pb_prev);
-      ++f;
+// tiles that reach past some row's last visible key (MASKED) compare keys:
+// element j of lane half g holds key c32_row(j, g) = c32_row(j, 0) + 4 g of the
+// tile, visible when c32_row(j, 0) < lim = (row's key limit) - (tile's first key)
+// - 4 g.
+template <bool NEXT, bool MASKED, int kPf>
+__device__ __forceinline__ void mla_step(float (&x)[16], const char* kbuf, const char* vbuf,
+                                         const bf16x8_t (&qf)[kKS], uint32_t kofs,
+                                         uint32_t vofs0, uint32_t vofs1, f32x16_t (&acc)[kDT],
+                                         float& m, float& lsum, float& lsr, int lim, float sl,
+                                         bool& restart) {
+  MlaQK<kPf> qk;
+  f32x16_t s0, s1;
+  if (NEXT) qk.start(kbuf, kofs);
+  int st = 0;
+  // One score MFMA of the next tile; the scheduling barrier keeps the compiler
+  // from regrouping the interleaved vector and matrix work.
+  auto qk_step = [&]() {
+    if (NEXT && st < kKS) {
+      qk.step(st, s0, s1, qf);
+      ++st;
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -478,21 +520,19 @@ __device__ __forceinline__ void mla_softmax_pv(const f32x16_t& s0, const f32x16_
   // the interleave: volatile asm keeps its order, so the arithmetic they depend
   // on cannot be sunk below the MFMAs it is meant to run beside.
   auto pin = [](float& v) { asm volatile("" : "+v"(v)); };
-  float x[16];
   float mx = kNegInf;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    x[j] = s0[j] + s1[j];
-    mx = fmaxf(mx, (!MASKED || j0 + c32_row(j, g) < hi) ? x[j] : kNegInf);
+    mx = fmaxf(mx, (!MASKED || c32_row(j, 0) < lim) ? x[j] : kNegInf);
     if (j % 2 == 1) {
       pin(mx);
-      pv_step();
+      qk_step();
     }
   }
   mx = max_xor32(mx);
   mx = (mx == kNegInf) ? kNegInf : mx * sl;
   pin(mx);
-  pv_step();
+  qk_step();
   const bool grow = mx > m + kHeadroom;
   restart = restart || (grow && m != kNegInf);  // a row's first visible tile: acc is still 0
   m = grow ? mx : m;
@@ -502,14 +542,15 @@ __device__ __forceinline__ void mla_softmax_pv(const f32x16_t& s0, const f32x16_
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     x[j] = fast_exp2(fmaf(x[j], sl, nms));
-    if (MASKED) x[j] = (j0 + c32_row(j, g) < hi) ? x[j] : 0.f;
+    if (MASKED) x[j] = (c32_row(j, 0) < lim) ? x[j] : 0.f;
     ps += x[j];
     if (j % 2 == 1) {
       pin(ps);
-      pv_step();
+      qk_step();
     }
   }
   lsum += ps;
+  bf16x8_t pb[2];
   float pr = 0.f;
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
@@ -519,13 +560,36 @@ __device__ __forceinline__ void mla_softmax_pv(const f32x16_t& s0, const f32x16_
       w[q] = pack_bf16(x[8 * kh + 2 * q], x[8 * kh + 2 * q + 1]);
       pr = dot2_bf16(w[q], 0x3f803f80u, pr);  // + both rounded weights (times bf16 1.0)
       pin(pr);
-      pv_step();
+      qk_step();
     }
     pb[kh] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
   }
   lsr += pr;
+  // P.V of this tile (its weights were just written by vector ops: the first two
+  // MFMAs that read them wait), the rest of the next tile's scores in between.
+  // Its V fragments are requested only now (x is dead, so their registers are
+  // free); three score MFMAs cover the read latency.
+  MlaPV pv;
+  pv.start(vbuf, vofs0, vofs1);
+  qk_step();
+  qk_step();
+  qk_step();
+  pv.step<true>(0, acc, pb);
+  qk_step();
+  pv.step<true>(1, acc, pb);
+  qk_step();
 #pragma unroll
-  for (int r = 0; r < MlaPV::kFrags; ++r) pv_step();  // the rest of the previous tile
+  for (int f = 2; f < MlaPV::kFrags; ++f) {
+    pv.step<false>(f, acc, pb);
+    qk_step();
+  }
+#pragma unroll
+  for (int r = 0; r < kKS; ++r) qk_step();  // none left when the P.V slots sufficed
+  if (NEXT) {
+    mfma_settle(s0, s1);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = s0[j] + s1[j];
+  }
 }
 
 template <bool V>
@@ -574,8 +638,12 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   // first and last token.
   const int t_first = (mb * kRows) / H;
   const int t_last = (min(nrows, (mb + 1) * kRows) - 1) / H;
-  const int hmin = max(k_lo, min(k_end, visible_keys(p, b, t_first)));
-  const int hmax = max(k_lo, min(k_end, visible_keys(p, b, t_last)));
+  // (uniform; pinned to scalar registers so that the per-tile key counts derived
+  // from them stay scalar too)
+  const int hmin =
+      __builtin_amdgcn_readfirstlane(max(k_lo, min(k_end, visible_keys(p, b, t_first))));
+  const int hmax =
+      __builtin_amdgcn_readfirstlane(max(k_lo, min(k_end, visible_keys(p, b, t_last))));
 
   // Q^T operand: k-slot (g, j) of depth step st <-> depth 16*st + 8*g + j.
   bf16x8_t qf[kKS];
@@ -601,11 +669,12 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   const uint32_t vofs0 = kRowBytes * vkey + ((16u * cl) ^ (16u * swz(vkey))) + 8u * (i16 & 1);
   const uint32_t vofs1 =
       kRowBytes * (vkey + 8) + ((16u * cl) ^ (16u * swz(vkey + 8))) + 8u * (i16 & 1);
-  // 4-stage ring, software-pipelined: iteration i computes the scores and the
-  // softmax of tile i while the matrix core contracts tile i - 1 with its
-  // weights (pb_prev), so stages i and i - 1 are being read; tile i + 2 is
-  // requested into the stage tile i - 2 left, and before each barrier a wave
-  // waits until only tile i + 2's requests are outstanding (tile i + 1 landed).
+  // 4-stage ring, software-pipelined: the scores of tile 0 come first; then
+  // iteration i takes the softmax and the P.V of tile i while the matrix core
+  // also computes the scores of tile i + 1, so stages i and i + 1 are being read;
+  // tile i + 3 is requested into the stage tile i - 1 left, and before each
+  // barrier a wave waits until only tile i + 3's requests are outstanding (tile
+  // i + 2 landed).
   // Restart votes: each wave writes its own slot for tile i (every tile, 0 or 1)
   // into buffer i & 1 before the tile's barrier; the slots of tile i - 1 are
   // read at the top of tile i, so a read and the next write of the same buffer
@@ -632,8 +701,8 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       return t & (kStages - 1);
     }
   };
-  // Sparse lists: row indices of tiles t, t + 1 sit in slots t % 4, (t + 1) % 4
-  // when tile t is requested.
+  // Sparse lists: row indices of tiles t, t + 1, t + 2 sit in slots t % 4 ..
+  // (t + 2) % 4 when tile t is requested.
   __shared__ __attribute__((aligned(16))) int32_t sp_slots[kSpSlots * kWaves * 8];
   auto issue = [&](int t) __attribute__((always_inline)) {
     const uint32_t stage = lds0 + (uint32_t)((t & (kStages - 1)) * kTileBytes);
@@ -646,11 +715,11 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     else
       mla_issue(p, stage, b, k_lo + t * kBN, hmax, wave, tab);
   };
-  // Sparse lists: the indices of tiles 0 and 1, waited for before tile 0 is
+  // Sparse lists: the indices of tiles 0, 1 and 2, waited for before tile 0 is
   // requested.
   auto prime = [&]() __attribute__((always_inline)) {
     if constexpr (SPARSE) {
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 3; ++t)
         sp_rows_issue(p, b, t, k_lo, hmax, wave, lane,
                       (uint32_t)(uintptr_t)sp_slots + (uint32_t)((t * kWaves + wave) * 32));
       wait_vm_lgkm0<0>();
@@ -662,8 +731,9 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       mla_convert_fp8(smem + kF8Ring0 + (t & 1) * kF8Tile, smem + bstage(t) * kTileBytes, wave,
                       lane, tab);
   };
-  // Start of a pass: tile 0 requested (8-bit: tiles 0 and 1 requested and tile 0
-  // converted once landed).
+  // Start of a pass: tiles 0, 1 and 2 requested (those that exist) and tile 0
+  // landed, with whatever was requested before it (the Q rows on the first pass).
+  // 8-bit: tile 0 is converted before tile 2 reuses its staging slot.
   auto start_pass = [&]() __attribute__((always_inline)) {
     if constexpr (FP8) {
       issue(0);
@@ -674,17 +744,29 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         wait_vm_lgkm0<0>();
       }
       convert(0);
+      if (n_tot > 2) {
+        wait_vm_lgkm0<63>();  // the conversion's reads of the slot are done
+        issue(2);
+      }
     } else {
       prime();
       issue(0);
+      if (n_tot > 2) {
+        issue(1);
+        issue(2);
+        wait_vm_lgkm0<2 * kIssue>();
+      } else if (n_tot > 1) {
+        issue(1);
+        wait_vm_lgkm0<kIssue>();
+      } else {
+        wait_vm_lgkm0<0>();
+      }
     }
   };
   if (n_tot > 0) {
-    // Tile 0 is requested while the Q loads are in flight; both are waited for
-    // before anything else is issued, so that only tile requests are counted
-    // below.
+    // Tile 0 is requested while the Q loads are in flight; start_pass waits for
+    // both.
     start_pass();
-    if constexpr (!FP8) wait_vm_lgkm0<0>();
     // Rows outside the fold get Q = 0; a negative scale flips Q's sign (exact).
     const uint32_t qx = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
@@ -694,74 +776,70 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       qf[s] = row_ok ? __builtin_bit_cast(bf16x8_t, u) : bf16x8_t{};
     }
     const float sl = fabsf(p.scale_log2);
-    bf16x8_t pb_prev[2];
+    const int hi4 = hi - 4 * g;  // the row's key limit, less the lane half's key offset
+    // K fragments in flight: 4 (8-bit: 3, its staging needs registers of its own)
+    constexpr int kKPf = 3;
     for (;;) {  // one pass over the partition; repeated only after a restart
-      // tile 0 is requested on entry; tile 1 now; wait for tile 0 (8-bit: done
-      // by start_pass)
-      if constexpr (!FP8) {
-        if (n_tot > 1) {
-          issue(1);
+      __syncthreads();  // tile 0 is in LDS for every wave
+      float x[16];      // scores of the tile the loop is at
+      {
+        f32x16_t s0, s1;
+        mla_scores<kKPf>(smem + bstage(0) * kTileBytes, qf, kofs, s0, s1);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = s0[j] + s1[j];
+      }
+      // tile 1 landed (8-bit: and converted); tile 2 may stay in flight
+      if (n_tot > 1) {
+        if (n_tot > 2)
           wait_vm_lgkm0<kIssue>();
-        } else {
+        else
           wait_vm_lgkm0<0>();
-        }
+        convert(1);
       }
       __syncthreads();
       // One tile: returns true when the votes of the tile before it ask for a
-      // restart.  PV: contract the previous tile; MASKED: compare keys against
-      // each row's last visible key.  Tile 0, the tiles every row sees whole
-      // and the tail are three loops, so that each loop body holds a single
-      // copy of the softmax / P.V interleave (registers are all in use).
-      auto tile = [&](int i, auto pv_tag, auto mask_tag) __attribute__((always_inline)) {
-        constexpr bool PV = decltype(pv_tag)::value;
+      // restart.  NEXT: the scores of tile i + 1 are computed alongside; MASKED:
+      // compare keys against each row's last visible key.  The tiles every row
+      // sees whole, the rest but the last, and the last are three loops, so that
+      // each loop body holds a single copy of the interleave (registers are all
+      // in use).
+      auto tile = [&](int i, auto next_tag, auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool NEXT = decltype(next_tag)::value;
         constexpr bool MASKED = decltype(mask_tag)::value;
         // Votes of tile i - 1, acted upon after tile i (the load has landed by
         // then; what tile i adds is dropped with the rest on a restart).
         int4 prev = make_int4(0, 0, 0, 0);
-        if (PV) prev = *(const int4*)votes[(i - 1) & 1];
-        const bool ahead = i + 2 < n_tot;
-        if (ahead) issue(i + 2);  // into the stage of tile i - 2, last read a barrier ago
-        f32x16_t s0, s1;
-        // K fragments ring: 4 pairs deep, 3 in the 8-bit form (its staging needs
-        // registers of its own)
-        mla_scores<FP8 ? 3 : 4>(smem + bstage(i) * kTileBytes, qf, kofs, s0, s1);
+        if (i > 0) prev = *(const int4*)votes[(i - 1) & 1];
+        const bool ahead = i + 3 < n_tot;
+        if (ahead) issue(i + 3);  // into the stage of tile i - 1, last read a barrier ago
         bool need = false;
-        bf16x8_t pb[2];
-        MlaPV pv;
-        if (PV) pv.start(smem + bstage(i - 1) * kTileBytes, vofs0, vofs1);
-        mla_softmax_pv<PV, MASKED>(s0, s1, pv, pb_prev, pb, acc, m, lsum, lsr, k_lo + i * kBN,
-                                   hi, sl, need);
-        pb_prev[0] = pb[0];
-        pb_prev[1] = pb[1];
+        mla_step<NEXT, MASKED, kKPf>(x, smem + bstage(i + 1) * kTileBytes,
+                                     smem + bstage(i) * kTileBytes, qf, kofs, vofs0, vofs1, acc,
+                                     m, lsum, lsr, hi4 - (k_lo + i * kBN), sl, need);
         if (lane == 0) votes[i & 1][wave] = __builtin_amdgcn_ballot_w64(need) != 0;
-        // tile i + 1 must have landed: tile i + 2 may stay in flight (8-bit: this
-        // wave's part of staged tile i + 1, converted into the bf16 stage tile i - 2
-        // left, last read a barrier ago)
+        // tile i + 2 must have landed: tile i + 3 may stay in flight (8-bit: this
+        // wave's part of staged tile i + 2, converted into the bf16 stage tile
+        // i - 1 left, last read a barrier ago)
         if (ahead)
           wait_vm_lgkm0<kIssue>();
         else
           wait_vm_lgkm0<0>();
         if constexpr (FP8) {
-          if (i + 1 < n_tot) convert(i + 1);
+          if (i + 2 < n_tot) convert(i + 2);
         }
         __syncthreads();
         return (prev.x | prev.y | prev.z | prev.w) != 0;  // same votes in every wave
       };
-      bool again = tile(0, BoolTag<false>{}, BoolTag<true>{});
-      int i = 1;
-      for (; !again && i < n_full; ++i) again = tile(i, BoolTag<true>{}, BoolTag<false>{});
-      for (; !again && i < n_tot; ++i) again = tile(i, BoolTag<true>{}, BoolTag<true>{});
-      if (!again) {  // the last tile's votes have not been looked at yet
-        const int4 last = *(const int4*)votes[(n_tot - 1) & 1];
-        if (!(last.x | last.y | last.z | last.w)) {
-          // the last tile's P.V (its stage is no longer written)
-          MlaPV pv;
-          pv.start(smem + bstage(n_tot - 1) * kTileBytes, vofs0, vofs1);
-          pv.step<true>(0, acc, pb_prev);
-          pv.step<true>(1, acc, pb_prev);
-#pragma unroll
-          for (int f = 2; f < MlaPV::kFrags; ++f) pv.step<false>(f, acc, pb_prev);
-          break;
+      const int n_body = min(n_full, n_tot - 1);
+      bool again = false;
+      int i = 0;
+      for (; !again && i < n_body; ++i) again = tile(i, BoolTag<true>{}, BoolTag<false>{});
+      for (; !again && i < n_tot - 1; ++i) again = tile(i, BoolTag<true>{}, BoolTag<true>{});
+      if (!again) {
+        again = tile(n_tot - 1, BoolTag<false>{}, BoolTag<true>{});
+        if (!again) {  // the last tile's votes, written before the barrier it ended on
+          const int4 last = *(const int4*)votes[(n_tot - 1) & 1];
+          if (!(last.x | last.y | last.z | last.w)) break;
         }
       }
       // Restart with the raised reference maxima: drop what was accumulated.
@@ -771,7 +849,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       lsum = 0.f;
       lsr = 0.f;
       __syncthreads();  // every wave has read the votes before the next pass writes them
-      start_pass();  // tile 0 of the next pass
+      start_pass();  // tiles 0 .. 2 of the next pass
     }
   }
 

@@ -271,14 +271,15 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
   p.part_o = po;
   p.part_m = pm;
   p.part_l = pl;
-  // Ragged batches on the bf16 GQA kernel take their work items from a queue
-  // (blocks that finish early take more), with two resident blocks per CU.
+  // Ragged batches on the streaming GQA kernels take their work items from a
+  // queue (blocks that finish early take more): one resident block per CU for
+  // bf16 (its queue form has a 96 KB ring), two for the 8-bit cache.
   p.queue = nullptr;
   p.queue_blocks = 0;
   if (split && (plan.variant == kStream || plan.variant == kStreamFp8) && c.valid_length &&
       plan.row_blocks == 1) {
     p.queue = queue;
-    p.queue_blocks = 2 * device_cus();
+    p.queue_blocks = (plan.variant == kStream ? 1 : 2) * device_cus();
   }
 
   hipStream_t s = (hipStream_t)stream;

@@ -6,8 +6,10 @@
 // to stream: each wave moves its own 16-key tiles from HBM straight into a
 // private ring of LDS stages (global_load_lds with the non-temporal hint, no
 // staging registers, no block barriers), the next tile in flight while it works
-// on the current one.  A block takes 64 KB of LDS, so two blocks share a CU and
-// one block's start-up latency hides behind the other's stream.
+// on the current one.  Under the static mapping a block takes 64 KB of LDS, so
+// two blocks share a CU and one block's start-up latency hides behind the other's
+// stream; work-queue blocks run one per CU with a 3-stage ring (96 KB), which
+// streams ragged batches faster.
 //
 // One block of 4 waves handles one (partition, sequence, KV head, 16-row block);
 // wave w takes the partition's tiles w, w + 4, w + 8, ... and keeps its own FA2
@@ -42,7 +44,7 @@ namespace {
 constexpr int kTK = 16;  // keys per tile
 constexpr int kWaves = 4;
 
-template <int D>
+template <int D, int NS = 2>
 struct StreamCfg {
   static constexpr int ROW = D * 2;                  // bytes per key row of one head
   static constexpr int CH = ROW / 16;                // 16-byte chunks per row
@@ -50,7 +52,10 @@ struct StreamCfg {
   static constexpr int STAGE = 2 * HALF;
   static constexpr int NI = HALF / 1024;             // 1 KB load instructions per half
   static constexpr int KEYS_PER_I = 1024 / ROW;      // rows per load instruction
-  static constexpr int STAGES = (D == 128) ? 2 : 4;  // 16 KB ring per wave: two blocks per CU
+  // LDS stages per wave.  Static mapping (NS = 2 at D = 128): a 16 KB ring per
+  // wave, 64 KB per block, so two blocks fit on a CU.  Work queue (NS = 3): one
+  // resident block per CU with a deeper ring.
+  static constexpr int STAGES = (D == 128) ? NS : 4;
   static constexpr int RING = STAGES * STAGE;
   static constexpr int KS = D / 32;                  // depth steps of q.K^T
   static constexpr int DT = D / 16;                  // 16-wide depth tiles of O
@@ -115,12 +120,12 @@ struct StreamState {
 // One tile from the LDS stage `st`.  `after` = tiles of this wave requested
 // after this one (still in flight); the K half is waited for first, the V half
 // just before the P.V contraction.
-template <int D>
+template <int D, int NS>
 __device__ __forceinline__ void stream_tile(const char* st, const bf16x8_t (&qf)[StreamCfg<D>::KS],
                                             StreamState<D>& s, int after, int j0, bool masked,
                                             int hi, float scale_log2, uint32_t kofs,
                                             uint32_t vofs, int g16) {
-  using C = StreamCfg<D>;
+  using C = StreamCfg<D, NS>;
   wait_after<2 * C::NI, C::NI, C::STAGES - 1>(after);  // K half of this tile landed
   f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -171,10 +176,10 @@ __device__ __forceinline__ void stream_tile(const char* st, const bf16x8_t (&qf)
 }
 
 // One work item: rows rb*16.. of (sequence b, KV head g) over partition pidx.
-template <int D>
+template <int D, int NS>
 __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, int b, int g,
                                             int pidx, int rb) {
-  using C = StreamCfg<D>;
+  using C = StreamCfg<D, NS>;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id_uniform();
   const int c16 = lane & 15, g16 = lane >> 4;
@@ -258,7 +263,7 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
                         ring_lds + sn * C::STAGE, off, lane);
       }
       const int t = wave + kWaves * i;
-      stream_tile<D>(ring + cur * C::STAGE, qf, s, my_cnt - 1 - i, k_lo + t * kTK, t >= n_full,
+      stream_tile<D, NS>(ring + cur * C::STAGE, qf, s, my_cnt - 1 - i, k_lo + t * kTK, t >= n_full,
                      hi, p.scale_log2, kofs, vofs, g16);
       cur = (cur + 1 == C::STAGES) ? 0 : cur + 1;
     }
@@ -349,9 +354,9 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
 // atomics order every access to it: a block counts itself done in the high half
 // after its last take, and the block that completes the count (every take is
 // then behind it) sets the word back to zero for the next call.
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
-  using C = StreamCfg<D>;
+  using C = StreamCfg<D, NS>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   __shared__ int s_next[2];
   const int n_work = p.num_partitions * p.batch * p.num_kv_heads;
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
     if (work >= n_work) return;  // padding block: no barrier reached yet
     const int g = work % p.num_kv_heads;
     work /= p.num_kv_heads;
-    stream_item<D>(p, smem, work % p.batch, g, work / p.batch, rb);
+    stream_item<D, NS>(p, smem, work % p.batch, g, work / p.batch, rb);
     return;
   }
   // s_next is double-buffered: slot it & 1 is written again two barriers after
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
     int w = item;
     const int g = w % p.num_kv_heads;
     w /= p.num_kv_heads;
-    stream_item<D>(p, smem, w % p.batch, g, w / p.batch, 0);
+    stream_item<D, NS>(p, smem, w % p.batch, g, w / p.batch, 0);
     __syncthreads();  // the LDS is free again
   }
   if (threadIdx.x == 0) {
@@ -399,9 +404,11 @@ hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s) {
     grid = n_work < p.queue_blocks ? n_work : p.queue_blocks;
   }
   if (p.depth == 64)
-    hipLaunchKernelGGL(decode_stream_kernel<64>, dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((decode_stream_kernel<64, 2>), dim3(grid), dim3(256), 0, s, p);
+  else if (p.queue)
+    hipLaunchKernelGGL((decode_stream_kernel<128, 3>), dim3(grid), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(decode_stream_kernel<128>, dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((decode_stream_kernel<128, 2>), dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -84,8 +84,9 @@ const char* decode_attention_status_string(int status);
  * partition) blocks fills `num_cus` compute units (one resident block per CU
  * for the bf16 kernels) while each partition keeps enough keys to amortise its
  * prologue and its partial write-back.  ragged != 0 (a valid_length array will
- * be passed) asks for about 8 blocks per CU instead, so that the long
- * sequences of a mixed batch are spread over many CUs.  num_cus <= 0 queries
+ * be passed) asks for more, smaller pieces instead (about 16 work items per CU
+ * for GQA, taken from a work queue; about 8 blocks per CU for MLA), so that
+ * the long sequences of a mixed batch are spread over many CUs.  num_cus <= 0 queries
  * the current device.  MLA calls pass num_kv_heads = 1, depth = 576,
  * depth_v = 512.  decode_attention() / mla_decode() with num_partitions = 0 use
  * this with ragged = (valid_length != NULL).  Returns P, or a negative status.

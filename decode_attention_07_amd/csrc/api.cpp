@@ -7,6 +7,7 @@
 // the caller's stream.  Nothing here reads device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -123,6 +124,8 @@ Plan plan_mla(int q_len, int num_q_heads) {
   return pl;
 }
 
+constexpr int kMhaMinKeys = 256;  // keys per partition at least (MHA / GQA heuristic)
+
 int heuristic_partitions(int base_blocks, int max_seq_len, int num_cus, int blocks_per_cu,
                          int min_keys) {
   if (base_blocks < 1) base_blocks = 1;
@@ -133,6 +136,11 @@ int heuristic_partitions(int base_blocks, int max_seq_len, int num_cus, int bloc
   if (P < 1) P = 1;
   if (P > DA_MAX_PARTITIONS) P = DA_MAX_PARTITIONS;
   return (int)P;
+}
+
+// Two KV heads fit one 16-row block of the streaming GQA kernels.
+bool fold_allows_two_heads(int q_len, int group, int num_kv_heads) {
+  return 2 * q_len * group <= 16 && num_kv_heads % 2 == 0;
 }
 
 int keys_per_partition(int max_seq_len, int P, int step) {
@@ -281,17 +289,27 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
     p.queue = queue;
     p.queue_blocks = (plan.variant == kStream ? 1 : 2) * device_cus();
   }
+  // A split call of the streaming GQA kernels (static mapping) whose fold leaves
+  // room in the 16 rows of a block folds two KV heads into one block, which then
+  // reads one contiguous piece of each key row instead of one head's: measured
+  // faster on this chip (long-context batch 1: kernel 86 -> 81 us).  Only while
+  // the blocks still cover the CUs; work-queue calls measured slower with it.
+  p.hb_shift = 0;
+  if (split && !p.queue && (plan.variant == kStream || plan.variant == kStreamFp8) &&
+      plan.row_blocks == 1 && fold_allows_two_heads(c.q_len, p.group, p.num_kv_heads) &&
+      (long)P * c.batch * (p.num_kv_heads / 2) * plan.row_blocks >= device_cus())
+    p.hb_shift = 1;
 
   hipStream_t s = (hipStream_t)stream;
   if (log_enabled())
     std::fprintf(stderr,
                  "[decode_attention] variant=%s B=%d T=%d H=%d KVH=%d D=%d Dv=%d S=%d P=%d C=%d "
-                 "rows/block=%d row_blocks=%d grid=%d paged=%d reduce=%d queue=%d\n",
+                 "rows/block=%d row_blocks=%d grid=%d paged=%d reduce=%d queue=%d heads/block=%d\n",
                  variant_name(plan.variant), c.batch, c.q_len, c.num_q_heads, p.num_kv_heads,
                  p.depth, p.depth_v, c.max_seq_len, P, p.keys_per_partition,
                  plan.rows_per_block, plan.row_blocks,
-                 P * c.batch * p.num_kv_heads * plan.row_blocks, c.page_table != nullptr,
-                 (!partials_only && P > 1) ? 1 : 0, p.queue != nullptr);
+                 P * c.batch * (p.num_kv_heads >> p.hb_shift) * plan.row_blocks, c.page_table != nullptr,
+                 (!partials_only && P > 1) ? 1 : 0, p.queue != nullptr, 1 << p.hb_shift);
   if (launch_partition_pass(p, plan.variant, bf16, s) != hipSuccess) return DA_ERR_HIP;
   if (!partials_only && P > 1) {
     if (da::launch_splitk_reduce(po, pm, pl, P, (int)rows, c.num_q_heads, p.depth_v, sink, out,
@@ -448,8 +466,16 @@ int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_head
     return heuristic_partitions(batch * pl.row_blocks, max_seq_len, num_cus, per_cu, 1024);
   }
   const Plan pl = plan_mha(q_len, num_q_heads / num_kv_heads, true);
-  return heuristic_partitions(batch * num_kv_heads * pl.row_blocks, max_seq_len, num_cus, per_cu,
-                              256);
+  long P = heuristic_partitions(batch * num_kv_heads * pl.row_blocks, max_seq_len, num_cus,
+                                per_cu, kMhaMinKeys);
+  // A dense split call at depth 128 with room for two KV heads per block runs
+  // them folded (bf16 and 8-bit caches): twice the partitions keep the grid full.
+  if (!ragged && P > 1 && depth == 128 &&
+      fold_allows_two_heads(q_len, num_q_heads / num_kv_heads, num_kv_heads)) {
+    const long by_len = ((long)max_seq_len + kMhaMinKeys - 1) / kMhaMinKeys;
+    P = std::min(std::min(2 * P, by_len), (long)DA_MAX_PARTITIONS);
+  }
+  return (int)P;
 }
 
 size_t decode_workspace_size(int num_partitions, int batch, int q_len, int num_q_heads,

@@ -26,6 +26,10 @@ struct DecodeParams {
   int num_partitions;
   int keys_per_partition;       // C: partition p covers keys [p*C, (p+1)*C)
   int row_blocks;               // row tiles per (batch, KV head)
+  // bf16 GQA stream kernel: a block folds 2^hb_shift KV heads (their query rows,
+  // 16 >> hb_shift per head, share the block's 16 rows) and reads them as one
+  // contiguous piece of each key row; 0 elsewhere.
+  int hb_shift;
   int write_partials;           // 1: write part_*; 0: write out / lse directly
   float scale_log2;             // scale * log2(e) (times k_scale for an 8-bit KV cache)
   float v_scale;                // 8-bit KV cache: real value = v_scale * stored value

@@ -73,9 +73,11 @@ __device__ __forceinline__ constexpr int swz(int k) {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-// Requests tile [j0, j0 + 16) of KV head g into the LDS stage at `lds`.  Keys at or
-// past `kend` read the same chunk of the tile's first key instead (finite data,
-// masked out of the softmax), so every tile costs exactly 2 NI instructions.
+// Requests the tile of keys [j0, j0 + 16 >> hb_shift) of KV heads g, g + 1, ...
+// (2^hb_shift of them) into the LDS stage at `lds`: stage row r holds key
+// j0 + (r >> hb_shift) of head g + (r & (2^hb_shift - 1)).  Keys at or past
+// `kend` read the same chunk of the tile's first key instead (finite data, masked
+// out of the softmax), so every tile costs exactly 2 NI instructions.
 template <int D>
 __device__ __forceinline__ void stream_issue(const DecodeParams& p, int b, int g, int j0,
                                              int kend, uint32_t lds,
@@ -98,8 +100,8 @@ __device__ __forceinline__ void stream_issue(const DecodeParams& p, int b, int g
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
     o[i] = off[i];
-    if (nvalid < kTK) {
-      const int key = i * C::KEYS_PER_I + lane / C::CH;
+    if (nvalid < (kTK >> p.hb_shift)) {
+      const int key = (i * C::KEYS_PER_I + lane / C::CH) >> p.hb_shift;
       if (key >= nvalid) o[i] -= (uint32_t)key * rs;
     }
   }
@@ -124,7 +126,7 @@ template <int D, int NS>
 __device__ __forceinline__ void stream_tile(const char* st, const bf16x8_t (&qf)[StreamCfg<D>::KS],
                                             StreamState<D>& s, int after, int j0, bool masked,
                                             int hi, float scale_log2, uint32_t kofs,
-                                            uint32_t vofs, int g16) {
+                                            uint32_t vofs, const int (&kkey)[4]) {
   using C = StreamCfg<D, NS>;
   wait_after<2 * C::NI, C::NI, C::STAGES - 1>(after);  // K half of this tile landed
   f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -135,10 +137,11 @@ __device__ __forceinline__ void stream_tile(const char* st, const bf16x8_t (&qf)
   }
   float x[4];
   float mx = kNegInf;
+  const int lim = hi - j0;  // this row's visible keys from the tile's first key on
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float v = sc[r] * scale_log2;
-    if (masked) v = (j0 + 4 * g16 + r < hi) ? v : kNegInf;
+    if (masked) v = (kkey[r] < lim) ? v : kNegInf;
     x[r] = v;
     mx = fmaxf(mx, v);
   }
@@ -175,7 +178,10 @@ __device__ __forceinline__ void stream_tile(const char* st, const bf16x8_t (&qf)
   }
 }
 
-// One work item: rows rb*16.. of (sequence b, KV head g) over partition pidx.
+// One work item: rows rb*16.. of (sequence b, KV heads g .. g + 2^hb_shift - 1)
+// over partition pidx.  With hb_shift > 0 (then rb = 0) the 16 rows are 2^hb_shift
+// slots of 16 >> hb_shift rows, slot s holding the token-major fold of KV head
+// g + s, and a score of a row against a stage row of another head is masked out.
 template <int D, int NS>
 __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, int b, int g,
                                             int pidx, int rb) {
@@ -183,14 +189,18 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
   const int lane = threadIdx.x & 63;
   const int wave = wave_id_uniform();
   const int c16 = lane & 15, g16 = lane >> 4;
+  const int hbs = p.hb_shift;
+  const int kpt = kTK >> hbs;            // keys per tile
+  const int rps = 4 - hbs;               // log2 of the rows per head slot
 
   // This lane's query row (16 rows per block: rows of the token-major fold).
   const int nrows = seq_tokens(p, b) * p.group;  // this sequence's fold
   const size_t row0q = seq_row0(p, b);
-  const int rr = rb * 16 + c16;
+  const int slot = c16 >> rps;
+  const int rr = rb * 16 + (c16 & ((1 << rps) - 1));
   const bool row_ok = rr < nrows;
   const int tok = row_ok ? rr / p.group : 0;
-  const int head = g * p.group + (row_ok ? rr % p.group : 0);
+  const int head = (g + slot) * p.group + (row_ok ? rr % p.group : 0);
   const int k_lo = pidx * p.keys_per_partition;
   const int lim = row_ok ? visible_keys(p, b, tok) : 0;
   const int hi = row_ok ? min(k_lo + p.keys_per_partition, lim) : k_lo;
@@ -220,13 +230,23 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
   s.lsr = 0.f;
 
   // Per-lane load offsets: instruction i moves stage chunk 64 i + lane, i.e.
-  // chunk (lane % CH) ^ swz(key) of key i * KEYS_PER_I + lane / CH.
+  // chunk (lane % CH) ^ swz(r) of stage row r = i * KEYS_PER_I + lane / CH, which
+  // is key r >> hbs of head slot r & (2^hbs - 1) (consecutive in the cache row).
   uint32_t off[C::NI];
   const uint32_t rs = (uint32_t)p.num_kv_heads * C::ROW;
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
-    const int key = i * C::KEYS_PER_I + lane / C::CH;
-    off[i] = (uint32_t)key * rs + 16u * (uint32_t)((lane % C::CH) ^ swz<D>(key));
+    const int r = i * C::KEYS_PER_I + lane / C::CH;
+    off[i] = (uint32_t)(r >> hbs) * rs + (uint32_t)(r & ((1 << hbs) - 1)) * C::ROW +
+             16u * (uint32_t)((lane % C::CH) ^ swz<D>(r));
+  }
+  // Key (from the tile's first) of the stage rows 4 g16 + 0..3 this lane scores;
+  // stage rows of another head slot never pass the mask.
+  int kkey[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * g16 + j;
+    kkey[j] = ((r & ((1 << hbs) - 1)) == slot) ? (r >> hbs) : 0x7fffffff;
   }
   // Read offsets inside a stage: K operand of depth step k at kofs ^ 64 k; the
   // V^T operand of depth tile dt at vofs ^ 32 dt (from the half's start).
@@ -235,8 +255,9 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
   const uint32_t vofs = vkey * C::ROW + 16u * (uint32_t)(((c16 & 3) >> 1) ^ swz<D>(vkey)) +
                         8u * (c16 & 1);
 
-  const int n_full = (hmin - k_lo) / kTK;
-  const int n_tot = (hmax - k_lo + kTK - 1) / kTK;
+  // Tiles below n_full are whole for every row; with several heads every tile is masked.
+  const int n_full = (hbs > 0) ? 0 : (hmin - k_lo) / kpt;
+  const int n_tot = (hmax - k_lo + kpt - 1) / kpt;
   const int my_cnt = (n_tot > wave) ? (n_tot - wave + kWaves - 1) / kWaves : 0;
   char* ring = smem + wave * C::RING;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
@@ -245,26 +266,26 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
     // everything so far is waited for, so that only tile loads are counted
     // below.  The builtin form lets the compiler see that the Q registers are
     // ready; the empty asm keeps memory accesses on their side of it.
-    stream_issue<D>(p, b, g, k_lo + wave * kTK, hmax, ring_lds, off, lane);
+    stream_issue<D>(p, b, g, k_lo + wave * kpt, hmax, ring_lds, off, lane);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int s = 0; s < C::KS; ++s) qf[s] = row_ok ? qf[s] : bf16x8_t{};
     const int pro = min(C::STAGES - 1, my_cnt);
     for (int i = 1; i < pro; ++i)
-      stream_issue<D>(p, b, g, k_lo + (wave + kWaves * i) * kTK, hmax, ring_lds + i * C::STAGE,
+      stream_issue<D>(p, b, g, k_lo + (wave + kWaves * i) * kpt, hmax, ring_lds + i * C::STAGE,
                       off, lane);
     int cur = 0;
     for (int i = 0; i < my_cnt; ++i) {
       const int nxt = i + C::STAGES - 1;
       if (nxt < my_cnt) {  // into the stage read one tile ago
         const int sn = (cur == 0) ? C::STAGES - 1 : cur - 1;
-        stream_issue<D>(p, b, g, k_lo + (wave + kWaves * nxt) * kTK, hmax,
+        stream_issue<D>(p, b, g, k_lo + (wave + kWaves * nxt) * kpt, hmax,
                         ring_lds + sn * C::STAGE, off, lane);
       }
       const int t = wave + kWaves * i;
-      stream_tile<D, NS>(ring + cur * C::STAGE, qf, s, my_cnt - 1 - i, k_lo + t * kTK, t >= n_full,
-                     hi, p.scale_log2, kofs, vofs, g16);
+      stream_tile<D, NS>(ring + cur * C::STAGE, qf, s, my_cnt - 1 - i, k_lo + t * kpt, t >= n_full,
+                     hi, p.scale_log2, kofs, vofs, kkey);
       cur = (cur + 1 == C::STAGES) ? 0 : cur + 1;
     }
   }
@@ -298,10 +319,10 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
   for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
     const int r = idx / D;
     const int d = idx % D;
-    const int rrow = rb * 16 + r;
+    const int rrow = rb * 16 + (r & ((1 << rps) - 1));
     if (rrow >= nrows) continue;
     const int tt = rrow / p.group;
-    const int h = g * p.group + rrow % p.group;
+    const int h = (g + (r >> rps)) * p.group + rrow % p.group;
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * 16 + r]);
@@ -359,7 +380,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
   using C = StreamCfg<D, NS>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   __shared__ int s_next[2];
-  const int n_work = p.num_partitions * p.batch * p.num_kv_heads;
+  const int n_hg = p.num_kv_heads >> p.hb_shift;  // KV head groups
+  const int n_work = p.num_partitions * p.batch * n_hg;
   if (p.queue == nullptr) {
     const int id = blockIdx.x;
     const int xcd = id & 7;
@@ -367,8 +389,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
     const int rb = rq % p.row_blocks;
     int work = (rq / p.row_blocks) * 8 + xcd;
     if (work >= n_work) return;  // padding block: no barrier reached yet
-    const int g = work % p.num_kv_heads;
-    work /= p.num_kv_heads;
+    const int g = (work % n_hg) << p.hb_shift;
+    work /= n_hg;
     stream_item<D, NS>(p, smem, work % p.batch, g, work / p.batch, rb);
     return;
   }
@@ -380,8 +402,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
     const int item = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
     if (item >= n_work) break;
     int w = item;
-    const int g = w % p.num_kv_heads;
-    w /= p.num_kv_heads;
+    const int g = (w % n_hg) << p.hb_shift;
+    w /= n_hg;
     stream_item<D, NS>(p, smem, w % p.batch, g, w / p.batch, 0);
     __syncthreads();  // the LDS is free again
   }
@@ -397,7 +419,10 @@ int stream_rows_per_block() { return 16; }
 int stream_step_keys() { return kTK; }
 
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s) {
-  const int n_work = p.num_partitions * p.batch * p.num_kv_heads;
+  if (p.hb_shift < 0 || p.hb_shift > 1 || (p.num_kv_heads & ((1 << p.hb_shift) - 1)) != 0 ||
+      (p.hb_shift > 0 && (p.row_blocks != 1 || (fold_rows(p) << p.hb_shift) > 16)))
+    return hipErrorInvalidValue;
+  const int n_work = p.num_partitions * p.batch * (p.num_kv_heads >> p.hb_shift);
   int grid = ((n_work + 7) / 8) * 8 * p.row_blocks;
   if (p.queue) {
     if (p.row_blocks != 1 || p.queue_blocks < 1) return hipErrorInvalidValue;

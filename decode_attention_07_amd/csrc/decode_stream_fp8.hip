@@ -83,9 +83,11 @@ __device__ __forceinline__ uint2 lds_read_tr8(const void* p) {
   return make_uint2((uint32_t)t.x, (uint32_t)t.y);
 }
 
-// Requests tile [j0, j0 + 32) of KV head g into the LDS stage at `lds`.  Keys at
-// or past `kend` read the same chunk of the tile's first key instead (finite
-// data, masked out of the softmax), so every tile costs exactly 2 NI loads.
+// Requests the tile of keys [j0, j0 + 32 >> hb_shift) of KV heads g, g + 1, ...
+// (2^hb_shift of them) into the LDS stage at `lds`: stage row r holds key
+// j0 + (r >> hb_shift) of head g + (r & (2^hb_shift - 1)).  Keys at or past
+// `kend` read the same chunk of the tile's first key instead (finite data,
+// masked out of the softmax), so every tile costs exactly 2 NI loads.
 __device__ __forceinline__ void fp8_issue(const DecodeParams& p, int b, int g, int j0, int kend,
                                           uint32_t lds, const uint32_t (&off)[Fp8Cfg::NI],
                                           int lane) {
@@ -102,8 +104,8 @@ __device__ __forceinline__ void fp8_issue(const DecodeParams& p, int b, int g, i
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
     o[i] = off[i];
-    if (nvalid < kTK8) {
-      const int key = i * C::KEYS_PER_I + lane / C::CH;
+    if (nvalid < (kTK8 >> p.hb_shift)) {
+      const int key = (i * C::KEYS_PER_I + lane / C::CH) >> p.hb_shift;
       if (key >= nvalid) o[i] -= (uint32_t)key * rs;
     }
   }
@@ -122,7 +124,8 @@ struct Fp8State {
 // it (still in flight).
 __device__ __forceinline__ void fp8_tile(const char* st, const bf16x8_t (&qf)[Fp8Cfg::KS],
                                          Fp8State& s, int after, int j0, bool masked, int hi,
-                                         float scale_log2, uint32_t kofs, uint32_t vofs, int g16) {
+                                         float scale_log2, uint32_t kofs, uint32_t vofs,
+                                         const int (&kkey)[8]) {
   using C = Fp8Cfg;
   wait_after<2 * C::NI, C::NI, C::STAGES - 1>(after);  // K half of this tile landed
   f32x4_t sc[2];
@@ -138,12 +141,13 @@ __device__ __forceinline__ void fp8_tile(const char* st, const bf16x8_t (&qf)[Fp
                                                        0, 0, 0);
     }
   }
-  float x[8];  // slot b: key pv_key(g16, b)
+  float x[8];  // slot b: stage row pv_key(g16, b)
   float mx = kNegInf;
+  const int lim = hi - j0;  // this row's visible keys from the tile's first key on
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     float v = sc[b >> 2][b & 3] * scale_log2;
-    if (masked) v = (j0 + pv_key(g16, b) < hi) ? v : kNegInf;
+    if (masked) v = (kkey[b] < lim) ? v : kNegInf;
     x[b] = v;
     mx = fmaxf(mx, v);
   }
@@ -180,7 +184,10 @@ __device__ __forceinline__ void fp8_tile(const char* st, const bf16x8_t (&qf)[Fp
   }
 }
 
-// One work item: rows rb*16.. of (sequence b, KV head g) over partition pidx.
+// One work item: rows rb*16.. of (sequence b, KV heads g .. g + 2^hb_shift - 1)
+// over partition pidx; with hb_shift > 0 (then rb = 0) the 16 rows are 2^hb_shift
+// slots of 16 >> hb_shift rows, slot s holding the fold of KV head g + s, and a
+// score of a row against a stage row of another head is masked out.
 __device__ __forceinline__ void fp8_item(const DecodeParams& p, char* smem, int b, int g,
                                          int pidx, int rb) {
   using C = Fp8Cfg;
@@ -188,13 +195,17 @@ __device__ __forceinline__ void fp8_item(const DecodeParams& p, char* smem, int 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id_uniform();
   const int c16 = lane & 15, g16 = lane >> 4;
+  const int hbs = p.hb_shift;
+  const int kpt = kTK8 >> hbs;           // keys per tile
+  const int rps = 4 - hbs;               // log2 of the rows per head slot
 
   const int nrows = seq_tokens(p, b) * p.group;  // this sequence's fold
   const size_t row0q = seq_row0(p, b);
-  const int rr = rb * 16 + c16;
+  const int slot = c16 >> rps;
+  const int rr = rb * 16 + (c16 & ((1 << rps) - 1));
   const bool row_ok = rr < nrows;
   const int tok = row_ok ? rr / p.group : 0;
-  const int head = g * p.group + (row_ok ? rr % p.group : 0);
+  const int head = (g + slot) * p.group + (row_ok ? rr % p.group : 0);
   const int k_lo = pidx * p.keys_per_partition;
   const int lim = row_ok ? visible_keys(p, b, tok) : 0;
   const int hi = row_ok ? min(k_lo + p.keys_per_partition, lim) : k_lo;
@@ -223,13 +234,24 @@ __device__ __forceinline__ void fp8_item(const DecodeParams& p, char* smem, int 
   s.lsr = 0.f;
 
   // Load instruction i moves stage chunk 64 i + lane: chunk position lane % CH
-  // of key i * KEYS_PER_I + lane / CH, holding the key's chunk (lane % CH) ^ swz8.
+  // of stage row r = i * KEYS_PER_I + lane / CH, holding its chunk
+  // (lane % CH) ^ swz8(r); stage row r is key r >> hbs of head slot
+  // r & (2^hbs - 1) (consecutive in the cache row).
   uint32_t off[C::NI];
   const uint32_t rs = (uint32_t)p.num_kv_heads * C::ROW;
 #pragma unroll
   for (int i = 0; i < C::NI; ++i) {
-    const int key = i * C::KEYS_PER_I + lane / C::CH;
-    off[i] = (uint32_t)key * rs + 16u * (uint32_t)((lane % C::CH) ^ swz8(key));
+    const int r = i * C::KEYS_PER_I + lane / C::CH;
+    off[i] = (uint32_t)(r >> hbs) * rs + (uint32_t)(r & ((1 << hbs) - 1)) * C::ROW +
+             16u * (uint32_t)((lane % C::CH) ^ swz8(r));
+  }
+  // Key (from the tile's first) of the stage row of each weight slot; rows of
+  // another head slot never pass the mask.
+  int kkey[8];
+#pragma unroll
+  for (int bq = 0; bq < 8; ++bq) {
+    const int r = pv_key(g16, bq);
+    kkey[bq] = ((r & ((1 << hbs) - 1)) == slot) ? (r >> hbs) : 0x7fffffff;
   }
   // Score reads: key c16 of the first half, depth step k: chunk 2 k + g16 / 2
   // at kofs ^ 32 k (the second half adds 16 rows and XORs 64, see fp8_tile).
@@ -241,32 +263,33 @@ __device__ __forceinline__ void fp8_item(const DecodeParams& p, char* smem, int 
   const int vkey = pv_key(g16, bb);
   const uint32_t vofs = vkey * C::ROW + 16u * (uint32_t)swz8(vkey) + 8u * hh;
 
-  const int n_full = (hmin - k_lo) / kTK8;
-  const int n_tot = (hmax - k_lo + kTK8 - 1) / kTK8;
+  // Tiles below n_full are whole for every row; with several heads every tile is masked.
+  const int n_full = (hbs > 0) ? 0 : (hmin - k_lo) / kpt;
+  const int n_tot = (hmax - k_lo + kpt - 1) / kpt;
   const int my_cnt = (n_tot > wave) ? (n_tot - wave + kW8 - 1) / kW8 : 0;
   char* ring = smem + wave * C::RING;
   const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
   if (my_cnt > 0) {
-    fp8_issue(p, b, g, k_lo + wave * kTK8, hmax, ring_lds, off, lane);
+    fp8_issue(p, b, g, k_lo + wave * kpt, hmax, ring_lds, off, lane);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): Q and the first tile
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int s2 = 0; s2 < C::KS; ++s2) qf[s2] = row_ok ? qf[s2] : bf16x8_t{};
     const int pro = min(C::STAGES - 1, my_cnt);
     for (int i = 1; i < pro; ++i)
-      fp8_issue(p, b, g, k_lo + (wave + kW8 * i) * kTK8, hmax, ring_lds + i * C::STAGE, off,
+      fp8_issue(p, b, g, k_lo + (wave + kW8 * i) * kpt, hmax, ring_lds + i * C::STAGE, off,
                 lane);
     int cur = 0;
     for (int i = 0; i < my_cnt; ++i) {
       const int nxt = i + C::STAGES - 1;
       if (nxt < my_cnt) {  // into the stage read one tile ago
         const int sn = (cur == 0) ? C::STAGES - 1 : cur - 1;
-        fp8_issue(p, b, g, k_lo + (wave + kW8 * nxt) * kTK8, hmax, ring_lds + sn * C::STAGE,
+        fp8_issue(p, b, g, k_lo + (wave + kW8 * nxt) * kpt, hmax, ring_lds + sn * C::STAGE,
                   off, lane);
       }
       const int t = wave + kW8 * i;
-      fp8_tile(ring + cur * C::STAGE, qf, s, my_cnt - 1 - i, k_lo + t * kTK8, t >= n_full, hi,
-               p.scale_log2, kofs, vofs, g16);
+      fp8_tile(ring + cur * C::STAGE, qf, s, my_cnt - 1 - i, k_lo + t * kpt, t >= n_full, hi,
+               p.scale_log2, kofs, vofs, kkey);
       cur = (cur + 1 == C::STAGES) ? 0 : cur + 1;
     }
   }
@@ -299,10 +322,10 @@ __device__ __forceinline__ void fp8_item(const DecodeParams& p, char* smem, int 
   for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
     const int r = idx / D;
     const int d = idx % D;
-    const int rrow = rb * 16 + r;
+    const int rrow = rb * 16 + (r & ((1 << rps) - 1));
     if (rrow >= nrows) continue;
     const int tt = rrow / p.group;
-    const int h = g * p.group + rrow % p.group;
+    const int h = (g + (r >> rps)) * p.group + rrow % p.group;
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < kW8; ++w) M = fmaxf(M, sm[w * 16 + r]);
@@ -348,7 +371,8 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p) 
   using C = Fp8Cfg;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
   __shared__ int s_next[2];
-  const int n_work = p.num_partitions * p.batch * p.num_kv_heads;
+  const int n_hg = p.num_kv_heads >> p.hb_shift;  // KV head groups
+  const int n_work = p.num_partitions * p.batch * n_hg;
   if (p.queue == nullptr) {
     const int id = blockIdx.x;
     const int xcd = id & 7;
@@ -356,8 +380,8 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p) 
     const int rb = rq % p.row_blocks;
     int work = (rq / p.row_blocks) * 8 + xcd;
     if (work >= n_work) return;  // padding block: no barrier reached yet
-    const int g = work % p.num_kv_heads;
-    work /= p.num_kv_heads;
+    const int g = (work % n_hg) << p.hb_shift;
+    work /= n_hg;
     fp8_item(p, smem, work % p.batch, g, work / p.batch, rb);
     return;
   }
@@ -367,8 +391,8 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p) 
     const int item = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
     if (item >= n_work) break;
     int w = item;
-    const int g = w % p.num_kv_heads;
-    w /= p.num_kv_heads;
+    const int g = (w % n_hg) << p.hb_shift;
+    w /= n_hg;
     fp8_item(p, smem, w % p.batch, g, w / p.batch, 0);
     __syncthreads();  // the LDS is free again
   }
@@ -384,7 +408,10 @@ int stream_fp8_step_keys() { return kTK8; }
 
 hipError_t launch_decode_stream_fp8(const DecodeParams& p, hipStream_t s) {
   if (p.depth != 128) return hipErrorInvalidValue;
-  const int n_work = p.num_partitions * p.batch * p.num_kv_heads;
+  if (p.hb_shift < 0 || p.hb_shift > 1 || (p.num_kv_heads & ((1 << p.hb_shift) - 1)) != 0 ||
+      (p.hb_shift > 0 && (p.row_blocks != 1 || (fold_rows(p) << p.hb_shift) > 16)))
+    return hipErrorInvalidValue;
+  const int n_work = p.num_partitions * p.batch * (p.num_kv_heads >> p.hb_shift);
   int grid = ((n_work + 7) / 8) * 8 * p.row_blocks;
   if (p.queue) {
     if (p.row_blocks != 1 || p.queue_blocks < 1) return hipErrorInvalidValue;

@@ -75,6 +75,22 @@ def test_heuristic_fills_the_device():
     assert DA.num_partitions(1, 1, 8, 8, 64, 64, 256, num_cus=256) == 1
 
 
+def test_heuristic_doubles_for_the_two_head_fold():
+    # a dense split call at depth 128 whose fold leaves room for two KV heads per
+    # block gets twice the partitions (the streaming kernels then fold the heads)
+    assert DA.num_partitions(1, 1, 32, 8, 128, 128, 131072, num_cus=256) == 64
+    assert DA.num_partitions(2, 2, 16, 4, 128, 128, 65536, num_cus=256) == 64  # fold 2 x 4
+    # ... but never past the minimum partition length (10000 keys: at most 40)
+    assert DA.num_partitions(1, 1, 32, 8, 128, 128, 10000, num_cus=256) == 40
+    # no doubling: depth 64, a fold of 16 rows, an odd KV head count, a ragged
+    # batch (work queue), or a call that is not split
+    assert DA.num_partitions(1, 1, 32, 8, 64, 64, 131072, num_cus=256) == 32
+    assert DA.num_partitions(1, 1, 128, 8, 128, 128, 131072, num_cus=256) == 32
+    assert DA.num_partitions(1, 1, 12, 3, 128, 128, 131072, num_cus=256) == 86
+    assert DA.num_partitions(1, 1, 32, 8, 128, 128, 131072, ragged=True, num_cus=256) == 512
+    assert DA.num_partitions(32, 1, 32, 8, 128, 128, 4096, num_cus=256) == 1
+
+
 def test_heuristic_rejects_bad_shapes():
     lib = DA.library()
     assert lib.decode_num_partitions(0, 1, 8, 8, 64, 64, 10, 0, 256) == DA.DA_ERR_INVALID_ARG

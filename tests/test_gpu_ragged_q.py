@@ -96,3 +96,15 @@ def test_ragged_q_uniform_equals_padded_call():
     torch.cuda.synchronize()
     assert torch.equal(out_r.reshape(out_p.shape).view(torch.int16), out_p.view(torch.int16))
     assert torch.equal(lse_r.reshape(lse_p.shape), lse_p)
+
+
+@pytest.mark.parametrize("tokens", [[2, 0, 1], [2, 2, 2]])
+def test_ragged_q_two_head_fold(tokens):
+    """A dense ragged-q call (no valid_length, so no work queue) with 2 tokens x
+    group 4 = 8 rows per KV head and P large enough for every CU: the streaming
+    kernel folds two KV heads into each block."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wl = W.Workload("ragged_q_fold", 9890, batch=3, num_heads=16, kv_heads=4, depth=128,
+                    max_seq_len=300, q_len=2, causal=True, sink=True)
+    P = min(1024, -(-2 * cus // (wl.batch * wl.kv_heads)))
+    _run(wl, tokens, P, f"fold tokens={tokens} P={P}")

@@ -38,8 +38,14 @@
  *  - Sink: sigma_h joins the softmax denominator once per row, as a virtual
  *    key of score sigma_h (not multiplied by scale) whose value row is zero.
  *  - A row with no visible key and no sink yields out = 0 and lse = -inf.
- *  - Keys at or past a row's visible length are never read into the result,
- *    whatever they hold (NaN included).
+ *  - Keys at or past a sequence's length (valid_length[b], else max_seq_len)
+ *    are never read into the result, whatever they hold (NaN included).
+ *    Keys and values inside it are expected to be finite: a row's score
+ *    against a key it may not see is masked before the softmax, but the
+ *    value rows a block loads are multiplied by weights that may be zero, so
+ *    a non-finite value can reach other rows of the same sequence (other
+ *    tokens under the causal mask; the paired KV head where a GQA block folds
+ *    two KV heads).
  *  - Every argument check runs before anything is enqueued; on error nothing
  *    is enqueued and a negative status is returned.  Launch failures map to
  *    DA_ERR_HIP.  Calls are thread-safe.

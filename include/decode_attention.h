@@ -92,7 +92,11 @@ const char* decode_attention_status_string(int status);
  * prologue and its partial write-back.  ragged != 0 (a valid_length array will
  * be passed) asks for more, smaller pieces instead (about 16 work items per CU
  * for GQA, taken from a work queue; about 8 blocks per CU for MLA), so that
- * the long sequences of a mixed batch are spread over many CUs.  num_cus <= 0 queries
+ * the long sequences of a mixed batch are spread over many CUs.  A dense
+ * split call (ragged = 0, P > 1) at depth 128 whose q_len x group is at most 8
+ * and whose KV head count is even gets twice the partitions (at most one per
+ * 256 keys): the bf16 and 8-bit streaming kernels then fold two KV heads into
+ * each block, and the grid keeps its size.  num_cus <= 0 queries
  * the current device.  MLA calls pass num_kv_heads = 1, depth = 576,
  * depth_v = 512.  decode_attention() / mla_decode() with num_partitions = 0 use
  * this with ragged = (valid_length != NULL).  Returns P, or a negative status.

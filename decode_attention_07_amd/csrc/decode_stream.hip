@@ -17,6 +17,11 @@
 // "decoding_warp_split_k" in its Parameters); the 4 states are merged by
 // log-sum-exp at the end, and the block writes either the finished rows or the
 // normalised partial (o, m, l) of its partition for the split-K merge.
+// A split call whose fold leaves room (at most 8 rows per KV head) may give a
+// block two KV heads instead (the two-head fold): its 16 rows are two slots of
+// 8, a 16-row stage holds 8 keys x 2 heads (512 contiguous bytes of each key
+// row per load), and a row's scores against the other head's stage rows are
+// masked out.
 //
 // Per 16-key tile and wave (rows padded to 16):
 //   S^T[16 keys x 16 rows] = K[16 x D] . Q^T[D x 16]      D/32 v_mfma_f32_16x16x32_bf16
@@ -362,7 +367,7 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
   }
 }
 
-// Static mapping: block -> (partition, sequence, KV head, row block); the row
+// Static mapping: block -> (partition, sequence, KV head or head pair, row block); the row
 // blocks of one (partition, sequence, KV head) get ids 8 apart, so that they
 // share an XCD and its L2 serves the second read of their tiles.
 //

@@ -9,7 +9,8 @@
 // its own FA2 online-softmax state ("mha_decoding_single_batch_pipelined",
 // description; "decoding_warp_split_k" in its Parameters), and the 4 states are
 // merged by log-sum-exp at the end.  A tile is 32 keys here, so that a stage
-// holds as many bytes as a 16-key bf16 stage.
+// holds as many bytes as a 16-key bf16 stage; under the two-head fold of split
+// calls it is 16 keys x 2 KV heads.
 //
 // The scales need no work per element: a key's real value is k_scale times
 // its stored one, so q.k picks up k_scale, which the host folds into the

@@ -180,4 +180,42 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
   if (lse && lane == 0) lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
 }
 
+// Two waves per row for a row split into 33..64 partitions at DV <= 128: wave
+// `half` takes partitions 32 half .. 32 half + 31, all requested at once (one
+// memory round trip), and returns its own max Mh (log2 units, no sink), the sum
+// of its weights lh = sum l_p 2^(m_p - Mh) and acc = sum l_p 2^(m_p - Mh) O_p
+// (this lane's DV/64 columns).  An empty half returns Mh = -inf, lh = 0, acc = 0.
+template <int DV>
+__device__ __forceinline__ void merge_half(const float* __restrict__ part_o,
+                                           const float* __restrict__ part_m,
+                                           const float* __restrict__ part_l, int P, int rows,
+                                           int row, int half, int lane,
+                                           float (&acc)[DV / 64], float& Mh, float& lh) {
+  constexpr int EPL = DV / 64;
+  constexpr int N = 32;
+  const int p0 = half * N;
+  const int n = min(N, P - p0);  // >= 1 for both halves when 32 < P <= 64
+  const float* orow = part_o + (size_t)row * DV + lane * EPL;
+  const size_t pstride = (size_t)rows * DV;
+  const int pc = p0 + (lane < n ? lane : 0);
+  const float lp_raw = part_l[(size_t)pc * rows + row];
+  const float mp_raw = part_m[(size_t)pc * rows + row];
+  MergeCols<EPL> c[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    c[u] = merge_load_cols<EPL>(orow + (size_t)(p0 + (u < n ? u : 0)) * pstride);
+  const float lp = lane < n ? lp_raw : 0.f;
+  Mh = wave_max(lp > 0.f ? mp_raw * kLog2e : kNegInf);
+  const float Ms = (Mh == kNegInf) ? 0.f : Mh;
+  const float w = lp > 0.f ? lp * fast_exp2(mp_raw * kLog2e - Ms) : 0.f;
+  lh = wave_sum(w);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float wj[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    wj[u] = (u < n) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u)) : 0.f;
+  merge_accumulate(acc, wj, c);
+}
+
 }  // namespace da

@@ -29,10 +29,79 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(
                          threadIdx.x & 63);
 }
 
+// Rows split into 33..64 partitions at DV <= 128 (a long sequence over few
+// rows): two waves per row, each merging 32 partitions with all their partial
+// rows in flight, then one combine through LDS: one memory round trip per row
+// instead of two.  Two rows per block of 4 waves.
+template <int DV, bool BF16OUT>
+__global__ __launch_bounds__(kThreads) void splitk_reduce_pair_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_m,
+    const float* __restrict__ part_l, int P, int rows, int num_heads,
+    const float* __restrict__ sink, void* __restrict__ out, float* __restrict__ lse) {
+  constexpr int EPL = DV / 64;
+  __shared__ float s_acc[2][64 * EPL];
+  __shared__ float s_ml[2][2];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slot = wave >> 1, half = wave & 1;
+  const int row = blockIdx.x * 2 + slot;
+  const bool valid = row < rows;  // both waves of a slot agree; every wave reaches the barrier
+  float acc[EPL];
+  float Mh = kNegInf, lh = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  if (valid) merge_half<DV>(part_o, part_m, part_l, P, rows, row, half, lane, acc, Mh, lh);
+  if (half == 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_acc[slot][lane * EPL + e] = acc[e];
+    if (lane == 0) {
+      s_ml[slot][0] = Mh;
+      s_ml[slot][1] = lh;
+    }
+  }
+  __syncthreads();
+  if (half == 1 || !valid) return;
+  const float M1 = s_ml[slot][0], l1 = s_ml[slot][1];
+  const float sig = sink ? sink[row % num_heads] * kLog2e : kNegInf;
+  const float M = fmaxf(fmaxf(Mh, M1), sig);
+  const float Ms = (M == kNegInf) ? 0.f : M;
+  const float f0 = fast_exp2(Mh - Ms), f1 = fast_exp2(M1 - Ms);  // 0 for an empty half
+  float L = lh * f0 + l1 * f1;
+  if (sink) L += fast_exp2(sig - Ms);
+  const bool any = L > 0.f;
+  const float inv = any ? 1.f / L : 0.f;
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = (acc[e] * f0 + s_acc[slot][lane * EPL + e] * f1) * inv;
+  if constexpr (BF16OUT) {
+    uint16_t* dst = (uint16_t*)out + (size_t)row * DV + lane * EPL;
+    if constexpr (EPL == 1)
+      dst[0] = to_bf16(o[0]);
+    else
+      *(uint32_t*)dst = pack_bf16(o[0], o[1]);
+  } else {
+    float* dst = (float*)out + (size_t)row * DV + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = o[e];
+  }
+  if (lse && lane == 0) lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
+}
+
 template <int DV>
 hipError_t launch_reduce_dv(const float* po, const float* pm, const float* pl, int P, int rows,
                             int H, const float* sink, void* out, bool bf16, float* lse,
                             hipStream_t s) {
+  if constexpr (DV <= 128) {
+    if (P > 32 && P <= 64) {
+      const int grid2 = (rows + 1) / 2;
+      if (bf16)
+        hipLaunchKernelGGL((splitk_reduce_pair_kernel<DV, true>), dim3(grid2), dim3(kThreads), 0,
+                           s, po, pm, pl, P, rows, H, sink, out, lse);
+      else
+        hipLaunchKernelGGL((splitk_reduce_pair_kernel<DV, false>), dim3(grid2), dim3(kThreads), 0,
+                           s, po, pm, pl, P, rows, H, sink, out, lse);
+      return hipGetLastError();
+    }
+  }
   const int grid = (rows + kWaves - 1) / kWaves;
   if (bf16)
     hipLaunchKernelGGL((splitk_reduce_kernel<DV, true>), dim3(grid), dim3(kThreads), 0, s, po,

@@ -103,13 +103,20 @@ def test_partials_plus_reduce_equals_decode_attention():
     assert torch.equal(lse.view(-1), lse2)
 
 
-def test_splitk_reduce_on_oracle_partials():
+@pytest.mark.parametrize("case", [
+    # (P, C, batch, heads, kv heads, depth, S): partitions past a row's keys are empty
+    (6, 16, 3, 4, 2, 64, 90),
+    (40, 4, 3, 3, 1, 64, 90),     # 33..64 partitions: two waves per row; second half empty
+    (64, 2, 3, 4, 2, 128, 90),    # ... the second half partly empty, 128 columns
+    (33, 3, 5, 3, 1, 128, 100),   # ... one partition in the second half, odd row count
+], ids=lambda c: "P%d_C%d_rows%d_dv%d" % (c[0], c[1], c[2] * c[3], c[5]))
+def test_splitk_reduce_on_oracle_partials(case):
     """splitk_reduce fed with partials made by the oracle matches the oracle merge."""
     from oracle import oracle as O
-    wl = W.Workload("reduce_src", 8601, batch=3, num_heads=4, kv_heads=2, depth=64,
-                    max_seq_len=90, ragged=(0, 90, 1), dtype="f32", sink=True)
+    P, C, B, H, KVH, D, S = case
+    wl = W.Workload("reduce_src", 8601 + P, batch=B, num_heads=H, kv_heads=KVH, depth=D,
+                    max_seq_len=S, ragged=(0, S, 1), dtype="f32", sink=True)
     inp = W.make_inputs(wl)
-    P, C = 6, 16
     po, pm, pl = O.partials(inp.q, inp.k, inp.v, scale=wl.softmax_scale, num_partitions=P,
                             keys_per_partition=C, valid_length=inp.valid_length)
     ref_out, ref_lse = O.merge(po, pm, pl, num_heads=wl.num_heads, sink=inp.sink)

@@ -21,7 +21,9 @@
  *     heads that share one KV head ("mha_sm100_dispatch", Parameters `group`).
  *   - Keys visible to row (b, t): N_b = valid_length[b] if given, else
  *     max_seq_len ("mha_sm100_dispatch", Args `valid_length`,
- *     `max_cache_valid_length_arg`).  N_b counts the current tokens too.  With
+ *     `max_cache_valid_length_arg`: the latter bounds the former), and a
+ *     length above max_seq_len counts as max_seq_len.  N_b counts the current
+ *     tokens too.  With
  *     the causal mask, token t of T sees keys j <= N_b - T + t (bottom-right
  *     aligned; the MTP tokens are the last T positions).
  *   - MLA ("flare_mla_decoding_dispatch", Args `k`): V is K[..., :depth_v];
@@ -41,6 +43,12 @@
  *     position), so a causal mask together with indices is rejected.  A count
  *     outside [0, indices_stride] or a counted index outside [0, pool_rows) is
  *     an invalid call.  Partition p covers list positions [p*C, (p+1)*C).
+ *   - Ragged KV layout ("mha_sm100_dispatch", Args `kv_input_row_offsets`;
+ *     "flare_mla_decoding_dispatch", Args `kv_input_row_offsets`: per-batch row
+ *     offsets into a ragged KV layout): the caches of all sequences are
+ *     concatenated into one cache [pool_rows, KVH, D], and key j of sequence b
+ *     is its row kv_offsets[b] + j.  N_b and the mask are as above.  A
+ *     sequence whose N_b keys would reach past the cache is an invalid call.
  *   - Split-K ("mha_decoding_single_batch_pipelined", description: the keys
  *     are cut into consecutive ranges, one per block, whose max and exp-sum a
  *     separate merge pass combines): partition p covers
@@ -99,6 +107,8 @@ typedef struct {
   const uint32_t* page_table; /* [B, max_pages] or NULL (contiguous)            */
   int page_size, max_pages;
   const uint32_t* valid_length; /* [B] or NULL                                  */
+  const uint32_t* kv_offsets; /* ragged KV layout: key j of sequence b is row kv_offsets[b] + j
+                                 of a cache [pool_rows, KVH, D]; NULL otherwise   */
   int B, T, H, KVH, D, Dv, S;
   double scale;
   const float* sink;          /* [H] or NULL                                    */
@@ -109,7 +119,7 @@ typedef struct {
   const int32_t* indices;     /* sparse: [B, indices_stride] pool rows, or NULL       */
   int indices_stride;
   const int32_t* topk_lengths;/* sparse: [B] listed keys of each sequence           */
-  int64_t pool_rows;          /* sparse: rows of the pool k (and v) is               */
+  int64_t pool_rows;          /* sparse or ragged KV layout: rows of the cache k (and v) */
 } problem_t;
 
 /* Query tokens of sequence b, and the q row of its first token. */
@@ -141,6 +151,8 @@ static size_t kv_index(const problem_t* p, int b, int j, int g, int d, int width
   size_t row;
   if (p->indices) {
     row = (size_t)p->indices[(size_t)b * p->indices_stride + (size_t)j];
+  } else if (p->kv_offsets) {
+    row = (size_t)p->kv_offsets[b] + (size_t)j;
   } else if (p->page_table) {
     uint32_t phys = p->page_table[(size_t)b * p->max_pages + (size_t)(j / p->page_size)];
     row = (size_t)phys * p->page_size + (size_t)(j % p->page_size);
@@ -159,10 +171,18 @@ static double value_elem(const problem_t* p, int b, int j, int g, int d) {
   return p->v_scale * elem(p->v, kv_index(p, b, j, g, d, p->Dv), p->kv_dtype);
 }
 
+/* Keys of sequence b before any mask: valid_length[b], or S without it.  A
+ * length above max_seq_len counts as max_seq_len (compared as unsigned: a
+ * uint32 length of 2^31 or more is a large count, not a negative one). */
+static int seq_keys(const problem_t* p, int b) {
+  uint32_t nv = p->valid_length ? p->valid_length[b] : (uint32_t)p->S;
+  return nv < (uint32_t)p->S ? (int)nv : p->S;
+}
+
 /* Number of keys visible to row (b, t). */
 static int visible_keys(const problem_t* p, int b, int t) {
   if (p->indices) return p->topk_lengths[b]; /* sparse: the listed keys, no mask */
-  int n = p->valid_length ? (int)p->valid_length[b] : p->S;
+  int n = seq_keys(p, b);
   if (p->causal) {
     int lim = n - seq_tokens(p, b) + t + 1;
     if (lim < n) n = lim;
@@ -222,9 +242,11 @@ static problem_t make_problem(const void* q, const void* k, const void* v, int d
                               int T, int H, int KVH, int D, int Dv, int S, float scale,
                               const float* sink, int causal, const uint32_t* q_offsets,
                               const int32_t* indices, int indices_stride,
-                              const int32_t* topk_lengths, int64_t pool_rows) {
+                              const int32_t* topk_lengths, int64_t pool_rows,
+                              const uint32_t* kv_offsets) {
   problem_t p;
   p.q_offsets = q_offsets;
+  p.kv_offsets = kv_offsets;
   p.indices = indices; p.indices_stride = indices_stride;
   p.topk_lengths = topk_lengths; p.pool_rows = pool_rows;
   p.q = q; p.k = k; p.v = v;
@@ -249,6 +271,17 @@ static int check_problem(const problem_t* p) {
   if (p->H % p->KVH != 0) return -1;
   if (p->v == NULL && p->Dv > p->D) return -1;
   if (p->page_table && (p->page_size < 1 || p->max_pages < 1)) return -1;
+  if (p->kv_offsets) {
+    if (p->page_table || p->indices || p->pool_rows < 0) return -1;
+    for (int b = 0; b < p->B; ++b) {
+      int64_t most = 0; /* keys of sequence b any of its rows may read */
+      for (int t = 0; t < seq_tokens(p, b); ++t) {
+        int n = visible_keys(p, b, t);
+        if (n > most) most = n;
+      }
+      if ((int64_t)p->kv_offsets[b] + most > p->pool_rows) return -1;
+    }
+  }
   if (p->indices) {
     if (p->causal || p->page_table || !p->topk_lengths || p->indices_stride < 0) return -1;
     for (int b = 0; b < p->B; ++b) {
@@ -266,9 +299,9 @@ static int check_problem(const problem_t* p) {
 static int longest_cache(const problem_t* p) {
   int s = p->S;
   if (p->indices && p->indices_stride > s) s = p->indices_stride;
-  if (p->valid_length)
+  if (!p->indices)
     for (int b = 0; b < p->B; ++b)
-      if ((int)p->valid_length[b] > s) s = (int)p->valid_length[b];
+      if (seq_keys(p, b) > s) s = seq_keys(p, b);
   return s;
 }
 
@@ -283,11 +316,12 @@ int oracle_decode_attention(const void* q, const void* k, const void* v, int dty
                             int Dv, int S, float scale, const float* sink, int causal,
                             const uint32_t* q_offsets, const int32_t* indices,
                             int indices_stride, const int32_t* topk_lengths, int64_t pool_rows,
-                            const int64_t* rows, int64_t num_rows,
+                            const uint32_t* kv_offsets, const int64_t* rows, int64_t num_rows,
                             double* out, double* lse, int num_threads) {
   problem_t p = make_problem(q, k, v, dtype, k_scale, v_scale, page_table, page_size, max_pages,
                              valid_length, B, T, H, KVH, D, Dv, S, scale, sink, causal,
-                             q_offsets, indices, indices_stride, topk_lengths, pool_rows);
+                             q_offsets, indices, indices_stride, topk_lengths, pool_rows,
+                             kv_offsets);
   if (check_problem(&p)) return -1;
   int64_t n_rows = rows ? num_rows : total_tokens(&p) * H;
   int smax = longest_cache(&p);
@@ -329,11 +363,14 @@ int oracle_decode_partials(const void* q, const void* k, const void* v, int dtyp
                            const uint32_t* valid_length, int B, int T, int H, int KVH, int D,
                            int Dv, int S, float scale, int causal, const uint32_t* q_offsets,
                            const int32_t* indices, int indices_stride,
-                           const int32_t* topk_lengths, int64_t pool_rows, int num_partitions, int keys_per_partition, double* part_o,
+                           const int32_t* topk_lengths, int64_t pool_rows,
+                           const uint32_t* kv_offsets, int num_partitions,
+                           int keys_per_partition, double* part_o,
                            double* part_m, double* part_l, int num_threads) {
   problem_t p = make_problem(q, k, v, dtype, k_scale, v_scale, page_table, page_size, max_pages,
                              valid_length, B, T, H, KVH, D, Dv, S, scale, NULL, causal,
-                             q_offsets, indices, indices_stride, topk_lengths, pool_rows);
+                             q_offsets, indices, indices_stride, topk_lengths, pool_rows,
+                             kv_offsets);
   if (check_problem(&p) || num_partitions < 1 || keys_per_partition < 1) return -1;
   int64_t n_rows = total_tokens(&p) * H;
   int64_t n_items = n_rows * num_partitions;

@@ -15,6 +15,10 @@ Array conventions (numpy, C-contiguous):
     lists the pool rows of each sequence's keys, topk_lengths int32 [B] how many
     of them count ("flare_mla_decoding_dispatch", Args ``d_indices``,
     ``indices_stride``, ``topk_lengths``).
+  * ragged KV layout: k (and v) is one cache [rows, KVH, D] holding every
+    sequence's keys; key j of sequence b is row kv_offsets[b] + j (uint32 [B];
+    "mha_sm100_dispatch", Args ``kv_input_row_offsets``); max_seq_len bounds
+    every N_b.
 
 Every routine returns float64 results.  The meaning of each argument and the
 readings taken where the pages are silent are stated in decode_oracle.c.
@@ -49,11 +53,11 @@ def _bind(lib):
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.oracle_decode_attention.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, i32, vp, i32, i32,
                                             i32, i32, i32, i32, i32, f32, vp, i32, vp, vp, i32, vp,
-                                            i64, vp, i64, vp, vp, i32]
+                                            i64, vp, vp, i64, vp, vp, i32]
     lib.oracle_decode_attention.restype = i32
     lib.oracle_decode_partials.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, i32, vp, i32, i32,
                                            i32, i32, i32, i32, i32, f32, i32, vp, vp, i32, vp, i64,
-                                           i32, i32, vp, vp, vp, i32]
+                                           vp, i32, i32, vp, vp, vp, i32]
     lib.oracle_decode_partials.restype = i32
     lib.oracle_splitk_merge.argtypes = [vp, vp, vp, i32, i64, i32, i32, vp, vp, vp]
     lib.oracle_splitk_merge.restype = i32
@@ -158,9 +162,27 @@ def _sparse(k, v, indices, topk_lengths, batch):
     return k4, v4, idx, tl, idx.shape[1], k.shape[0]
 
 
+def _ragged_kv(k, v, kv_offsets, max_seq_len, batch):
+    """Ragged KV layout: the cache [rows, KVH, D] as [rows, 1, KVH, D] for the shape
+    checks, the offsets [B], the row count and the key bound S."""
+    if kv_offsets is None:
+        return k, v, None, 0, max_seq_len
+    k = np.asarray(k)
+    if k.ndim != 3 or (v is not None and np.asarray(v).ndim != 3):
+        raise ValueError("ragged KV layout: k (and v) must be caches [rows, KVH, D]")
+    off = np.ascontiguousarray(kv_offsets, dtype=np.uint32)
+    if off.shape != (batch,) or max_seq_len is None:
+        raise ValueError("ragged KV layout: kv_offsets [B] and max_seq_len are required")
+    k4 = k.reshape(k.shape[0], 1, *k.shape[1:])
+    v4 = None if v is None else np.asarray(v).reshape(np.asarray(v).shape[0], 1,
+                                                      *np.asarray(v).shape[1:])
+    return k4, v4, off, k.shape[0], int(max_seq_len)
+
+
 def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=None,
               causal=False, depth_v=None, max_seq_len=None, rows=None, threads=0, lib=None,
-              k_scale=1.0, v_scale=1.0, q_offsets=None, indices=None, topk_lengths=None):
+              k_scale=1.0, v_scale=1.0, q_offsets=None, indices=None, topk_lengths=None,
+              kv_offsets=None):
     """Reference attention.  Returns (out, lse) as float64.
 
     q_offsets: ragged q -- q is [total, H, D] and the tokens of sequence b are rows
@@ -172,18 +194,24 @@ def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=N
     indices / topk_lengths: sparse top-k -- k (and v) is a pool [pool_rows, KVH, D] and
     the keys of sequence b are its rows indices[b, :topk_lengths[b]] (no mask).
 
+    kv_offsets: ragged KV layout -- k (and v) is a cache [rows, KVH, D] and key j of
+    sequence b is its row kv_offsets[b] + j (max_seq_len required).
+
     With rows=None: out [B, T, H, Dv], lse [B, T, H].  With rows (int64 row ids
     (b*T + t)*H + h): out [len(rows), Dv], lse [len(rows)].
     """
     lib = lib or load_library()
     q, qo, rB, rT = _ragged(q, q_offsets)
-    k, v, idx, tl, stride, pool_rows = _sparse(k, v, indices, topk_lengths,
-                                               rB if qo is not None else np.shape(q)[0])
+    nb = rB if qo is not None else np.shape(q)[0]
+    k, v, idx, tl, stride, pool_rows = _sparse(k, v, indices, topk_lengths, nb)
+    k, v, kvo, kv_rows, S_kv = _ragged_kv(k, v, kv_offsets, max_seq_len, nb)
     q, k, v, page_table, valid_length, sink, code, dims = _common(
-        q, k, v, page_table, valid_length, sink, depth_v, max_seq_len)
+        q, k, v, page_table, valid_length, sink, depth_v, None if kvo is not None else max_seq_len)
     B, T, H, KVH, D, Dv, S, page_size, max_pages = dims
     if idx is not None:
         S = stride
+    if kvo is not None:
+        S, pool_rows = S_kv, kv_rows
     total = q.shape[0] * q.shape[1]
     if qo is not None:
         B, T = rB, rT
@@ -198,7 +226,7 @@ def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=N
                                      float(v_scale), _ptr(page_table), page_size,
                                      max_pages, _ptr(valid_length), B, T, H, KVH, D, Dv, S,
                                      float(scale), _ptr(sink), int(bool(causal)), _ptr(qo),
-                                     _ptr(idx), stride, _ptr(tl), pool_rows, _ptr(rows), n,
+                                     _ptr(idx), stride, _ptr(tl), pool_rows, _ptr(kvo), _ptr(rows), n,
                                      _ptr(out), _ptr(lse), int(threads))
     if rc != 0:
         raise RuntimeError(f"oracle_decode_attention failed ({rc})")
@@ -212,18 +240,21 @@ def attention(q, k, v=None, *, scale, page_table=None, valid_length=None, sink=N
 def partials(q, k, v=None, *, scale, num_partitions, keys_per_partition, page_table=None,
              valid_length=None, causal=False, depth_v=None, max_seq_len=None, threads=0,
              lib=None, k_scale=1.0, v_scale=1.0, q_offsets=None, indices=None,
-             topk_lengths=None):
+             topk_lengths=None, kv_offsets=None):
     """Split-K partials.  Returns (O_p [P, rows, Dv], m_p [P, rows], l_p [P, rows]) with
     rows = (q tokens) * H.  Sparse: partition p covers list positions [p*C, (p+1)*C)."""
     lib = lib or load_library()
     q, qo, rB, rT = _ragged(q, q_offsets)
-    k, v, idx, tl, stride, pool_rows = _sparse(k, v, indices, topk_lengths,
-                                               rB if qo is not None else np.shape(q)[0])
+    nb = rB if qo is not None else np.shape(q)[0]
+    k, v, idx, tl, stride, pool_rows = _sparse(k, v, indices, topk_lengths, nb)
+    k, v, kvo, kv_rows, S_kv = _ragged_kv(k, v, kv_offsets, max_seq_len, nb)
     q, k, v, page_table, valid_length, _, code, dims = _common(
-        q, k, v, page_table, valid_length, None, depth_v, max_seq_len)
+        q, k, v, page_table, valid_length, None, depth_v, None if kvo is not None else max_seq_len)
     B, T, H, KVH, D, Dv, S, page_size, max_pages = dims
     if idx is not None:
         S = stride
+    if kvo is not None:
+        S, pool_rows = S_kv, kv_rows
     if qo is not None:
         B, T = rB, rT
     rows = q.shape[0] * q.shape[1] * H
@@ -234,7 +265,7 @@ def partials(q, k, v=None, *, scale, num_partitions, keys_per_partition, page_ta
                                     float(v_scale), _ptr(page_table), page_size,
                                     max_pages, _ptr(valid_length), B, T, H, KVH, D, Dv, S,
                                     float(scale), int(bool(causal)), _ptr(qo), _ptr(idx), stride,
-                                    _ptr(tl), pool_rows, int(num_partitions),
+                                    _ptr(tl), pool_rows, _ptr(kvo), int(num_partitions),
                                     int(keys_per_partition), _ptr(po), _ptr(pm), _ptr(pl),
                                     int(threads))
     if rc != 0:

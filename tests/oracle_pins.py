@@ -373,6 +373,82 @@ def pin_nan_poison_past_valid_length(lib):
     _close(got[1], ref[1], tol=0, what="lse")
 
 
+def pin_sdpa_valid_length_above_max_seq_len(lib):
+    """A length above max_seq_len counts as max_seq_len (the key bound of
+    "mha_sm100_dispatch", Args `max_cache_valid_length_arg`, caps Args
+    `valid_length`), also a uint32 length of 2^31 or more: torch SDPA over the
+    first S keys, dense and paged, causal and not."""
+    rng = _rng(40)
+    B, T, H, KVH, D, S, ps = 3, 2, 4, 2, 8, 12, 4
+    q, k, v = (_randn(rng, (B, T, H, D)), _randn(rng, (B, S, KVH, D)),
+               _randn(rng, (B, S, KVH, D)))
+    over = np.array([S + 5, 0xFFFFFFFF, 7], np.uint32)
+    capped = np.array([S, S, 7], np.uint32)
+    kp, vp, table = _paged_from_contiguous(rng, k, v, capped, ps, extra_pages=0)
+    for causal in (False, True):
+        vis = _visible(capped, T, S, causal)
+        allowed = np.broadcast_to(vis[:, None], (B, H, T, S)).copy()
+        ro, rl = _sdpa(q, _expand_heads(k, 2), _expand_heads(v, 2), 0.5, allowed=allowed)
+        out, lse = O.attention(q, k, v, scale=0.5, valid_length=over, causal=causal, lib=lib)
+        _close(out, ro, what=f"dense out causal={causal}")
+        _close(lse, rl, what=f"dense lse causal={causal}")
+        out, lse = O.attention(q, kp, vp, scale=0.5, valid_length=over, causal=causal,
+                               page_table=table, max_seq_len=S, lib=lib)
+        _close(out, ro, what=f"paged out causal={causal}")
+        _close(lse, rl, what=f"paged lse causal={causal}")
+
+
+def _concat_cache(rng, k, v, lens, gap=2):
+    """The ragged KV layout of a dense cache: the sequences' valid rows in a shuffled
+    order in one cache [rows, KVH, D], NaN rows between and after them (enough
+    that a misplaced row read stays inside the array)."""
+    B, S = k.shape[:2]
+    total = gap + sum(int(n) + gap for n in lens) + B * S + 1
+    kc = np.full((total,) + k.shape[2:], np.nan, np.float32)
+    vc = None if v is None else np.full((total,) + v.shape[2:], np.nan, np.float32)
+    offs = np.zeros(B, np.uint32)
+    pos = gap
+    for b in rng.permutation(B):
+        n = int(lens[b])
+        offs[b] = pos
+        kc[pos:pos + n] = k[b, :n]
+        if v is not None:
+            vc[pos:pos + n] = v[b, :n]
+        pos += n + gap
+    return kc, vc, offs
+
+
+def pin_ragged_kv_layout_equals_dense(lib):
+    """Per-sequence row offsets into one concatenated cache ("mha_sm100_dispatch",
+    Args `kv_input_row_offsets`) give the dense call over the same rows, bit for bit:
+    GQA causal with a sink, its split-K partials, and MLA (V = K[..., :Dv])."""
+    rng = _rng(41)
+    B, T, H, KVH, D, S = 3, 2, 4, 2, 8, 11
+    q, k, v = (_randn(rng, (B, T, H, D)), _randn(rng, (B, S, KVH, D)),
+               _randn(rng, (B, S, KVH, D)))
+    lens = np.array([11, 4, 1], np.uint32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    kc, vc, offs = _concat_cache(rng, k, v, lens)
+    kw = dict(scale=0.5, valid_length=lens, causal=True, lib=lib)
+    ref = O.attention(q, k, v, sink=sink, **kw)
+    got = O.attention(q, kc, vc, sink=sink, kv_offsets=offs, max_seq_len=S, **kw)
+    _close(got[0], ref[0], tol=0, what="out")
+    _close(got[1], ref[1], tol=0, what="lse")
+    for P, C in ((2, 6), (3, 4)):
+        a = O.partials(q, k, v, num_partitions=P, keys_per_partition=C, **kw)
+        b = O.partials(q, kc, vc, num_partitions=P, keys_per_partition=C, kv_offsets=offs,
+                       max_seq_len=S, **kw)
+        for x, y, name in zip(a, b, ("O_p", "m_p", "l_p")):
+            _close(y, x, tol=0, what=f"{name} P={P}")
+    q1, kv = _randn(rng, (B, 1, 8, 10)), _randn(rng, (B, S, 1, 10))
+    kc1, _, offs1 = _concat_cache(rng, kv, None, lens)
+    ref = O.attention(q1, kv, None, depth_v=6, scale=0.4, valid_length=lens, lib=lib)
+    got = O.attention(q1, kc1, None, depth_v=6, scale=0.4, valid_length=lens, kv_offsets=offs1,
+                      max_seq_len=S, lib=lib)
+    _close(got[0], ref[0], tol=0, what="mla out")
+    _close(got[1], ref[1], tol=0, what="mla lse")
+
+
 def pin_causal_rows_are_shorter_rows(lib):
     """Token t of T under the causal mask = a single-token row over N - T + t + 1 keys."""
     rng = _rng(18)

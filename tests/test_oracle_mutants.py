@@ -22,8 +22,20 @@ MUTANTS = [
     ("causal_top_left", "int lim = n - seq_tokens(p, b) + t + 1;", "int lim = t + 1;"),
     ("scale_dropped", "s[j - lo] = p->scale * dot;", "s[j - lo] = dot;"),
     ("scale_squared", "s[j - lo] = p->scale * dot;", "s[j - lo] = p->scale * p->scale * dot;"),
-    ("valid_length_ignored", "int n = p->valid_length ? (int)p->valid_length[b] : p->S;",
-     "int n = p->S;"),
+    ("valid_length_ignored",
+     "uint32_t nv = p->valid_length ? p->valid_length[b] : (uint32_t)p->S;",
+     "uint32_t nv = (uint32_t)p->S;"),
+    ("valid_length_not_capped", "return nv < (uint32_t)p->S ? (int)nv : p->S;",
+     "return (int)nv;"),
+    ("valid_length_capped_signed", "return nv < (uint32_t)p->S ? (int)nv : p->S;",
+     "return (int)nv < p->S ? (int)nv : p->S;"),
+    # ragged KV layout (per-sequence row offsets into one cache)
+    ("kv_offsets_ignored", "row = (size_t)p->kv_offsets[b] + (size_t)j;",
+     "row = (size_t)b * p->S + (size_t)j;"),
+    ("kv_offsets_off_by_one", "row = (size_t)p->kv_offsets[b] + (size_t)j;",
+     "row = (size_t)p->kv_offsets[b] + (size_t)j + 1;"),
+    ("kv_offsets_of_next_sequence", "row = (size_t)p->kv_offsets[b] + (size_t)j;",
+     "row = (size_t)p->kv_offsets[(b + 1) % p->B] + (size_t)j;"),
     ("sink_scaled", "(double)p->sink[h] : -INFINITY;", "p->scale * (double)p->sink[h] : -INFINITY;"),
     ("sink_not_in_denominator", "if (sigma != -INFINITY) l += exp(sigma - m);",
      "if (sigma != -INFINITY) l += 0.0;"),

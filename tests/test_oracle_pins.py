@@ -33,3 +33,23 @@ def test_sparse_contract_violations_rejected():
     bad_idx[1, 2] = -1  # past the count of 2: not part of the call
     bad_idx[1, 3] = 99
     O.attention(q, pool, pool, **dict(ok, indices=bad_idx))
+
+
+def test_ragged_kv_layout_contract_violations_rejected():
+    """The oracle refuses a ragged KV layout whose sequence would read past the cache,
+    or that is combined with a page table or a sparse list."""
+    import numpy as np
+
+    from oracle import oracle as O
+
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 1, 2, 8)).astype(np.float32)
+    cache = rng.standard_normal((20, 1, 8)).astype(np.float32)
+    lens = np.array([5, 7], np.uint32)
+    ok = dict(scale=0.5, valid_length=lens, max_seq_len=8)
+    O.attention(q, cache, cache, kv_offsets=np.array([0, 13], np.uint32), **ok)
+    with pytest.raises(RuntimeError):  # rows 14 .. 20 of a 20-row cache
+        O.attention(q, cache, cache, kv_offsets=np.array([0, 14], np.uint32), **ok)
+    with pytest.raises(RuntimeError):  # no valid_length: 8 keys each
+        O.attention(q, cache, cache, kv_offsets=np.array([0, 13], np.uint32), scale=0.5,
+                    max_seq_len=8)

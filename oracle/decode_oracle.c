@@ -86,9 +86,22 @@ static double e4m3_value(uint8_t c) {
   return sign ? -mag : mag;
 }
 
+/* e4m3_value of every code, filled once (by the first call that needs it). */
+static double e4m3_table[256];
+static int e4m3_table_ready = 0;
+
+static void fill_e4m3_table(void) {
+#pragma omp critical(oracle_e4m3_table)
+  if (!e4m3_table_ready) {
+    for (int c = 0; c < 256; ++c) e4m3_table[c] = e4m3_value((uint8_t)c);
+#pragma omp flush
+    e4m3_table_ready = 1;
+  }
+}
+
 static double elem(const void* base, size_t idx, int dtype) {
   if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
-  if (dtype == ORACLE_E4M3) return e4m3_value(((const uint8_t*)base)[idx]);
+  if (dtype == ORACLE_E4M3) return e4m3_table[((const uint8_t*)base)[idx]];
   uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
@@ -257,6 +270,7 @@ static problem_t make_problem(const void* q, const void* k, const void* v, int d
   p.valid_length = valid_length;
   p.B = B; p.T = T; p.H = H; p.KVH = KVH; p.D = D; p.Dv = Dv; p.S = S;
   p.scale = (double)scale; p.sink = sink; p.causal = causal;
+  if (p.kv_dtype == ORACLE_E4M3) fill_e4m3_table();
   return p;
 }
 

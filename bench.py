@@ -4,13 +4,17 @@
 A step is one full decode-attention pass (every kernel of the call: the
 partition pass and, when the keys are split, the log-sum-exp merge) over one
 batch of synthetic inputs already resident in HBM.  The default workload is the
-GQA decode problem (batch 32, 32 query / 8 KV heads, depth 128, 4096 keys per
-sequence, bf16).  Prints one JSON line.
+largest configured problem: ragged paged decode (batch 64, 64 query / 8 KV heads,
+depth 128, bf16, lengths uniform in [1, 32768] with four set to 1, 128-key pages
+placed by a seeded permutation of one pool; 3.69 GB of KV per step).  Prints one
+JSON line.
 
   value      = algorithmic KV bytes per step / time per step  (GB/s)
   roofline   = the partition-pass kernel alone: the same bytes / its average
                HIP-event duration, against the 8 TB/s HBM peak
   cpu_baseline = the fp64 CPU oracle on this host, on a bounded sample
+  step_us    = the distribution of single steps (median, p10, p90), each timed
+               between its own pair of HIP events in a separate pass
 
 Input sets are rotated so that consecutive steps never find their KV cache in
 the 256 MB last-level cache.
@@ -135,7 +139,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gqa")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="paged")
     ap.add_argument("--partitions", type=int, default=0, help="0 = library heuristic")
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -376,6 +380,23 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     kern_avg_ms = ev0.elapsed_time(ev1) / K
+
+    # The step distribution: a separate pass of K steps, each between its own pair of
+    # events (the pairs add idle time between steps, which is why the headline above
+    # times the steps back to back).
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(K)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(pairs):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    step_us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+
+    def pct(q):
+        return round(step_us[min(len(step_us) - 1, int(q * (len(step_us) - 1) + 0.5))], 2)
+
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     # The roofline of the dominant kernel is the tighter of its two bounds: the KV
     # bytes at the HBM peak, or (bf16 matrix-core kernels) its flops at the MFMA peak.
@@ -401,6 +422,9 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "us_per_step_device": round(ev_ms_per_step * 1e3, 2),
+        "step_us": {"p10": pct(0.10), "median": pct(0.50), "p90": pct(0.90),
+                    "min": round(step_us[0], 2), "max": round(step_us[-1], 2),
+                    "method": f"{K} steps, each between its own pair of HIP events"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",

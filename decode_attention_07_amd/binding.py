@@ -29,7 +29,8 @@ EXPORTS = ("decode_attention_status_string", "decode_num_partitions", "decode_wo
            "decode_attention_fp8kv", "decode_attention_fp8kv_partials", "mla_decode_ragged",
            "decode_attention_partials", "mla_decode", "mla_decode_partials", "mla_decode_fp8kv",
            "mla_decode_fp8kv_partials", "mla_decode_sparse",
-           "mla_decode_sparse_partials", "mla_sparse_num_partitions", "splitk_reduce")
+           "mla_decode_sparse_partials", "mla_sparse_num_partitions", "splitk_reduce",
+           "decode_attention_ragged_kv", "mla_decode_ragged_kv")
 
 _lock = threading.Lock()
 _lib = None
@@ -94,6 +95,12 @@ def _declare(lib):
     lib.mla_sparse_num_partitions.restype = i32
     lib.splitk_reduce.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, vp, vp]
     lib.splitk_reduce.restype = i32
+    lib.decode_attention_ragged_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                               f32, i32, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.decode_attention_ragged_kv.restype = i32
+    lib.mla_decode_ragged_kv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, i32,
+                                         vp, vp, vp, sz, vp]
+    lib.mla_decode_ragged_kv.restype = i32
     return lib
 
 
@@ -163,17 +170,43 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
 
 
-def _need(t, name, dims=None, dtype=None):
+def _need(t, name, dims=None, dtype=None, shape=None, device=None):
+    """Checks an array argument; None passes: dimensions, shape, dtype, contiguity
+    and (given `device`) the device it shares with the call's other arrays."""
     if t is None:
         return
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA/HIP tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
     if dims is not None and t.dim() != dims:
         raise ValueError(f"{name} must have {dims} dimensions, got {tuple(t.shape)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if dtype is not None and t.dtype not in dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _need_cuda(t, name):
+    """The call's anchor tensor (every other array was checked to share its
+    device) must live on a GPU: checked after the shapes."""
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA/HIP tensor")
+
+
+def _need_outputs(out, lse, out_shape, out_dtype, lse_shape, device):
+    """Caller-supplied out / lse: exact shape, the output dtype / float32, contiguous,
+    on the inputs' device."""
+    _need(out, "out", dtype=(out_dtype,), shape=out_shape, device=device)
+    _need(lse, "lse", dtype=(torch.float32,), shape=lse_shape, device=device)
+
+
+def _need_per_sequence(valid_length, sink_weights, batch, num_q_heads, device):
+    _need(valid_length, "valid_length", 1, _U32, shape=(batch,), device=device)
+    _need(sink_weights, "sink_weights", 1, (torch.float32,), shape=(num_q_heads,),
+          device=device)
 
 
 _U32 = (torch.int32, torch.uint32)
@@ -213,8 +246,11 @@ def workspace_views(workspace: torch.Tensor, num_partitions, batch, q_len, num_q
 
 
 def _cache_geometry(q, k, page_table, max_seq_len, batch=None):
+    nb = q.shape[0] if batch is None else batch
     if page_table is not None:
-        _need(page_table, "page_table", 2, _U32)
+        _need(page_table, "page_table", 2, _U32, device=q.device)
+        if page_table.shape[0] < nb:
+            raise ValueError(f"page_table has {page_table.shape[0]} rows for {nb} sequences")
         page_size, max_pages = k.shape[1], page_table.shape[1]
         S = page_size * max_pages if max_seq_len is None else int(max_seq_len)
     else:
@@ -234,14 +270,52 @@ def _resolve_partitions(num_parts, batch, T, H, KVH, D, Dv, S, ragged):
 
 
 def _workspace(workspace, P, B, T, H, Dv, device, always=False):
+    if workspace is not None:
+        _need(workspace, "workspace", device=device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     need = decode_workspace_size(P, B, T, H, Dv)
     if P == 1 and not always:
-        return workspace, (0 if workspace is None else workspace.numel())
+        return workspace, nbytes
     if workspace is None:  # zero-filled: the work-queue word starts at 0
         workspace = torch.zeros(need, dtype=torch.uint8, device=device)
-    elif workspace.numel() < need:
-        raise ValueError(f"workspace has {workspace.numel()} bytes, needs {need}")
-    return workspace, workspace.numel()
+        nbytes = need
+    elif nbytes < need:
+        raise ValueError(f"workspace has {nbytes} bytes, needs {need}")
+    return workspace, nbytes
+
+
+def _kv_like(k, v):
+    """v must match k's shape (the V cache mirrors the K cache's layout)."""
+    if v is not None and tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v has shape {tuple(v.shape)}, k {tuple(k.shape)}")
+
+
+def _mha_inputs(q, k, v, group, kv_dims=4, kv_dtype=None):
+    """q, k, v of a GQA call: shapes, dtypes, one device.  Returns the dtype code."""
+    qd = q.dim() if isinstance(q, torch.Tensor) else None
+    _need(q, "q", qd if qd in (3, 4) else 4, (torch.bfloat16,) if kv_dtype else None)
+    _need(k, "k", kv_dims, kv_dtype, device=q.device)
+    _need(v, "v", kv_dims, kv_dtype, device=q.device)
+    _kv_like(k, v)
+    dt = _dtype_code(q)
+    if kv_dtype is None and (k.dtype != q.dtype or v.dtype != q.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    D, H = q.shape[-1], q.shape[-2]
+    if group < 1 or H % group or k.shape[-1] != D or k.shape[-2] * group != H:
+        raise ValueError("k/v shape does not match q and group")
+    return dt
+
+
+def _mla_inputs(q, kv, kv_dims=4, kv_dtype=(torch.bfloat16,)):
+    qd = q.dim() if isinstance(q, torch.Tensor) else None
+    _need(q, "q", qd if qd in (3, 4) else 4, (torch.bfloat16,))
+    _need(kv, "kv", kv_dims, kv_dtype, device=q.device)
+    if q.shape[-1] != MLA_DEPTH or kv.shape[-1] != MLA_DEPTH or kv.shape[-2] != 1:
+        raise ValueError("MLA needs q [..., 576] and kv [..., 1, 576]")
+
+
+def _mask(causal):
+    return DA_MASK_CAUSAL if causal else DA_MASK_NONE
 
 
 def decode_attention(q, k, v, *, group, scale, page_table=None, valid_length=None,
@@ -250,18 +324,12 @@ def decode_attention(q, k, v, *, group, scale, page_table=None, valid_length=Non
                      prepare=False):
     """GQA/MHA decode attention.  Returns (out [B,T,H,D], lse [B,T,H] or None);
     with prepare=True, a BoundCall that enqueues this call and returns them."""
-    _need(q, "q", 4)
-    _need(k, "k", 4)
-    _need(v, "v", 4)
-    _need(valid_length, "valid_length", 1, _U32)
-    _need(sink_weights, "sink_weights", 1, (torch.float32,))
-    dt = _dtype_code(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
+    dt = _mha_inputs(q, k, v, group)
     B, T, H, D = q.shape
-    if k.shape[3] != D or v.shape[3] != D or k.shape[2] * group != H:
-        raise ValueError("k/v shape does not match q and group")
+    _need_per_sequence(valid_length, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (B, T, H, D), q.dtype, (B, T, H), q.device)
     page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len)
+    _need_cuda(q, "q")
     P = _resolve_partitions(num_partitions, B, T, H, H // group, D, D, S,
                             valid_length is not None)
     if out is None:
@@ -271,8 +339,7 @@ def decode_attention(q, k, v, *, group, scale, page_table=None, valid_length=Non
     workspace, wbytes = _workspace(workspace, P, B, T, H, D, q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(page_table), page_size, max_pages,
             _ptr(valid_length), B, T, H, group, D, S, float(scale), P, _ptr(sink_weights),
-            DA_MASK_CAUSAL if causal else DA_MASK_NONE, dt, _ptr(out), _ptr(lse),
-            _ptr(workspace), wbytes, _stream(stream))
+            _mask(causal), dt, _ptr(out), _ptr(lse), _ptr(workspace), wbytes, _stream(stream))
     return _finish(library().decode_attention, args, "decode_attention", (out, lse),
                    (q, k, v, page_table, valid_length, sink_weights, out, lse, workspace),
                    prepare)
@@ -283,26 +350,23 @@ def decode_attention_partials(q, k, v, *, group, scale, num_partitions, page_tab
                               stream=None, prepare=False):
     """Partition pass only.  Returns the workspace (uint8 tensor, header layout), or
     with prepare=True a BoundCall that enqueues the pass and returns it."""
-    _need(q, "q", 4)
-    _need(k, "k", 4)
-    _need(v, "v", 4)
-    _need(valid_length, "valid_length", 1, _U32)
-    dt = _dtype_code(q)
+    dt = _mha_inputs(q, k, v, group)
     B, T, H, D = q.shape
+    _need_per_sequence(valid_length, None, B, H, q.device)
     page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len)
+    _need_cuda(q, "q")
     P = int(num_partitions)
     workspace, wbytes = _workspace(workspace, P, B, T, H, D, q.device, always=True)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(page_table), page_size, max_pages,
-            _ptr(valid_length), B, T, H, group, D, S, float(scale), P,
-            DA_MASK_CAUSAL if causal else DA_MASK_NONE, dt, _ptr(workspace), wbytes,
-            _stream(stream))
+            _ptr(valid_length), B, T, H, group, D, S, float(scale), P, _mask(causal), dt,
+            _ptr(workspace), wbytes, _stream(stream))
     return _finish(library().decode_attention_partials, args, "decode_attention_partials",
                    workspace, (q, k, v, page_table, valid_length, workspace), prepare)
 
 
 def _ragged_q(q, q_offsets, max_q_len):
     _need(q, "q", 3)
-    _need(q_offsets, "q_offsets", 1, _U32)
+    _need(q_offsets, "q_offsets", 1, _U32, device=q.device)
     if q_offsets is None or q_offsets.shape[0] < 1:
         raise ValueError("q_offsets [batch + 1] is required")
     if max_q_len is None or int(max_q_len) < 1:
@@ -317,17 +381,12 @@ def decode_attention_ragged(q, q_offsets, k, v, *, max_q_len, group, scale, page
     """GQA/MHA decode with a ragged q [total, H, D]: the tokens of sequence b are rows
     q_offsets[b] .. q_offsets[b+1].  Returns (out [total, H, D], lse [total, H])."""
     B, Tm = _ragged_q(q, q_offsets, max_q_len)
-    _need(k, "k", 4)
-    _need(v, "v", 4)
-    _need(valid_length, "valid_length", 1, _U32)
-    _need(sink_weights, "sink_weights", 1, (torch.float32,))
-    dt = _dtype_code(q)
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise TypeError("q, k, v must share a dtype")
+    dt = _mha_inputs(q, k, v, group)
     total, H, D = q.shape
-    if k.shape[3] != D or v.shape[3] != D or k.shape[2] * group != H:
-        raise ValueError("k/v shape does not match q and group")
+    _need_per_sequence(valid_length, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (total, H, D), q.dtype, (total, H), q.device)
     page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len, batch=B)
+    _need_cuda(q, "q")
     P = _resolve_partitions(num_partitions, B, Tm, H, H // group, D, D, S,
                             valid_length is not None)
     if out is None:
@@ -337,8 +396,8 @@ def decode_attention_ragged(q, q_offsets, k, v, *, max_q_len, group, scale, page
     workspace, wbytes = _workspace(workspace, P, 1, total, H, D, q.device)
     args = (_ptr(q), _ptr(q_offsets), total, Tm, _ptr(k), _ptr(v), _ptr(page_table), page_size,
             max_pages, _ptr(valid_length), B, H, group, D, S, float(scale), P,
-            _ptr(sink_weights), DA_MASK_CAUSAL if causal else DA_MASK_NONE, dt, _ptr(out),
-            _ptr(lse), _ptr(workspace), wbytes, _stream(stream))
+            _ptr(sink_weights), _mask(causal), dt, _ptr(out), _ptr(lse), _ptr(workspace),
+            wbytes, _stream(stream))
     return _finish(library().decode_attention_ragged, args, "decode_attention_ragged",
                    (out, lse), (q, q_offsets, k, v, page_table, valid_length, sink_weights, out,
                                 lse, workspace), prepare)
@@ -351,14 +410,12 @@ def mla_decode_ragged(q, q_offsets, kv, *, max_q_len, scale, page_table=None,
     """MLA decode with a ragged q [total, H, 576].  Returns (out [total, H, 512],
     lse [total, H])."""
     B, Tm = _ragged_q(q, q_offsets, max_q_len)
-    _need(q, "q", 3, (torch.bfloat16,))
-    _need(kv, "kv", 4, (torch.bfloat16,))
-    _need(valid_length, "valid_length", 1, _U32)
-    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    _mla_inputs(q, kv)
     total, H, D = q.shape
-    if D != MLA_DEPTH or kv.shape[3] != MLA_DEPTH or kv.shape[2] != 1:
-        raise ValueError("MLA needs q [..., 576] and kv [..., 1, 576]")
+    _need_per_sequence(valid_length, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (total, H, MLA_DEPTH_V), q.dtype, (total, H), q.device)
     page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len, batch=B)
+    _need_cuda(q, "q")
     P = _resolve_partitions(num_partitions, B, Tm, H, 1, MLA_DEPTH, MLA_DEPTH_V, S,
                             valid_length is not None)
     if out is None:
@@ -368,11 +425,71 @@ def mla_decode_ragged(q, q_offsets, kv, *, max_q_len, scale, page_table=None,
     workspace, wbytes = _workspace(workspace, P, 1, total, H, MLA_DEPTH_V, q.device)
     args = (_ptr(q), _ptr(q_offsets), total, Tm, _ptr(kv), _ptr(page_table), page_size,
             max_pages, _ptr(valid_length), B, H, S, float(scale), P, _ptr(sink_weights),
-            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(out), _ptr(lse), _ptr(workspace),
-            wbytes, _stream(stream))
+            _mask(causal), _ptr(out), _ptr(lse), _ptr(workspace), wbytes, _stream(stream))
     return _finish(library().mla_decode_ragged, args, "mla_decode_ragged", (out, lse),
                    (q, q_offsets, kv, page_table, valid_length, sink_weights, out, lse,
                     workspace), prepare)
+
+
+def _kv_offsets(kv_row_offsets, batch, device):
+    _need(kv_row_offsets, "kv_row_offsets", 1, _U32, shape=(batch,), device=device)
+    if kv_row_offsets is None and batch > 0:
+        raise ValueError("kv_row_offsets [batch] is required")
+
+
+def decode_attention_ragged_kv(q, k, v, kv_row_offsets, *, group, scale, max_seq_len,
+                               valid_length=None, num_partitions=0, sink_weights=None,
+                               causal=False, out=None, lse=None, workspace=None, stream=None,
+                               want_lse=True, prepare=False):
+    """GQA/MHA decode over a ragged KV layout: k, v are one cache [rows, KVH, D] and key
+    j of sequence b is row kv_row_offsets[b] + j.  Returns (out [B,T,H,D], lse [B,T,H])."""
+    dt = _mha_inputs(q, k, v, group, kv_dims=3)
+    B, T, H, D = q.shape
+    _kv_offsets(kv_row_offsets, B, q.device)
+    _need_per_sequence(valid_length, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (B, T, H, D), q.dtype, (B, T, H), q.device)
+    _need_cuda(q, "q")
+    S = int(max_seq_len)
+    P = _resolve_partitions(num_partitions, B, T, H, H // group, D, D, S,
+                            valid_length is not None)
+    if out is None:
+        out = torch.empty((B, T, H, D), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    workspace, wbytes = _workspace(workspace, P, B, T, H, D, q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(kv_row_offsets), _ptr(valid_length), B, T, H, group,
+            D, S, float(scale), P, _ptr(sink_weights), _mask(causal), dt, _ptr(out), _ptr(lse),
+            _ptr(workspace), wbytes, _stream(stream))
+    return _finish(library().decode_attention_ragged_kv, args, "decode_attention_ragged_kv",
+                   (out, lse), (q, k, v, kv_row_offsets, valid_length, sink_weights, out, lse,
+                                workspace), prepare)
+
+
+def mla_decode_ragged_kv(q, kv, kv_row_offsets, *, scale, max_seq_len, valid_length=None,
+                         num_partitions=0, sink_weights=None, causal=False, out=None, lse=None,
+                         workspace=None, stream=None, want_lse=True, prepare=False):
+    """MLA decode over a ragged KV layout: kv is one cache [rows, 1, 576] and key j of
+    sequence b is row kv_row_offsets[b] + j.  Returns (out [B,T,H,512], lse [B,T,H])."""
+    _mla_inputs(q, kv, kv_dims=3)
+    B, T, H, D = q.shape
+    _kv_offsets(kv_row_offsets, B, q.device)
+    _need_per_sequence(valid_length, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (B, T, H, MLA_DEPTH_V), q.dtype, (B, T, H), q.device)
+    _need_cuda(q, "q")
+    S = int(max_seq_len)
+    P = _resolve_partitions(num_partitions, B, T, H, 1, MLA_DEPTH, MLA_DEPTH_V, S,
+                            valid_length is not None)
+    if out is None:
+        out = torch.empty((B, T, H, MLA_DEPTH_V), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device)
+    args = (_ptr(q), _ptr(kv), _ptr(kv_row_offsets), _ptr(valid_length), B, T, H, S,
+            float(scale), P, _ptr(sink_weights), _mask(causal), _ptr(out), _ptr(lse),
+            _ptr(workspace), wbytes, _stream(stream))
+    return _finish(library().mla_decode_ragged_kv, args, "mla_decode_ragged_kv", (out, lse),
+                   (q, kv, kv_row_offsets, valid_length, sink_weights, out, lse, workspace),
+                   prepare)
 
 
 _FP8 = (torch.uint8, torch.float8_e4m3fn)
@@ -385,15 +502,12 @@ def decode_attention_fp8kv(q, k, v, *, k_scale, v_scale, group, scale, page_tabl
     """GQA/MHA decode attention over an 8-bit e4m3 KV cache (k, v: uint8 bits or
     float8_e4m3fn; real key = k_scale * k, real value = v_scale * v); q and out
     bf16.  Returns (out, lse), or with prepare=True a BoundCall."""
-    _need(q, "q", 4, (torch.bfloat16,))
-    _need(k, "k", 4, _FP8)
-    _need(v, "v", 4, _FP8)
-    _need(valid_length, "valid_length", 1, _U32)
-    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    _mha_inputs(q, k, v, group, kv_dtype=_FP8)
     B, T, H, D = q.shape
-    if k.shape[3] != D or v.shape[3] != D or k.shape[2] * group != H:
-        raise ValueError("k/v shape does not match q and group")
+    _need_per_sequence(valid_length, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (B, T, H, D), q.dtype, (B, T, H), q.device)
     page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len)
+    _need_cuda(q, "q")
     P = _resolve_partitions(num_partitions, B, T, H, H // group, D, D, S,
                             valid_length is not None)
     if out is None:
@@ -403,8 +517,8 @@ def decode_attention_fp8kv(q, k, v, *, k_scale, v_scale, group, scale, page_tabl
     workspace, wbytes = _workspace(workspace, P, B, T, H, D, q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), float(k_scale), float(v_scale), _ptr(page_table),
             page_size, max_pages, _ptr(valid_length), B, T, H, group, D, S, float(scale), P,
-            _ptr(sink_weights), DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(out),
-            _ptr(lse), _ptr(workspace), wbytes, _stream(stream))
+            _ptr(sink_weights), _mask(causal), _ptr(out), _ptr(lse), _ptr(workspace), wbytes,
+            _stream(stream))
     return _finish(library().decode_attention_fp8kv, args, "decode_attention_fp8kv", (out, lse),
                    (q, k, v, page_table, valid_length, sink_weights, out, lse, workspace),
                    prepare)
@@ -415,18 +529,16 @@ def decode_attention_fp8kv_partials(q, k, v, *, k_scale, v_scale, group, scale, 
                                     causal=False, workspace=None, stream=None, prepare=False):
     """Partition pass of decode_attention_fp8kv() only.  Returns the workspace, or
     with prepare=True a BoundCall."""
-    _need(q, "q", 4, (torch.bfloat16,))
-    _need(k, "k", 4, _FP8)
-    _need(v, "v", 4, _FP8)
-    _need(valid_length, "valid_length", 1, _U32)
+    _mha_inputs(q, k, v, group, kv_dtype=_FP8)
     B, T, H, D = q.shape
+    _need_per_sequence(valid_length, None, B, H, q.device)
     page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len)
+    _need_cuda(q, "q")
     P = int(num_partitions)
     workspace, wbytes = _workspace(workspace, P, B, T, H, D, q.device, always=True)
     args = (_ptr(q), _ptr(k), _ptr(v), float(k_scale), float(v_scale), _ptr(page_table),
             page_size, max_pages, _ptr(valid_length), B, T, H, group, D, S, float(scale), P,
-            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(workspace), wbytes,
-            _stream(stream))
+            _mask(causal), _ptr(workspace), wbytes, _stream(stream))
     return _finish(library().decode_attention_fp8kv_partials, args,
                    "decode_attention_fp8kv_partials", workspace,
                    (q, k, v, page_table, valid_length, workspace), prepare)
@@ -437,14 +549,12 @@ def mla_decode(q, kv, *, scale, page_table=None, valid_length=None, max_seq_len=
                workspace=None, stream=None, want_lse=True, prepare=False):
     """MLA decode (one KV head, depth 576, V = K[..., :512]).  Returns (out, lse), or
     with prepare=True a BoundCall that enqueues the call and returns them."""
-    _need(q, "q", 4, (torch.bfloat16,))
-    _need(kv, "kv", 4, (torch.bfloat16,))
-    _need(valid_length, "valid_length", 1, _U32)
-    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    _mla_inputs(q, kv)
     B, T, H, D = q.shape
-    if D != MLA_DEPTH or kv.shape[3] != MLA_DEPTH or kv.shape[2] != 1:
-        raise ValueError("MLA needs q [..., 576] and kv [..., 1, 576]")
+    _need_per_sequence(valid_length, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (B, T, H, MLA_DEPTH_V), q.dtype, (B, T, H), q.device)
     page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len)
+    _need_cuda(q, "q")
     P = _resolve_partitions(num_partitions, B, T, H, 1, MLA_DEPTH, MLA_DEPTH_V, S,
                             valid_length is not None)
     if out is None:
@@ -453,9 +563,8 @@ def mla_decode(q, kv, *, scale, page_table=None, valid_length=None, max_seq_len=
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device)
     args = (_ptr(q), _ptr(kv), _ptr(page_table), page_size, max_pages, _ptr(valid_length), B, T,
-            H, S, float(scale), P, _ptr(sink_weights),
-            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(out), _ptr(lse), _ptr(workspace),
-            wbytes, _stream(stream))
+            H, S, float(scale), P, _ptr(sink_weights), _mask(causal), _ptr(out), _ptr(lse),
+            _ptr(workspace), wbytes, _stream(stream))
     return _finish(library().mla_decode, args, "mla_decode", (out, lse),
                    (q, kv, page_table, valid_length, sink_weights, out, lse, workspace), prepare)
 
@@ -464,16 +573,15 @@ def mla_decode_partials(q, kv, *, scale, num_partitions, page_table=None, valid_
                         max_seq_len=None, causal=False, workspace=None, stream=None,
                         prepare=False):
     """MLA partition pass only.  Returns the workspace, or with prepare=True a BoundCall."""
-    _need(q, "q", 4, (torch.bfloat16,))
-    _need(kv, "kv", 4, (torch.bfloat16,))
-    _need(valid_length, "valid_length", 1, _U32)
+    _mla_inputs(q, kv)
     B, T, H, D = q.shape
+    _need_per_sequence(valid_length, None, B, H, q.device)
     page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len)
+    _need_cuda(q, "q")
     P = int(num_partitions)
     workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device, always=True)
     args = (_ptr(q), _ptr(kv), _ptr(page_table), page_size, max_pages, _ptr(valid_length), B, T,
-            H, S, float(scale), P, DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(workspace),
-            wbytes, _stream(stream))
+            H, S, float(scale), P, _mask(causal), _ptr(workspace), wbytes, _stream(stream))
     return _finish(library().mla_decode_partials, args, "mla_decode_partials", workspace,
                    (q, kv, page_table, valid_length, workspace), prepare)
 
@@ -484,14 +592,12 @@ def mla_decode_fp8kv(q, kv, *, k_scale, scale, page_table=None, valid_length=Non
                      prepare=False):
     """MLA over an 8-bit e4m3 cache (uint8 / float8_e4m3fn [..., 1, 576]; real element =
     k_scale x stored) with bf16 q.  Returns (out, lse), or with prepare=True a BoundCall."""
-    _need(q, "q", 4, (torch.bfloat16,))
-    _need(kv, "kv", 4, _FP8)
-    _need(valid_length, "valid_length", 1, _U32)
-    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    _mla_inputs(q, kv, kv_dtype=_FP8)
     B, T, H, D = q.shape
-    if D != MLA_DEPTH or kv.shape[3] != MLA_DEPTH or kv.shape[2] != 1:
-        raise ValueError("MLA needs q [..., 576] and kv [..., 1, 576]")
+    _need_per_sequence(valid_length, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (B, T, H, MLA_DEPTH_V), q.dtype, (B, T, H), q.device)
     page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len)
+    _need_cuda(q, "q")
     P = _resolve_partitions(num_partitions, B, T, H, 1, MLA_DEPTH, MLA_DEPTH_V, S,
                             valid_length is not None)
     if out is None:
@@ -500,9 +606,8 @@ def mla_decode_fp8kv(q, kv, *, k_scale, scale, page_table=None, valid_length=Non
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
     workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device)
     args = (_ptr(q), _ptr(kv), float(k_scale), _ptr(page_table), page_size, max_pages,
-            _ptr(valid_length), B, T, H, S, float(scale), P, _ptr(sink_weights),
-            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(out), _ptr(lse), _ptr(workspace),
-            wbytes, _stream(stream))
+            _ptr(valid_length), B, T, H, S, float(scale), P, _ptr(sink_weights), _mask(causal),
+            _ptr(out), _ptr(lse), _ptr(workspace), wbytes, _stream(stream))
     return _finish(library().mla_decode_fp8kv, args, "mla_decode_fp8kv", (out, lse),
                    (q, kv, page_table, valid_length, sink_weights, out, lse, workspace), prepare)
 
@@ -512,16 +617,16 @@ def mla_decode_fp8kv_partials(q, kv, *, k_scale, scale, num_partitions, page_tab
                               stream=None, prepare=False):
     """Partition pass of mla_decode_fp8kv() alone.  Returns the workspace, or with
     prepare=True a BoundCall."""
-    _need(q, "q", 4, (torch.bfloat16,))
-    _need(kv, "kv", 4, _FP8)
-    _need(valid_length, "valid_length", 1, _U32)
+    _mla_inputs(q, kv, kv_dtype=_FP8)
     B, T, H, D = q.shape
+    _need_per_sequence(valid_length, None, B, H, q.device)
     page_size, max_pages, S = _cache_geometry(q, kv, page_table, max_seq_len)
+    _need_cuda(q, "q")
     P = int(num_partitions)
     workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device, always=True)
     args = (_ptr(q), _ptr(kv), float(k_scale), _ptr(page_table), page_size, max_pages,
-            _ptr(valid_length), B, T, H, S, float(scale), P,
-            DA_MASK_CAUSAL if causal else DA_MASK_NONE, _ptr(workspace), wbytes, _stream(stream))
+            _ptr(valid_length), B, T, H, S, float(scale), P, _mask(causal), _ptr(workspace),
+            wbytes, _stream(stream))
     return _finish(library().mla_decode_fp8kv_partials, args, "mla_decode_fp8kv_partials",
                    workspace, (q, kv, page_table, valid_length, workspace), prepare)
 
@@ -535,13 +640,13 @@ def mla_sparse_num_partitions(batch, q_len, num_q_heads, topk, num_cus=0) -> int
 
 def _sparse_args(q, kv, indices, topk_lengths):
     _need(q, "q", 4, (torch.bfloat16,))
-    _need(kv, "kv", 3, (torch.bfloat16,))
-    _need(indices, "indices", 2, (torch.int32,))
-    _need(topk_lengths, "topk_lengths", 1, (torch.int32,))
+    _need(kv, "kv", 3, (torch.bfloat16,), device=q.device)
     B, T, H, D = q.shape
     if D != MLA_DEPTH or kv.shape[1] != 1 or kv.shape[2] != MLA_DEPTH:
         raise ValueError("sparse MLA needs q [..., 576] and a pool kv [rows, 1, 576]")
-    if indices.shape[0] != B or topk_lengths.shape[0] != B:
+    _need(indices, "indices", 2, (torch.int32,), device=q.device)
+    _need(topk_lengths, "topk_lengths", 1, (torch.int32,), shape=(B,), device=q.device)
+    if indices is None or topk_lengths is None or indices.shape[0] != B:
         raise ValueError("indices [B, stride] and topk_lengths [B] must match q's batch")
     return B, T, H, kv.shape[0], indices.shape[1]
 
@@ -553,7 +658,9 @@ def mla_decode_sparse(q, kv, indices, topk_lengths, *, scale, num_partitions=0,
     of kv [pool_rows, 1, 576].  Returns (out [B,T,H,512], lse [B,T,H]), or with
     prepare=True a BoundCall."""
     B, T, H, R, stride = _sparse_args(q, kv, indices, topk_lengths)
-    _need(sink_weights, "sink_weights", 1, (torch.float32,))
+    _need_per_sequence(None, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (B, T, H, MLA_DEPTH_V), q.dtype, (B, T, H), q.device)
+    _need_cuda(q, "q")
     P = int(num_partitions) or (mla_sparse_num_partitions(B, T, H, stride) if B else 1)
     if out is None:
         out = torch.empty((B, T, H, MLA_DEPTH_V), dtype=q.dtype, device=q.device)
@@ -572,6 +679,7 @@ def mla_decode_sparse_partials(q, kv, indices, topk_lengths, *, scale, num_parti
     """Partition pass of mla_decode_sparse() alone.  Returns the workspace, or with
     prepare=True a BoundCall."""
     B, T, H, R, stride = _sparse_args(q, kv, indices, topk_lengths)
+    _need_cuda(q, "q")
     P = int(num_partitions)
     workspace, wbytes = _workspace(workspace, P, B, T, H, MLA_DEPTH_V, q.device, always=True)
     args = (_ptr(q), _ptr(kv), R, _ptr(indices), stride, _ptr(topk_lengths), B, T, H,
@@ -586,14 +694,21 @@ def splitk_reduce(part_o, part_max, part_sum, *, num_q_heads, sink_weights=None,
     """LSE merge of partials [P, rows, Dv] / [P, rows] -> (out [rows, Dv], lse [rows]);
     with prepare=True a BoundCall that enqueues the merge and returns them."""
     _need(part_o, "part_o", 3, (torch.float32,))
-    _need(part_max, "part_max", 2, (torch.float32,))
-    _need(part_sum, "part_sum", 2, (torch.float32,))
-    _need(sink_weights, "sink_weights", 1, (torch.float32,))
     P, rows, Dv = part_o.shape
+    dev = part_o.device
+    _need(part_max, "part_max", 2, (torch.float32,), shape=(P, rows), device=dev)
+    _need(part_sum, "part_sum", 2, (torch.float32,), shape=(P, rows), device=dev)
+    _need(sink_weights, "sink_weights", 1, (torch.float32,), shape=(num_q_heads,), device=dev)
+    if out is not None:
+        out_dtype = out.dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"out dtype {out_dtype}: use bfloat16 or float32")
+    _need_outputs(out, lse, (rows, Dv), out_dtype, (rows,), dev)
+    _need_cuda(part_o, "part_o")
     if out is None:
-        out = torch.empty((rows, Dv), dtype=out_dtype, device=part_o.device)
+        out = torch.empty((rows, Dv), dtype=out_dtype, device=dev)
     if lse is None and want_lse:
-        lse = torch.empty((rows,), dtype=torch.float32, device=part_o.device)
+        lse = torch.empty((rows,), dtype=torch.float32, device=dev)
     args = (_ptr(part_o), _ptr(part_max), _ptr(part_sum), P, rows, num_q_heads, Dv,
             _ptr(sink_weights), _ptr(out), _dtype_code(out), _ptr(lse), _stream(stream))
     return _finish(library().splitk_reduce, args, "splitk_reduce", (out, lse),

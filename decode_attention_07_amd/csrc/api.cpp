@@ -160,6 +160,8 @@ struct Common {
   // sequence's tokens) and the total token count; nullptr / 0 otherwise.
   const uint32_t* q_offsets = nullptr;
   int total_q_tokens = 0;
+  // Ragged KV layout: per-sequence row offsets into one cache; nullptr otherwise.
+  const uint32_t* kv_row_offsets = nullptr;
 };
 
 // q / out rows of a call (tokens x heads).
@@ -174,6 +176,7 @@ int check_common(const Common& c) {
   if (c.total_q_tokens < 0) return DA_ERR_INVALID_ARG;
   if (c.mask != DA_MASK_NONE && c.mask != DA_MASK_CAUSAL) return DA_ERR_INVALID_ARG;
   if (!std::isfinite(c.scale)) return DA_ERR_INVALID_ARG;
+  if (c.kv_row_offsets && c.page_table) return DA_ERR_INVALID_ARG;
   if (c.page_table) {
     if (c.page_size < 1 || c.max_pages < 1) return DA_ERR_INVALID_ARG;
     if (!is_pow2(c.page_size) || c.page_size < 32) return DA_ERR_UNSUPPORTED;
@@ -205,6 +208,7 @@ da::DecodeParams base_params(const Common& c, const void* q, const void* k, cons
   p.v_scale = 1.f;
   p.q_offsets = c.q_offsets;
   p.rows_total = (int)call_rows(c);
+  p.kv_row_offsets = c.kv_row_offsets;
   return p;
 }
 
@@ -580,6 +584,46 @@ int mla_decode_ragged(const void* q, const uint32_t* q_offsets, int total_q_toke
       base_params(c, q, kv, kv, 1, num_q_heads, kMlaDepth, kMlaDepthV);
   return run(c, p, plan_mla(max_q_len, num_q_heads), true, num_partitions, false, sink_weights,
              out, lse, workspace, workspace_bytes, stream);
+}
+
+int decode_attention_ragged_kv(const void* q, const void* k, const void* v,
+                               const uint32_t* kv_row_offsets, const uint32_t* valid_length,
+                               int batch, int q_len, int num_q_heads, int group, int depth,
+                               int max_seq_len, float scale, int num_partitions,
+                               const float* sink_weights, int mask, int dtype, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Common c{nullptr, 0,     0,           valid_length, batch,
+           q_len,   num_q_heads, max_seq_len, mask, scale};
+  c.kv_row_offsets = kv_row_offsets;
+  if (!kv_row_offsets && batch > 0) return DA_ERR_INVALID_ARG;
+  int rc = check_mha(c, q, k, v, group, depth, dtype);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  const bool bf16 = dtype == DA_BF16;
+  const int kv_heads = num_q_heads / group;
+  const da::DecodeParams p = base_params(c, q, k, v, kv_heads, group, depth, depth);
+  return run(c, p, plan_mha(q_len, group, bf16), bf16, num_partitions, false, sink_weights, out,
+             lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_ragged_kv(const void* q, const void* kv, const uint32_t* kv_row_offsets,
+                         const uint32_t* valid_length, int batch, int q_len, int num_q_heads,
+                         int max_seq_len, float scale, int num_partitions,
+                         const float* sink_weights, int mask, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  Common c{nullptr, 0,     0,           valid_length, batch,
+           q_len,   num_q_heads, max_seq_len, mask, scale};
+  c.kv_row_offsets = kv_row_offsets;
+  if (!kv_row_offsets && batch > 0) return DA_ERR_INVALID_ARG;
+  int rc = check_mla(c, q, kv);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  const da::DecodeParams p = base_params(c, q, kv, kv, 1, num_q_heads, kMlaDepth, kMlaDepthV);
+  return run(c, p, plan_mla(q_len, num_q_heads), true, num_partitions, false, sink_weights, out,
+             lse, workspace, workspace_bytes, stream);
 }
 
 int decode_attention_fp8kv(const void* q, const void* k, const void* v, float k_scale,

@@ -121,6 +121,17 @@ __device__ __forceinline__ uint64_t pin_uniform_u64(uint64_t x) {
   return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
+// Cache row of key 0 of sequence b in an unpaged cache: b * max_seq_len in the
+// dense layout, kv_row_offsets[b] in the ragged KV layout.  The offset is read
+// through the scalar cache (b is uniform, the offsets are constant during the
+// call); its address is pinned to scalar registers first so that the read stays
+// a scalar load wherever the compiler placed b.
+__device__ __forceinline__ size_t seq_kv_row0(const DecodeParams& p, int b) {
+  if (!p.kv_row_offsets) return (size_t)b * p.max_seq_len;
+  const uint64_t a = pin_uniform_u64((uint64_t)(p.kv_row_offsets + b));
+  return (size_t)*(const __attribute__((address_space(4))) uint32_t*)a;
+}
+
 // ---- online-softmax state merge (log2 domain) ----------------------------------
 // Combines (mA, lA) with (mB, lB); returns the scale factors for A and B.
 __device__ __forceinline__ void merge_factors(float mA, float mB, float& m, float& fa,
@@ -134,8 +145,18 @@ __device__ __forceinline__ void merge_factors(float mA, float mB, float& m, floa
 // ---- per-row key limits ----------------------------------------------------------
 // Keys of sequence b visible to query token t.
 __device__ __forceinline__ int visible_keys(const DecodeParams& p, int b, int t) {
-  int n = p.valid_length ? (int)p.valid_length[b] : p.max_seq_len;
-  if (n > p.max_seq_len) n = p.max_seq_len;
+  int n;
+  if (p.indices) {
+    // sparse top-k counts (int32): a negative count is 0, one above the list
+    // stride (max_seq_len here) is the stride
+    const int c = (int)p.valid_length[b];
+    n = c < 0 ? 0 : (c < p.max_seq_len ? c : p.max_seq_len);
+  } else {
+    // A length above max_seq_len counts as max_seq_len; compared as unsigned, so
+    // that a length of 2^31 or more is a large count, not a negative one.
+    const uint32_t nv = p.valid_length ? p.valid_length[b] : (uint32_t)p.max_seq_len;
+    n = nv < (uint32_t)p.max_seq_len ? (int)nv : p.max_seq_len;
+  }
   if (p.causal) {
     int lim = n - seq_tokens(p, b) + t + 1;
     n = lim < n ? lim : n;
@@ -150,7 +171,7 @@ __device__ __forceinline__ size_t kv_row(const DecodeParams& p, int b, int j, in
     uint32_t phys = p.page_table[(size_t)b * p.max_pages + (j >> p.page_shift)];
     row = ((size_t)phys << p.page_shift) + (size_t)(j & ((1 << p.page_shift) - 1));
   } else {
-    row = (size_t)b * p.max_seq_len + j;
+    row = seq_kv_row0(p, b) + j;
   }
   return (row * p.num_kv_heads + g) * (size_t)width;
 }

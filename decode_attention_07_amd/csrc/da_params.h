@@ -48,6 +48,10 @@ struct DecodeParams {
   // nullptr: keys from the contiguous or paged cache.
   const int32_t* indices;
   uint32_t pool_rows;
+  // Ragged KV layout: key j of sequence b is row kv_row_offsets[b] + j of one
+  // cache [rows, KVH, D] holding every sequence (instead of row b * max_seq_len
+  // + j of the dense layout); nullptr otherwise.  Never set with a page table.
+  const uint32_t* kv_row_offsets;
 };
 
 // Row-block geometry of a (batch, KV head): T*group rows (token-major:

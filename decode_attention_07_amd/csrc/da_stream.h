@@ -48,7 +48,7 @@ __device__ __forceinline__ size_t stream_row0(const DecodeParams& p, int b, int 
     const uint32_t phys = pt[(size_t)b * p.max_pages + (j0 >> p.page_shift)];
     return ((size_t)phys << p.page_shift) + (size_t)(j0 & ((1 << p.page_shift) - 1));
   }
-  return (size_t)b * p.max_seq_len + j0;
+  return seq_kv_row0(p, b) + j0;
 }
 
 __device__ __forceinline__ float max_xor16(float x) {

@@ -78,7 +78,7 @@ __device__ __forceinline__ void valu_load(const DecodeParams& p, ValuTile<BF16, 
       uint32_t phys = p.page_table[(size_t)b * p.max_pages + (jbase >> p.page_shift)];
       row0 = ((size_t)phys << p.page_shift) + (size_t)(jbase & ((1 << p.page_shift) - 1));
     } else {
-      row0 = (size_t)b * p.max_seq_len + jbase;
+      row0 = seq_kv_row0(p, b) + jbase;
     }
     const int jl = wave * 8 + slot;
     const size_t elem = ((row0 + jl) * p.num_kv_heads + g) * (size_t)D;

@@ -116,7 +116,7 @@ __device__ __forceinline__ size_t mla_row0(const DecodeParams& p, int b, int j0)
     const uint32_t phys = *(const __attribute__((address_space(4))) uint32_t*)a;
     return ((size_t)phys << p.page_shift) + (size_t)(j0 & ((1 << p.page_shift) - 1));
   }
-  return (size_t)b * p.max_seq_len + j0;
+  return seq_kv_row0(p, b) + j0;
 }
 
 // Requests the 32-key tile starting at key j0 into one LDS stage.  Keys at or

@@ -144,7 +144,9 @@ size_t decode_workspace_sum_offset(int num_partitions, int batch, int q_len, int
  *   page_table      NULL for a dense cache; otherwise page_size must be a power
  *                   of two >= 32 and max_pages_per_seq >= ceil(max_seq_len / page_size).
  *   valid_length    per-sequence key counts or NULL ("mha_sm100_dispatch", Args
- *                   `valid_length`); values above max_seq_len count as max_seq_len.
+ *                   `valid_length`); values above max_seq_len count as max_seq_len
+ *                   (compared as unsigned 32-bit numbers: 0xFFFFFFFF counts as
+ *                   max_seq_len, too).
  *   group           query heads per KV head; num_q_heads % group == 0.
  *   depth           64 or 128 (the value depth equals depth).
  *   max_seq_len     host upper bound of the key count ("mha_sm100_dispatch",
@@ -211,6 +213,41 @@ int mla_decode_ragged(const void* q, const uint32_t* q_offsets, int total_q_toke
                       int num_q_heads, int max_seq_len, float scale, int num_partitions,
                       const float* sink_weights, int mask, void* out, float* lse,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode attention over a ragged KV layout ("mha_sm100_dispatch", Args
+ * `kv_input_row_offsets`: per-batch row offsets into a ragged KV layout).  The
+ * caches of all sequences are concatenated into one cache
+ *     k, v  [kv_rows, num_kv_heads, depth]
+ * and key j of sequence b is its row kv_row_offsets[b] + j.
+ *   kv_row_offsets  device uint32 [batch] (required when batch > 0).  The
+ *                   caller keeps kv_row_offsets[b] + N_b <= kv_rows for every
+ *                   sequence, N_b being its key count below; the kernels do
+ *                   not check it.  Sequences may share rows.
+ *   valid_length    key counts N_b (values above max_seq_len count as
+ *                   max_seq_len), or NULL: every sequence has max_seq_len keys.
+ *   max_seq_len     bound of every N_b (no stride: there is no dense layout).
+ * q, out, lse, the mask, the sinks, the partitions and the workspace are as for
+ * decode_attention(); there is no page table.
+ */
+int decode_attention_ragged_kv(const void* q, const void* k, const void* v,
+                               const uint32_t* kv_row_offsets, const uint32_t* valid_length,
+                               int batch, int q_len, int num_q_heads, int group, int depth,
+                               int max_seq_len, float scale, int num_partitions,
+                               const float* sink_weights, int mask, int dtype, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* MLA over a ragged KV layout ("flare_mla_decoding_dispatch", Args
+ * `kv_input_row_offsets`): kv is one cache [kv_rows, 1, 576] and key j of
+ * sequence b is its row kv_row_offsets[b] + j (V = the first 512 columns of the
+ * same rows).  kv_row_offsets, valid_length and max_seq_len as for
+ * decode_attention_ragged_kv(); every other argument as for mla_decode(). */
+int mla_decode_ragged_kv(const void* q, const void* kv, const uint32_t* kv_row_offsets,
+                         const uint32_t* valid_length, int batch, int q_len, int num_q_heads,
+                         int max_seq_len, float scale, int num_partitions,
+                         const float* sink_weights, int mask, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Decode attention with an 8-bit KV cache: q bf16, k and v one byte per element

@@ -29,8 +29,9 @@ int oracle_decode_attention(const void* q, const void* k, const void* v, int dty
                             int T, int H, int KVH, int D, int Dv, int S, float scale,
                             const float* sink, int causal, const uint32_t* q_offsets,
                             const int32_t* indices, int indices_stride,
-                            const int32_t* topk_lengths, int64_t pool_rows, const int64_t* rows,
-                            int64_t num_rows, double* out, double* lse, int num_threads);
+                            const int32_t* topk_lengths, int64_t pool_rows,
+                            const uint32_t* kv_offsets, const int64_t* rows, int64_t num_rows,
+                            double* out, double* lse, int num_threads);
 
 static int failures = 0;
 
@@ -168,7 +169,7 @@ static void gqa_case(void) {
   double* ref_lse = (double*)malloc(sizeof(double) * rows);
   int rc = oracle_decode_attention(q, k, v, 1, 1.f, 1.f, table, ps, max_pages, lens, B, T, H,
                                    KVH, D, D, S, scale, sink, 0, NULL, NULL, 0, NULL, 0, NULL,
-                                   (int64_t)rows, ref, ref_lse, 0);
+                                   NULL, (int64_t)rows, ref, ref_lse, 0);
   CHECK(rc == 0, "oracle (GQA): %d", rc);
 
   void *dq = to_device(q, nq * 2), *dk = to_device(k, nkv * 2), *dv = to_device(v, nkv * 2);
@@ -240,7 +241,7 @@ static void mla_case(void) {
   double* ref = (double*)malloc(sizeof(double) * rows * Dv);
   double* ref_lse = (double*)malloc(sizeof(double) * rows);
   int rc = oracle_decode_attention(q, kv, NULL, 1, 1.f, 1.f, NULL, 0, 0, lens, B, T, H, 1, D, Dv,
-                                   S, scale, NULL, 1, NULL, NULL, 0, NULL, 0, NULL,
+                                   S, scale, NULL, 1, NULL, NULL, 0, NULL, 0, NULL, NULL,
                                    (int64_t)rows, ref, ref_lse, 0);
   CHECK(rc == 0, "oracle (MLA): %d", rc);
   void *dq = to_device(q, nq * 2), *dkv = to_device(kv, nkv * 2);

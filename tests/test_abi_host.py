@@ -20,7 +20,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     lib = ctypes.CDLL(DA.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
@@ -313,3 +313,78 @@ def test_mla_fp8kv_argument_checks():
                                          0, None, 0, None) == DA.DA_ERR_INVALID_ARG
     assert lib.mla_decode_fp8kv_partials(1, 1, 0.125, None, 0, 0, None, 1, 1, 128, 64, 0.1, 2,
                                          0, None, 0, None) == DA.DA_ERR_WORKSPACE
+
+
+def test_ragged_kv_argument_checks():
+    lib = DA.library()
+    # decode_attention_ragged_kv(q, k, v, offs, valid, B, T, H, group, D, S, scale, P, sink,
+    #                            mask, dtype, out, lse, ws, wbytes, stream)
+    ok = [1, 1, 1, 1, None, 2, 1, 8, 2, 128, 256, 0.1, 1, None, 0, 1, 1, None, None, 0, None]
+    for i, v, code in [(3, None, DA.DA_ERR_INVALID_ARG),    # the offsets are required
+                       (0, None, DA.DA_ERR_INVALID_ARG), (16, None, DA.DA_ERR_INVALID_ARG),
+                       (8, 3, DA.DA_ERR_INVALID_ARG), (9, 96, DA.DA_ERR_UNSUPPORTED),
+                       (10, -1, DA.DA_ERR_INVALID_ARG), (14, 2, DA.DA_ERR_INVALID_ARG),
+                       (12, 4, DA.DA_ERR_WORKSPACE)]:
+        a = list(ok)
+        a[i] = v
+        assert lib.decode_attention_ragged_kv(*a) == code, (i, v)
+    a = list(ok)
+    a[5], a[3] = 0, None
+    assert lib.decode_attention_ragged_kv(*a) == DA.DA_OK   # empty batch: nothing launched
+    # mla_decode_ragged_kv(q, kv, offs, valid, B, T, H, S, scale, P, sink, mask, out, lse, ws,
+    #                      wbytes, stream)
+    ok = [1, 1, 1, None, 2, 1, 128, 256, 0.1, 1, None, 0, 1, None, None, 0, None]
+    for i, v, code in [(2, None, DA.DA_ERR_INVALID_ARG), (1, None, DA.DA_ERR_INVALID_ARG),
+                       (12, None, DA.DA_ERR_INVALID_ARG), (11, 5, DA.DA_ERR_INVALID_ARG),
+                       (9, 3, DA.DA_ERR_WORKSPACE)]:
+        a = list(ok)
+        a[i] = v
+        assert lib.mla_decode_ragged_kv(*a) == code, (i, v)
+
+
+# ---- the Python binding checks its arguments before marshalling (host tensors) -------
+
+def _bf16(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def test_binding_rejects_misshaped_outputs_and_per_sequence_arrays():
+    import torch
+    q, k, v = _bf16(2, 1, 8, 128), _bf16(2, 64, 2, 128), _bf16(2, 64, 2, 128)
+    bad = [
+        dict(out=_bf16(2, 1, 8, 64)),                                     # out shape
+        dict(out=torch.zeros((2, 1, 8, 128), dtype=torch.float32)),       # out dtype
+        dict(lse=torch.zeros((2, 1, 7), dtype=torch.float32)),            # lse shape
+        dict(lse=torch.zeros((2, 1, 8), dtype=torch.float64)),            # lse dtype
+        dict(out=_bf16(2, 1, 128, 8).transpose(2, 3)),                    # not contiguous
+        dict(valid_length=torch.zeros(3, dtype=torch.int32)),             # one per sequence
+        dict(sink_weights=torch.zeros(4, dtype=torch.float32)),           # one per query head
+        dict(page_table=torch.zeros((1, 4), dtype=torch.int32)),          # a row per sequence
+    ]
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError)) as e:
+            DA.decode_attention(q, k, v, group=4, scale=0.1, **kw)
+        assert "CUDA" not in str(e.value), kw   # rejected by the shape check itself
+    with pytest.raises(ValueError):  # v must mirror k
+        DA.decode_attention(q, k, _bf16(2, 64, 2, 64), group=4, scale=0.1)
+    with pytest.raises(ValueError):
+        DA.decode_attention_ragged_kv(q, _bf16(100, 2, 128), _bf16(100, 2, 128),
+                                      torch.zeros(3, dtype=torch.int32), group=4, scale=0.1,
+                                      max_seq_len=64)
+
+
+def test_binding_rejects_misshaped_reduce_arguments():
+    import torch
+    po = torch.zeros((4, 6, 128), dtype=torch.float32)
+    pm = torch.zeros((4, 6), dtype=torch.float32)
+    for kw in (dict(part_max=torch.zeros((4, 5), dtype=torch.float32)),
+               dict(part_sum=torch.zeros((3, 6), dtype=torch.float32)),
+               dict(out=_bf16(6, 64)),
+               dict(lse=torch.zeros(5, dtype=torch.float32)),
+               dict(sink_weights=torch.zeros(3, dtype=torch.float32))):
+        a = dict(part_max=pm, part_sum=pm, num_q_heads=2)
+        a.update(kw)
+        with pytest.raises((ValueError, TypeError)) as e:
+            DA.splitk_reduce(po, a.pop("part_max"), a.pop("part_sum"), **a)
+        assert "CUDA" not in str(e.value), kw

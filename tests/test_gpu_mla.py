@@ -8,21 +8,7 @@ from gpu_util import check
 pytestmark = pytest.mark.gpu
 
 
-def _sample_rows(wl, n, seed):
-    rng = np.random.default_rng(seed)
-    total = wl.batch * wl.q_len * wl.num_heads
-    return np.sort(rng.choice(total, size=min(n, total), replace=False)).astype(np.int64)
-
-
-# ---- the MLA problem at full size (sampled rows: every row is 8192 keys x 1088 MACs) --
-
-@pytest.mark.parametrize("P", [0, 1])
-def test_mla_full_sampled(P):
-    check(W.MLA, num_partitions=P, rows=_sample_rows(W.MLA, 768, 1))
-
-
-def test_mla_mtp_full_sampled():
-    check(W.MLA_MTP, num_partitions=0, rows=_sample_rows(W.MLA_MTP, 768, 2))
+# The MLA problem at full size, every row: tests/test_gpu_full_size.py.
 
 
 # ---- small MLA shapes: every row compared ----------------------------------------

@@ -6,7 +6,7 @@ import torch
 
 import workloads as W
 from decode_attention_07_amd import binding as DA
-from gpu_util import check, compare, device_inputs, run_gpu, run_oracle
+from gpu_util import check, device_inputs, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -18,12 +18,6 @@ def _wl(name, seed, B, T, H, S, page=0, causal=False, ragged=False, sink=False, 
                       depth_v=512, max_seq_len=S, q_len=T, mla=True, causal=causal,
                       page_size=page, ragged=(1, S, 1) if ragged else None, scale=SCALE,
                       sink=sink, kv_dtype="e4m3", k_scale=k_scale, v_scale=k_scale)
-
-
-def _sample_rows(wl, n, seed):
-    rng = np.random.default_rng(seed)
-    total = wl.batch * wl.q_len * wl.num_heads
-    return np.sort(rng.choice(total, size=min(n, total), replace=False)).astype(np.int64)
 
 
 SMALL = [
@@ -107,17 +101,7 @@ def test_mla_fp8_partials_plus_reduce_equals_full_call():
     assert torch.equal(lse.view(-1), lse2)
 
 
-@pytest.mark.parametrize("T", [1, 2])
-def test_mla_fp8_full_size_sampled(T):
-    """The MLA problem (64 sequences x 128 heads x 8192 keys) over the 8-bit cache, at
-    the heuristic's P, on sampled rows."""
-    wl = W.MLA_FP8 if T == 1 else W.MLA_FP8.with_(name="mla_fp8_mtp2", q_len=2, causal=True)
-    rows = _sample_rows(wl, 512, 10 + T)
-    inp = W.make_inputs(wl)
-    dev = device_inputs(inp)
-    out, lse = run_gpu(wl, dev, 0)
-    ref_out, ref_lse = run_oracle(wl, inp, rows)
-    compare(wl, out, lse, ref_out, ref_lse, rows=rows, what=f"{wl.name} P=auto")
+# The 8-bit MLA problem at full size, every row: tests/test_gpu_full_size.py.
 
 
 def test_mla_fp8_rejects_bad_scale():

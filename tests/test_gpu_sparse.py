@@ -6,7 +6,7 @@ import torch
 
 import workloads as W
 from decode_attention_07_amd import binding as DA
-from gpu_util import TOL_LSE, TOL_OUT, check, compare, device_inputs, run_gpu, say
+from gpu_util import check, compare, device_inputs, run_gpu, say
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -160,20 +160,7 @@ def test_sparse_rows_at_the_top_of_a_4gib_pool():
     torch.cuda.empty_cache()
 
 
-def test_sparse_full_size_sampled_rows():
-    """The sparse MLA problem (64 sequences x 128 heads, 2048 of 8192 rows each) at the
-    heuristic's P and at P = 1, on a sample of rows the oracle computes one by one."""
-    wl = W.MLA_SPARSE
-    inp = W.make_inputs(wl)
-    dev = device_inputs(inp)
-    rng = np.random.default_rng(123)
-    rows = np.sort(rng.choice(wl.batch * wl.num_heads, size=192, replace=False)).astype(np.int64)
-    ref_out, ref_lse = O.attention(inp.q, inp.k, None, scale=wl.softmax_scale, depth_v=512,
-                                   rows=rows, indices=inp.indices,
-                                   topk_lengths=inp.topk_lengths)
-    for P in (0, 1):
-        out, lse = run_gpu(wl, dev, P)
-        compare(wl, out, lse, ref_out, ref_lse, rows=rows, what=f"{wl.name} P={P or 'auto'}")
+# The sparse MLA problem at full size, every row: tests/test_gpu_full_size.py.
 
 
 def test_sparse_rejects_bad_shapes():

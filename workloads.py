@@ -194,6 +194,34 @@ def pack_ragged_q(inp: Inputs, tokens):
     return np.ascontiguousarray(q), qo
 
 
+def ragged_kv_layout(k: np.ndarray, v: np.ndarray | None, lens, seed: int, gap: int = 3):
+    """A dense cache [B, S, KVH, D] laid out as one concatenated cache [rows, KVH, D]:
+    the valid rows of each sequence, in a seeded random sequence order, with `gap`
+    poison rows (NaN) between sequences and after the last one.  Returns (k_cat,
+    v_cat, offsets) with offsets uint32 [B] the first row of each sequence."""
+    B = k.shape[0]
+    lens = np.asarray(lens, np.int64)
+    total = gap + int(sum(int(n) + gap for n in lens))
+    kind = {np.dtype(np.uint16): "bf16", np.dtype(np.uint8): "e4m3",
+            np.dtype(np.float32): "f32"}[k.dtype]
+    kc = np.empty((total,) + k.shape[2:], k.dtype)
+    _poison(kc, kind)
+    vc = None
+    if v is not None:
+        vc = np.empty((total,) + v.shape[2:], v.dtype)
+        _poison(vc, kind)
+    offs = np.zeros(B, np.uint32)
+    pos = gap
+    for b in np.random.Generator(np.random.PCG64(seed)).permutation(B):
+        n = int(lens[b])
+        offs[b] = pos
+        kc[pos:pos + n] = k[b, :n]
+        if v is not None:
+            vc[pos:pos + n] = v[b, :n]
+        pos += n + gap
+    return kc, vc, offs
+
+
 @dataclass
 class Inputs:
     """Host arrays of one problem instance (numpy; bf16 as uint16 bits)."""

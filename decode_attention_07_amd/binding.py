@@ -30,7 +30,8 @@ EXPORTS = ("decode_attention_status_string", "decode_num_partitions", "decode_wo
            "decode_attention_partials", "mla_decode", "mla_decode_partials", "mla_decode_fp8kv",
            "mla_decode_fp8kv_partials", "mla_decode_sparse",
            "mla_decode_sparse_partials", "mla_sparse_num_partitions", "splitk_reduce",
-           "decode_attention_ragged_kv", "mla_decode_ragged_kv")
+           "decode_attention_ragged_kv", "mla_decode_ragged_kv", "decode_attention_no_alloc")
+DA_NO_ALLOC_SCRATCH_BYTES = 32 << 20
 
 _lock = threading.Lock()
 _lib = None
@@ -101,6 +102,9 @@ def _declare(lib):
     lib.mla_decode_ragged_kv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, i32,
                                          vp, vp, vp, sz, vp]
     lib.mla_decode_ragged_kv.restype = i32
+    lib.decode_attention_no_alloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, i32, i32, i32,
+                                              i32, i32, f32, i32, vp, i32, i32, vp, vp, vp]
+    lib.decode_attention_no_alloc.restype = i32
     return lib
 
 
@@ -342,6 +346,29 @@ def decode_attention(q, k, v, *, group, scale, page_table=None, valid_length=Non
             _mask(causal), dt, _ptr(out), _ptr(lse), _ptr(workspace), wbytes, _stream(stream))
     return _finish(library().decode_attention, args, "decode_attention", (out, lse),
                    (q, k, v, page_table, valid_length, sink_weights, out, lse, workspace),
+                   prepare)
+
+
+def decode_attention_no_alloc(q, k, v, *, group, scale, out, lse=None, page_table=None,
+                              valid_length=None, max_seq_len=None, num_partitions=0,
+                              sink_weights=None, causal=False, stream=None, prepare=False):
+    """decode_attention() for callers that cannot allocate: the split-K workspace is
+    the library's static per-device scratch (calls on one device must not overlap),
+    and out (and lse, if wanted) are the caller's -- nothing is allocated here either.
+    Returns (out, lse); with prepare=True a BoundCall."""
+    dt = _mha_inputs(q, k, v, group)
+    B, T, H, D = q.shape
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    _need_per_sequence(valid_length, sink_weights, B, H, q.device)
+    _need_outputs(out, lse, (B, T, H, D), q.dtype, (B, T, H), q.device)
+    page_size, max_pages, S = _cache_geometry(q, k, page_table, max_seq_len)
+    _need_cuda(q, "q")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(page_table), page_size, max_pages,
+            _ptr(valid_length), B, T, H, group, D, S, float(scale), int(num_partitions),
+            _ptr(sink_weights), _mask(causal), dt, _ptr(out), _ptr(lse), _stream(stream))
+    return _finish(library().decode_attention_no_alloc, args, "decode_attention_no_alloc",
+                   (out, lse), (q, k, v, page_table, valid_length, sink_weights, out, lse),
                    prepare)
 
 

@@ -227,6 +227,34 @@ void ws_sections(void* ws, int P, size_t rows, int depth_v, float** po, float** 
   *pl = (float*)(base + kQueueBytes + o_bytes + m_bytes);
 }
 
+// ---- scratch of decode_attention_no_alloc() ------------------------------------
+// The split-K workspace of callers that cannot allocate (graph capture, serving
+// loops): one file-scope device array, a copy per device, held until the process
+// ends.  Host code never uses the array's name as an address: the device address
+// comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static_assert(kNoAllocScratchBytes == DA_NO_ALLOC_SCRATCH_BYTES, "header and library agree");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The current device's address of `scratch`, or nullptr if it cannot be had.
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+// Zeroes the 256-byte work-queue section at the start of a workspace (a kernel, not
+// a memset: the call may be captured into a graph).  Each lane stores its own word.
+__global__ void clear_queue_section(unsigned long long* q) { q[threadIdx.x] = 0ull; }
+
 hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16,
                                  hipStream_t s) {
   switch (v) {
@@ -251,7 +279,7 @@ const char* variant_name(Variant v) {
 // Shared driver of decode_attention / mla_decode (and their partial passes).
 int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int num_partitions,
         bool partials_only, const float* sink, void* out, float* lse, void* workspace,
-        size_t workspace_bytes, void* stream) {
+        size_t workspace_bytes, void* stream, bool clear_queue = false) {
   const size_t rows = call_rows(c);
   if (rows == 0) return DA_OK;  // empty batch: nothing to enqueue
   if (rows > (size_t)INT32_MAX) return DA_ERR_INVALID_ARG;
@@ -314,6 +342,10 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
                  plan.rows_per_block, plan.row_blocks,
                  P * c.batch * (p.num_kv_heads >> p.hb_shift) * plan.row_blocks, c.page_table != nullptr,
                  (!partials_only && P > 1) ? 1 : 0, p.queue != nullptr, 1 << p.hb_shift);
+  if (clear_queue && p.queue) {
+    hipLaunchKernelGGL(clear_queue_section, dim3(1), dim3(kQueueBytes / 8), 0, s, p.queue);
+    if (hipGetLastError() != hipSuccess) return DA_ERR_HIP;
+  }
   if (launch_partition_pass(p, plan.variant, bf16, s) != hipSuccess) return DA_ERR_HIP;
   if (!partials_only && P > 1) {
     if (da::launch_splitk_reduce(po, pm, pl, P, (int)rows, c.num_q_heads, p.depth_v, sink, out,
@@ -522,6 +554,41 @@ int decode_attention(const void* q, const void* k, const void* v, const uint32_t
   const da::DecodeParams p = base_params(c, q, k, v, kv_heads, group, depth, depth);
   return run(c, p, plan_mha(q_len, group, bf16), bf16, num_partitions, false, sink_weights, out,
              lse, workspace, workspace_bytes, stream);
+}
+
+int decode_attention_no_alloc(const void* q, const void* k, const void* v,
+                              const uint32_t* page_table, int page_size, int max_pages_per_seq,
+                              const uint32_t* valid_length, int batch, int q_len,
+                              int num_q_heads, int group, int depth, int max_seq_len,
+                              float scale, int num_partitions, const float* sink_weights,
+                              int mask, int dtype, void* out, float* lse, void* stream) {
+  const Common c{page_table, page_size, max_pages_per_seq, valid_length, batch,
+                 q_len,      num_q_heads, max_seq_len, mask, scale};
+  int rc = check_mha(c, q, k, v, group, depth, dtype);
+  if (rc) return rc;
+  if (!out) return DA_ERR_INVALID_ARG;
+  if (num_partitions < 0 || num_partitions > DA_MAX_PARTITIONS) return DA_ERR_INVALID_ARG;
+  if (call_rows(c) == 0) return DA_OK;
+  int P = num_partitions;
+  if (P == 0) {
+    P = decode_num_partitions(batch, q_len, num_q_heads, num_q_heads / group, depth, depth,
+                              max_seq_len, valid_length != nullptr, 0);
+    if (P < 1) return P;
+  }
+  // The scratch must hold this call's workspace (checked before anything is enqueued).
+  if (P > 1 && decode_workspace_size(P, batch, q_len, num_q_heads, depth) > kNoAllocScratchBytes)
+    return DA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (P > 1) {
+    ws = scratch_address();
+    if (!ws) return DA_ERR_HIP;
+    ws_bytes = kNoAllocScratchBytes;
+  }
+  const bool bf16 = dtype == DA_BF16;
+  const da::DecodeParams p = base_params(c, q, k, v, num_q_heads / group, group, depth, depth);
+  return run(c, p, plan_mha(q_len, group, bf16), bf16, P, false, sink_weights, out, lse, ws,
+             ws_bytes, stream, /*clear_queue=*/true);
 }
 
 int decode_attention_partials(const void* q, const void* k, const void* v,

@@ -168,6 +168,31 @@ int decode_attention(const void* q, const void* k, const void* v, const uint32_t
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * decode_attention() for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without workspace, and the same results.  The split-K workspace
+ * is a static device array of DA_NO_ALLOC_SCRATCH_BYTES bytes inside the library,
+ * one per device, held until the process ends (its address is looked up once per
+ * device, on the first call there).  The call allocates nothing; q, k, v, out and
+ * lse are the caller's as before (out is required).
+ *   - A call whose workspace, decode_workspace_size(P, batch, q_len, num_q_heads,
+ *     depth), exceeds DA_NO_ALLOC_SCRATCH_BYTES returns DA_ERR_WORKSPACE before
+ *     anything is enqueued (with P resolved as for decode_attention(); a call
+ *     with one partition uses no scratch and is never refused for its size).
+ *   - Every call on a device shares that device's array, which keeps the last
+ *     call's contents: calls that overlap on one device (other streams, other
+ *     threads) race on it and must be serialised by the caller.  The work-queue
+ *     word is cleared by a small kernel at the start of each call that uses it.
+ */
+#define DA_NO_ALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int decode_attention_no_alloc(const void* q, const void* k, const void* v,
+                              const uint32_t* page_table, int page_size, int max_pages_per_seq,
+                              const uint32_t* valid_length, int batch, int q_len,
+                              int num_q_heads, int group, int depth, int max_seq_len,
+                              float scale, int num_partitions, const float* sink_weights,
+                              int mask, int dtype, void* out, float* lse, void* stream);
+
+/*
  * The partition pass of decode_attention() alone: writes the split-K partials
  * of every row into `workspace` (layout above) for a later splitk_reduce()
  * (e.g. after the partials of several devices have been gathered).  Takes the

@@ -20,7 +20,7 @@ def header_functions():
 
 def test_every_declared_function_is_exported():
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     lib = ctypes.CDLL(DA.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in the header but not exported"
@@ -388,3 +388,20 @@ def test_binding_rejects_misshaped_reduce_arguments():
         with pytest.raises((ValueError, TypeError)) as e:
             DA.splitk_reduce(po, a.pop("part_max"), a.pop("part_sum"), **a)
         assert "CUDA" not in str(e.value), kw
+
+
+def test_no_alloc_argument_checks():
+    """decode_attention_no_alloc() refuses a workspace larger than its scratch, and bad
+    arguments, before anything reaches the GPU."""
+    lib = DA.library()
+    # decode_attention_no_alloc(q, k, v, table, ps, max_pages, valid, B, T, H, group, D, S,
+    #                           scale, P, sink, mask, dtype, out, lse, stream)
+    ok = [1, 1, 1, None, 0, 0, None, 8, 1, 64, 8, 128, 4096, 0.1, 1, None, 0, 1, 1, None, None]
+    assert DA.decode_workspace_size(1024, 8, 1, 64, 128) > DA.DA_NO_ALLOC_SCRATCH_BYTES
+    for i, v, code in [(14, 1024, DA.DA_ERR_WORKSPACE), (0, None, DA.DA_ERR_INVALID_ARG),
+                       (18, None, DA.DA_ERR_INVALID_ARG), (10, 3, DA.DA_ERR_INVALID_ARG),
+                       (11, 96, DA.DA_ERR_UNSUPPORTED), (14, -1, DA.DA_ERR_INVALID_ARG),
+                       (7, 0, DA.DA_OK)]:
+        a = list(ok)
+        a[i] = v
+        assert lib.decode_attention_no_alloc(*a) == code, (i, v)

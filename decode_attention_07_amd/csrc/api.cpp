@@ -32,6 +32,8 @@ hipError_t launch_decode_stream_fp8(const DecodeParams& p, hipStream_t s);
 int stream_fp8_step_keys();
 hipError_t launch_mla(const DecodeParams& p, hipStream_t s);
 hipError_t launch_mla_fp8(const DecodeParams& p, hipStream_t s);
+hipError_t launch_mla_wave8(const DecodeParams& p, hipStream_t s);
+bool mla_wave8_enabled();
 int mla_step_keys(int q_len);
 int mla_rows_per_block(int q_len, int num_q_heads);
 bool splitk_reduce_supported(int depth_v, int P);
@@ -255,6 +257,12 @@ void* scratch_address() {
 // a memset: the call may be captured into a graph).  Each lane stores its own word.
 __global__ void clear_queue_section(unsigned long long* q) { q[threadIdx.x] = 0ull; }
 
+// The bf16 MLA problem over the contiguous, paged or ragged-KV cache runs on the
+// two-waves-per-SIMD matrix-core kernel; the sparse form on the one-wave kernel.
+bool uses_mla_wave8(const da::DecodeParams& p, Variant v) {
+  return v == kMla && !p.indices && da::mla_wave8_enabled();
+}
+
 hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16,
                                  hipStream_t s) {
   switch (v) {
@@ -262,7 +270,9 @@ hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16
     case kStream: return da::launch_decode_stream(p, s);
     case kStreamFp8: return da::launch_decode_stream_fp8(p, s);
     case kMlaFp8: return da::launch_mla_fp8(p, s);
-    default: return da::launch_mla(p, s);
+    default:
+      if (uses_mla_wave8(p, v)) return da::launch_mla_wave8(p, s);
+      return da::launch_mla(p, s);
   }
 }
 

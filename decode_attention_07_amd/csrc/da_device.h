@@ -69,6 +69,12 @@ __device__ __forceinline__ float max_xor32(float x) {
                                                   false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// max(x, x of lane ^ 16) with v_permlane16_swap (rows of 16 lanes swapped in pairs).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);

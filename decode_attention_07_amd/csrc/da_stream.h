@@ -1,6 +1,5 @@
 // da_stream.h -- pieces shared by the streaming decode kernels (bf16 and
-// 8-bit KV): global->LDS loads, vmcnt waits, the page-table lookup, and a
-// lane-swap max.
+// 8-bit KV): global->LDS loads, vmcnt waits and the page-table lookup.
 #pragma once
 
 #include "da_device.h"
@@ -51,10 +50,5 @@ __device__ __forceinline__ size_t stream_row0(const DecodeParams& p, int b, int 
   return seq_kv_row0(p, b) + j0;
 }
 
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
 
 }  // namespace da

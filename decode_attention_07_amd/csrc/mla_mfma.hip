@@ -14,9 +14,10 @@
 //       kernel (144 VGPRs).
 //   softmax on the accumulator layout: lane l owns row l % 32 and 16 of the 32
 //       keys, lane l ^ 32 the other 16.  Each row keeps a fixed reference max,
-//       set by its first visible tile: p = 2^(s - m) may grow to 2^100 (fp32 and
-//       bf16 hold that, and the sums stay below 2^128), so O is never rescaled
-//       inside the loop.  If a row ever exceeds its reference by more than that,
+//       set by its first visible tile: p = 2^(s - m) may grow to 2^64 (so that a
+//       weight times a value of the cache, summed over every key of a partition,
+//       stays below fp32's 2^128 for |v| up to 2^40 at 2^20 keys), so O is never
+//       rescaled inside the loop.  If a row ever exceeds its reference by more than that,
 //       the block restarts its partition with the raised reference; each restart
 //       lifts the row's reference above every score seen so far, so restarts
 //       end, and for attention scores they do not occur in practice.
@@ -61,7 +62,7 @@ constexpr int kTileBytes = kCols * kBN * 16; // 36 KB
 constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;  // 9
 static_assert(kDmaPerWave * kWaves * 1024 == kTileBytes, "tile must split into 1 KB pieces");
 constexpr int kStages = 4;
-constexpr float kHeadroom = 100.0f;          // largest exp2 argument (log2 units)
+constexpr float kHeadroom = 64.0f;           // largest exp2 argument (log2 units)
 
 // 16 bytes per lane from base + voff straight into LDS (gfx950
 // global_load_lds_dwordx4, scalar base + 32-bit vector offset): lane i of the
@@ -483,8 +484,8 @@ __device__ __forceinline__ void mfma_settle(f32x16_t& s) {
 //
 // Softmax on the accumulator layout: lane l owns row l % 32 and 16 of the 32
 // keys, lane l ^ 32 the other 16.  Each row keeps a fixed reference max, set by
-// its first visible tile: p = 2^(s - m) may grow to 2^100 (fp32 and bf16 hold
-// that, and the sums stay below 2^128), so O is never rescaled inside the loop.
+// its first visible tile: p = 2^(s - m) may grow to 2^64 (weight x value sums stay
+// far below fp32's 2^128), so O is never rescaled inside the loop.
 // If a row ever exceeds its reference by more than that, the block restarts its
 // partition with the raised reference.  The weights enter the MFMA rounded to
 // bf16; their rounded sum (lsr) is what O is normalised by, so the effective

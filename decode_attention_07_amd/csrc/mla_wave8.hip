@@ -21,9 +21,10 @@
 //              V^T read from the same LDS tile by transposing reads, P^T from
 //              the buffer.
 // The split works because the softmax keeps a fixed reference max per row (set
-// by the row's first visible tile; weights up to 2^kHeadroom): O is never
-// rescaled, so a P.V wave needs no other wave's running max, only the rows'
-// final normalisers at the end (through LDS).  A row whose scores exceed its
+// by the row's first visible tile; weights up to 2^kHeadroom = 2^64, so that
+// weight x value sums over a partition stay far below fp32's 2^128 for any
+// realistic cache value): O is never rescaled, so a P.V wave needs no other
+// wave's running max, only the rows' final normalisers at the end (through LDS).  A row whose scores exceed its
 // reference by more than kHeadroom raises it; the accumulated O of that row is
 // then inconsistent, and the block runs its partition again with the raised
 // references (one vote at the end of the pass).

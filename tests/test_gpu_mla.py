@@ -63,6 +63,50 @@ def test_mla_score_jump_restart():
         check(wl, num_partitions=P, inp=inp, what=f"mla score jump P={P}", ulp_rel=True)
 
 
+@pytest.mark.parametrize("jump", [58.0, 90.0], ids=["inside_headroom", "restart"])
+def test_mla_large_values_near_headroom(jump):
+    """Cache values of magnitude 2^15 with weights up to 2^58 (inside the fixed-reference
+    headroom of 2^64: no restart) or a jump of 90 (restart): the weight x value sums
+    of a partition reach about 2^81 and must stay finite and exact to the bound.  The
+    scores come from the rope part of q only (q[..., :512] = 0), so the large values
+    do not move them; 200 keys past the first tile score `jump` (log2 units) above it.
+    Both MLA kernels: the dense call, and the sparse call over an identity list."""
+    import torch
+    from decode_attention_07_amd import binding as DA
+    from gpu_util import compare, device_inputs
+    from oracle import oracle as O
+    B, H, S = 2, 128, 700
+    wl = W.Workload(f"mla_large_values_{int(jump)}", 9450 + int(jump), batch=B, num_heads=H,
+                    kv_heads=1, depth=576, depth_v=512, max_seq_len=S, mla=True,
+                    scale=1.0 / np.sqrt(192.0))
+    rng = np.random.default_rng(9450 + int(jump))
+    qpe = rng.standard_normal(64).astype(np.float32)
+    q = np.zeros((B, 1, H, 576), np.float32)
+    q[..., 512:] = qpe + 0.02 * rng.standard_normal((B, 1, H, 64)).astype(np.float32)
+    k = np.zeros((B, S, 1, 576), np.float32)
+    k[..., :512] = 2.0 ** 15 * (1.0 + 0.5 * rng.random((B, S, 1, 512), dtype=np.float32))
+    k[..., 512:] = 0.1 * rng.standard_normal((B, S, 1, 64)).astype(np.float32)
+    log2_per_dot = wl.softmax_scale * np.log2(np.e)
+    c = jump / (np.abs(qpe).sum() * log2_per_dot)  # aligned key: score ~ jump
+    hot = rng.choice(np.arange(64, S), size=(B, 200), replace=True)
+    for b in range(B):
+        k[b, hot[b], 0, 512:] = c * np.sign(qpe)
+    q16, k16 = W.f32_to_bf16_bits(q), W.f32_to_bf16_bits(k)
+    ref = O.attention(q16, k16, None, depth_v=512, scale=wl.softmax_scale, max_seq_len=S)
+    dq, dk = DA.to_device(q16), DA.to_device(k16)
+    idx = np.stack([b * S + np.arange(S) for b in range(B)]).astype(np.int32)
+    counts = np.full(B, S, np.int32)
+    for P in (1, 2):
+        out, lse = DA.mla_decode(dq, dk, scale=wl.softmax_scale, num_partitions=P)
+        compare(wl, out, lse, *ref, what=f"dense |v|~2^15 jump {jump} P={P}", ulp_rel=True)
+        out_s, lse_s = DA.mla_decode_sparse(dq, dk.reshape(B * S, 1, 576), DA.to_device(idx),
+                                            DA.to_device(counts), scale=wl.softmax_scale,
+                                            num_partitions=P)
+        compare(wl, out_s, lse_s, *ref, what=f"sparse |v|~2^15 jump {jump} P={P}",
+                ulp_rel=True)
+    torch.cuda.synchronize()
+
+
 def test_mla_partials_plus_reduce_equals_full_call():
     """mla_decode() with P > 1 equals, bit for bit, its two halves called through
     the boundary: the partials pass, then splitk_reduce()."""

@@ -49,22 +49,23 @@ def test_mla_fp8_scales(k_scale):
                   k_scale=k_scale), num_partitions=P, what=f"mla fp8 k_scale={k_scale} P={P}")
 
 
-def test_mla_fp8_unit_scale_equals_bf16_kernel():
-    """With k_scale = 1 the 8-bit form computes what mla_decode() computes on the same
-    cache converted to bf16 (exactly), bit for bit: the same tiles, partitions and
-    arithmetic, only the loads differ."""
-    wl = _wl("unit", 9660, 3, 2, 128, 520, 64, True, True, sink=True, k_scale=1.0)
+def test_mla_fp8_matches_bf16_call_on_converted_cache():
+    """The 8-bit form computes the attention of the real cache values: with k_scale =
+    1/8 (a power of two, so e4m3 x 1/8 is exact in bf16) the 8-bit call and
+    mla_decode() on the converted cache both match the oracle, element by element."""
+    from gpu_util import compare, run_oracle
+    wl = _wl("converted", 9660, 3, 2, 128, 520, 64, True, True, sink=True, k_scale=0.125)
     inp = W.make_inputs(wl)
     dev = device_inputs(inp)
-    k_bf16 = dev["k"].view(torch.float8_e4m3fn).to(torch.bfloat16)
+    k_bf16 = (dev["k"].view(torch.float8_e4m3fn).to(torch.float32) * 0.125).to(torch.bfloat16)
+    ref = run_oracle(wl, inp)
     for P in (1, 3):
         out8, lse8 = run_gpu(wl, dev, P)
         out16, lse16 = DA.mla_decode(dev["q"], k_bf16, scale=SCALE, page_table=dev["page_table"],
                                      valid_length=dev["valid_length"], max_seq_len=wl.max_seq_len,
                                      num_partitions=P, sink_weights=dev["sink"], causal=True)
-        torch.cuda.synchronize()
-        assert torch.equal(out8.view(torch.int16), out16.view(torch.int16)), f"out P={P}"
-        assert torch.equal(lse8, lse16), f"lse P={P}"
+        compare(wl, out8, lse8, *ref, what=f"8-bit call P={P}")
+        compare(wl, out16, lse16, *ref, what=f"bf16 call on the converted cache P={P}")
 
 
 def test_mla_fp8_score_jump_restart():

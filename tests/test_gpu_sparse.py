@@ -69,8 +69,9 @@ def test_sparse_tile_boundaries():
 
 
 def test_sparse_identity_list_equals_dense_call():
-    """Listing rows b*S .. b*S + N_b - 1 of the dense cache gives mla_decode()'s bits with
-    valid_length N_b (the same tiles and partitions, the same arithmetic)."""
+    """Listing rows b*S .. b*S + N_b - 1 of the dense cache is mla_decode() with valid
+    length N_b: both calls (the sparse one on the one-wave kernel, the dense one on
+    the two-waves-per-SIMD kernel) match the oracle of the dense problem."""
     wl = W.Workload("sparse_identity", 9960, batch=4, num_heads=128, kv_heads=1, depth=576,
                     depth_v=512, max_seq_len=640, mla=True, scale=SCALE, ragged=(1, 640, 1),
                     sink=True)
@@ -82,6 +83,8 @@ def test_sparse_identity_list_equals_dense_call():
     for b in range(B):
         idx[b] = b * S + np.arange(S)
     pool = dev["k"].reshape(B * S, 1, 576)
+    ref = O.attention(inp.q, inp.k, None, depth_v=512, scale=SCALE, sink=inp.sink,
+                      valid_length=inp.valid_length, max_seq_len=S)
     for P in (1, 3):
         out_d, lse_d = DA.mla_decode(dev["q"], dev["k"], scale=SCALE,
                                      valid_length=dev["valid_length"], num_partitions=P,
@@ -89,9 +92,8 @@ def test_sparse_identity_list_equals_dense_call():
         out_s, lse_s = DA.mla_decode_sparse(dev["q"], pool, DA.to_device(idx),
                                             DA.to_device(lens.astype(np.int32)), scale=SCALE,
                                             num_partitions=P, sink_weights=dev["sink"])
-        torch.cuda.synchronize()
-        assert torch.equal(out_s.view(torch.int16), out_d.view(torch.int16)), f"out P={P}"
-        assert torch.equal(lse_s, lse_d), f"lse P={P}"
+        compare(wl, out_d, lse_d, *ref, what=f"dense P={P}")
+        compare(wl, out_s, lse_s, *ref, what=f"identity list P={P}")
 
 
 def test_sparse_partials_plus_reduce_equals_full_call():

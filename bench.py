@@ -52,7 +52,9 @@ COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
 
 def kernel_sources(wl: W.Workload):
     """Source files of the partition-pass kernel a workload runs."""
-    if wl.mla:
+    if wl.mla and wl.kv_type != "e4m3" and not wl.topk:
+        main = ["mla_wave8.hip"]
+    elif wl.mla:
         main = ["mla_mfma.hip"]
     elif wl.kv_type == "e4m3":
         main = ["decode_stream_fp8.hip", "da_stream.h"]

@@ -33,7 +33,6 @@ int stream_fp8_step_keys();
 hipError_t launch_mla(const DecodeParams& p, hipStream_t s);
 hipError_t launch_mla_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_mla_wave8(const DecodeParams& p, hipStream_t s);
-bool mla_wave8_enabled();
 int mla_step_keys(int q_len);
 int mla_rows_per_block(int q_len, int num_q_heads);
 bool splitk_reduce_supported(int depth_v, int P);
@@ -260,7 +259,7 @@ __global__ void clear_queue_section(unsigned long long* q) { q[threadIdx.x] = 0u
 // The bf16 MLA problem over the contiguous, paged or ragged-KV cache runs on the
 // two-waves-per-SIMD matrix-core kernel; the sparse form on the one-wave kernel.
 bool uses_mla_wave8(const da::DecodeParams& p, Variant v) {
-  return v == kMla && !p.indices && da::mla_wave8_enabled();
+  return v == kMla && !p.indices;
 }
 
 hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16,

@@ -42,8 +42,6 @@
 // (c & ~7) | ((c & 7) ^ swz(k)) of its 72-chunk row (swz below): the K reads and
 // the transposing V^T reads are conflict-free, and each 1 KB load instruction
 // fills whole 128-byte lines (which lets the loads carry the non-temporal hint).
-#include <cstdlib>
-
 #include "da_device.h"
 
 namespace da {
@@ -519,14 +517,6 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
 }
 
 }  // namespace
-
-bool mla_wave8_enabled() {
-  static const bool on = [] {
-    const char* e = std::getenv("DA_MLA_KERNEL");
-    return !(e && e[0] == '4');
-  }();
-  return on;
-}
 
 hipError_t launch_mla_wave8(const DecodeParams& p, hipStream_t s) {
   const int n_mblocks = p.row_blocks;

@@ -36,6 +36,10 @@ hipError_t launch_mla_wave8(const DecodeParams& p, hipStream_t s);
 int mla_step_keys(int q_len);
 int mla_rows_per_block(int q_len, int num_q_heads);
 bool splitk_reduce_supported(int depth_v, int P);
+hipError_t launch_splitk_reduce_bf16_partials(const uint16_t* po, const float* pm,
+                                              const float* pl, int P, int rows, int H,
+                                              const float* sink, void* out, float* lse,
+                                              hipStream_t s);
 hipError_t launch_splitk_reduce(const float* po, const float* pm, const float* pl, int P,
                                 int rows, int H, int depth_v, const float* sink, void* out,
                                 bool bf16, float* lse, hipStream_t s);
@@ -45,6 +49,8 @@ namespace {
 
 constexpr int kMlaDepth = 576;
 constexpr int kMlaDepthV = 512;
+// Shortest partition whose dense MLA partial rows go to the merge in bf16.
+constexpr int kMlaBf16PartialKeys = 1024;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -314,6 +320,16 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
   p.out = out;
   p.lse = lse;
   p.write_partials = split ? 1 : 0;
+  // The dense MLA kernel's own split over partitions of at least kMlaBf16PartialKeys
+  // keys hands its merge bf16 partial rows, as the pages' partition kernel writes
+  // its partial output in the output type: half the bytes of the write-back and of
+  // the merge's read.  Such a partial row averages values over many keys and its
+  // rounding adds at most one bf16 rounding of the same size to the output; short
+  // partitions keep fp32 rows.
+  p.part_bf16 = (split && !partials_only && uses_mla_wave8(p, plan.variant) &&
+                 p.keys_per_partition >= kMlaBf16PartialKeys)
+                    ? 1
+                    : 0;
   float *po = nullptr, *pm = nullptr, *pl = nullptr;
   unsigned long long* queue = nullptr;
   if (split) ws_sections(workspace, P, rows, p.depth_v, &po, &pm, &pl, &queue);
@@ -357,9 +373,13 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
   }
   if (launch_partition_pass(p, plan.variant, bf16, s) != hipSuccess) return DA_ERR_HIP;
   if (!partials_only && P > 1) {
-    if (da::launch_splitk_reduce(po, pm, pl, P, (int)rows, c.num_q_heads, p.depth_v, sink, out,
-                                 bf16, lse, s) != hipSuccess)
-      return DA_ERR_HIP;
+    const hipError_t e =
+        p.part_bf16 ? da::launch_splitk_reduce_bf16_partials((const uint16_t*)po, pm, pl, P,
+                                                             (int)rows, c.num_q_heads, sink, out,
+                                                             lse, s)
+                    : da::launch_splitk_reduce(po, pm, pl, P, (int)rows, c.num_q_heads,
+                                               p.depth_v, sink, out, bf16, lse, s);
+    if (e != hipSuccess) return DA_ERR_HIP;
   }
   return DA_OK;
 }

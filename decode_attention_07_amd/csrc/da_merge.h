@@ -34,6 +34,24 @@ struct MergeCols {
   float v[EPL];
 };
 
+// EPL consecutive bf16 partial values (the dense MLA kernel's own long split).
+template <int EPL>
+__device__ __forceinline__ MergeCols<EPL> merge_load_cols(const uint16_t* p) {
+  static_assert(EPL % 8 == 0, "bf16 partial rows are read 8 values at a time");
+  MergeCols<EPL> c;
+#pragma unroll
+  for (int i = 0; i < EPL / 8; ++i) {
+    const uint4 u = *(const uint4*)(p + 8 * i);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c.v[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+      c.v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  }
+  return c;
+}
+
 template <int EPL>
 __device__ __forceinline__ MergeCols<EPL> merge_load_cols(const float* p) {
   MergeCols<EPL> c;
@@ -69,12 +87,12 @@ __device__ __forceinline__ void merge_accumulate(float (&acc)[EPL], const float 
     }
 }
 
-// Merges row `row` (of `rows` per partition) of part_o [P, rows, DV],
-// part_m / part_l [P, rows]; writes out[row, :] (bf16 or fp32) and lse[row]
-// (if lse).  Called by all 64 lanes of one wave; sink (or nullptr) is indexed by
-// row % num_heads.
-template <int DV, bool BF16OUT>
-__device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
+// Merges row `row` (of `rows` per partition) of part_o [P, rows, DV] (fp32, or
+// bf16 with PO = uint16_t), part_m / part_l [P, rows]; writes out[row, :] (bf16
+// or fp32) and lse[row] (if lse).  Called by all 64 lanes of one wave; sink (or
+// nullptr) is indexed by row % num_heads.
+template <int DV, bool BF16OUT, typename PO = float>
+__device__ __forceinline__ void merge_row(const PO* __restrict__ part_o,
                                           const float* __restrict__ part_m,
                                           const float* __restrict__ part_l, int P, int rows,
                                           int row, const float* __restrict__ sink,
@@ -84,7 +102,7 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ part_o,
   // Partial rows requested ahead: 64 values per lane in flight (8 rows at
   // DV = 512, 32 at DV <= 128, where a long split of few rows is latency bound).
   constexpr int kInFlight = (64 / EPL) < 32 ? (64 / EPL) : 32;
-  const float* orow = part_o + (size_t)row * DV + lane * EPL;
+  const PO* orow = part_o + (size_t)row * DV + lane * EPL;
   const size_t pstride = (size_t)rows * DV;
   float acc[EPL];
 #pragma unroll

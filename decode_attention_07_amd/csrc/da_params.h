@@ -31,6 +31,10 @@ struct DecodeParams {
   // contiguous piece of each key row; 0 elsewhere.
   int hb_shift;
   int write_partials;           // 1: write part_*; 0: write out / lse directly
+  // 1: part_o holds bf16 values (same [P, rows, Dv] indexing, 2 bytes each).  Set
+  // only for the internal split of the dense MLA kernel with long partitions,
+  // whose merge pass reads them back; partials handed to the caller stay fp32.
+  int part_bf16;
   float scale_log2;             // scale * log2(e) (times k_scale for an 8-bit KV cache)
   float v_scale;                // 8-bit KV cache: real value = v_scale * stored value
   // Work queue of the bf16 GQA kernel (ragged split calls; nullptr otherwise):

@@ -493,9 +493,9 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
     if (r2 >= nrows) continue;
     const float inv = rinv[row];
     const size_t orow = (row0q + r2 / H) * H + r2 % H;
-    if (p.write_partials) {
-      float* dst = p.part_o + ((size_t)pidx * (size_t)p.rows_total + orow) * kDv + kCols * wq +
-                   4 * hg;
+    const size_t prow = (size_t)pidx * (size_t)p.rows_total + orow;
+    if (p.write_partials && !p.part_bf16) {
+      float* dst = p.part_o + prow * kDv + kCols * wq + 4 * hg;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -503,8 +503,10 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
           *(float4*)(dst + 32 * ct + 8 * q) =
               make_float4(acc[ct][rt][4 * q + 0] * inv, acc[ct][rt][4 * q + 1] * inv,
                           acc[ct][rt][4 * q + 2] * inv, acc[ct][rt][4 * q + 3] * inv);
-    } else {
-      uint16_t* dst = (uint16_t*)p.out + orow * kDv + kCols * wq + 4 * hg;
+    } else {  // the bf16 output, or bf16 partials (row prow of part_o)
+      uint16_t* dst = (p.write_partials ? (uint16_t*)p.part_o + prow * kDv
+                                        : (uint16_t*)p.out + orow * kDv) +
+                      kCols * wq + 4 * hg;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll

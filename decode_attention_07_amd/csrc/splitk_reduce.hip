@@ -18,15 +18,15 @@ constexpr int kWaves = 4;          // rows per block
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxP = 1024;
 
-template <int DV, bool BF16OUT>
+template <int DV, bool BF16OUT, typename PO>
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_m,
+    const PO* __restrict__ part_o, const float* __restrict__ part_m,
     const float* __restrict__ part_l, int P, int rows, int num_heads,
     const float* __restrict__ sink, void* __restrict__ out, float* __restrict__ lse) {
   const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole wave; nothing below synchronises the block
-  merge_row<DV, BF16OUT>(part_o, part_m, part_l, P, rows, row, sink, num_heads, out, lse,
-                         threadIdx.x & 63);
+  merge_row<DV, BF16OUT, PO>(part_o, part_m, part_l, P, rows, row, sink, num_heads, out, lse,
+                             threadIdx.x & 63);
 }
 
 // Rows split into 33..64 partitions at DV <= 128 (a long sequence over few
@@ -104,11 +104,11 @@ hipError_t launch_reduce_dv(const float* po, const float* pm, const float* pl, i
   }
   const int grid = (rows + kWaves - 1) / kWaves;
   if (bf16)
-    hipLaunchKernelGGL((splitk_reduce_kernel<DV, true>), dim3(grid), dim3(kThreads), 0, s, po,
-                       pm, pl, P, rows, H, sink, out, lse);
+    hipLaunchKernelGGL((splitk_reduce_kernel<DV, true, float>), dim3(grid), dim3(kThreads), 0, s,
+                       po, pm, pl, P, rows, H, sink, out, lse);
   else
-    hipLaunchKernelGGL((splitk_reduce_kernel<DV, false>), dim3(grid), dim3(kThreads), 0, s, po,
-                       pm, pl, P, rows, H, sink, out, lse);
+    hipLaunchKernelGGL((splitk_reduce_kernel<DV, false, float>), dim3(grid), dim3(kThreads), 0,
+                       s, po, pm, pl, P, rows, H, sink, out, lse);
   return hipGetLastError();
 }
 
@@ -118,6 +118,17 @@ bool splitk_reduce_supported(int depth_v, int P) {
   return (depth_v == 64 || depth_v == 128 || depth_v == 256 || depth_v == 512 ||
           depth_v == 1024) &&
          P >= 1 && P <= kMaxP;
+}
+
+hipError_t launch_splitk_reduce_bf16_partials(const uint16_t* po, const float* pm,
+                                              const float* pl, int P, int rows, int H,
+                                              const float* sink, void* out, float* lse,
+                                              hipStream_t s) {
+  // bf16 partial O of the 512-wide MLA rows, bf16 output
+  const int grid = (rows + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL((splitk_reduce_kernel<512, true, uint16_t>), dim3(grid), dim3(kThreads), 0,
+                     s, po, pm, pl, P, rows, H, sink, out, lse);
+  return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const float* po, const float* pm, const float* pl, int P,

@@ -37,7 +37,8 @@
 // every half.  Group 0: scores of tile t in half 2t, its P.V in half 2t + 1;
 // group 1 one half later.  A tile is read in halves 2t .. 2t + 2; the 4-stage
 // ring keeps two tiles in flight (tile t + 4 is requested, by group 0, at the
-// start of half 2t + 3, into the stage tile t left).
+// start of half 2t + 3, into the stage tile t left; tiles 0 and 1 before the
+// loop, 2 and 3 at the start of half 1).
 // LDS stage layout: row-major, chunk c (16 bytes) of key k at position
 // (c & ~7) | ((c & 7) ^ swz(k)) of its 72-chunk row (swz below): the K reads and
 // the transposing V^T reads are conflict-free, and each 1 KB load instruction
@@ -391,10 +392,13 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
     // Rows outside the fold get Q = 0; a negative scale flips Q's sign (exact).
     const uint32_t qx = p.scale_log2 < 0.f ? 0x80008000u : 0u;
     for (int pass = 0;; ++pass) {  // one pass over the partition; repeated after a restart
-      // Tiles 0..3 requested; tile 0 landed (the Q loads before it, on the first pass).
+      // Tiles 0 and 1 requested; tile 0 landed (the Q loads before it, on the first
+      // pass).  Every block starts at once and needs its Q and first tile before any
+      // work: the fewer tile bytes in that first burst, the sooner it ends.  Tiles 2
+      // and 3 follow at the start of half 1.
       if (grp == 0) {
-        for (int t = 0; t < 4 && t < n_tot; ++t) issue(t);
-        wait_tiles(min(n_tot - 1, 3));
+        for (int t = 0; t < 2 && t < n_tot; ++t) issue(t);
+        wait_tiles(min(n_tot - 1, 1));
       }
       if (pass == 0) {
 #pragma unroll
@@ -413,8 +417,13 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
         for (int t = 0; t < n_tot; ++t) {
           score_tile(t);
           __syncthreads();
-          // Tile t + 3 into the stage tile t - 1 left (tiles 0..3 came first).
-          if (t >= 1 && t + 3 < n_tot) issue(t + 3);
+          // Tile t + 3 into the stage tile t - 1 left (tiles 2 and 3 in half 1).
+          if (t == 0) {
+            if (2 < n_tot) issue(2);
+            if (3 < n_tot) issue(3);
+          } else if (t + 3 < n_tot) {
+            issue(t + 3);
+          }
           wave_pv(smem + (t & (kStages - 1)) * kTileBytes, pgrp, vofs0, vofs1, pofs, wq, acc);
           if (t + 1 < n_tot) wait_tiles(min(2, n_tot - 2 - t));  // tile t + 1 landed
           __syncthreads();

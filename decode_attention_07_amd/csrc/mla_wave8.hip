@@ -408,6 +408,12 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
           qf[q] = row_ok ? __builtin_bit_cast(bf16x8_t, u) : bf16x8_t{};
         }
       }
+      // The Q registers pass through an empty asm: from here on the compiler sees
+      // them as defined, not as loads that may still be in flight.  Otherwise it
+      // re-waits for them before every score MFMA of the loop, and the hardware
+      // count it waits on also holds this wave's tile loads.
+#pragma unroll
+      for (int q = 0; q < kKS; ++q) asm volatile("" : "+v"(qf[q]));
       __syncthreads();  // tile 0 visible
       // Half h: group 0 scores tile t in half 2t and does its P.V in half 2t + 1;
       // group 1 runs one half behind.  One block barrier per half, the same count in

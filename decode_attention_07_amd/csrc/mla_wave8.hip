@@ -24,10 +24,10 @@
 // by the row's first visible tile; weights up to 2^kHeadroom = 2^64, so that
 // weight x value sums over a partition stay far below fp32's 2^128 for any
 // realistic cache value): O is never rescaled, so a P.V wave needs no other
-// wave's running max, only the rows' final normalisers at the end (through LDS).  A row whose scores exceed its
-// reference by more than kHeadroom raises it; the accumulated O of that row is
-// then inconsistent, and the block runs its partition again with the raised
-// references (one vote at the end of the pass).
+// wave's running max, only the rows' final normalisers at the end (through
+// LDS).  A row whose scores exceed its reference by more than kHeadroom raises
+// it; the accumulated O of that row is then inconsistent, and the block runs its
+// partition again with the raised references (one vote at the end of the pass).
 //
 // The two groups run half an iteration apart (ping-pong): in every half, one
 // group does the scores and softmax of a tile (K reads from LDS, 16x16x32
@@ -102,7 +102,8 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ uint32_t dma_chunk(int wave, int i, int lane) {
   return 64u * (uint32_t)(wave + kDmaWaves * i) + (uint32_t)lane;
 }
-__device__ __forceinline__ int dma_key(uint32_t c) { return (int)(((c >> 3) * 57u) >> 9); }  // c / 72
+// c / 72 (exact for c < 2304: (c / 8) * 57 / 512 = floor(c / 72) on this range)
+__device__ __forceinline__ int dma_key(uint32_t c) { return (int)(((c >> 3) * 57u) >> 9); }
 
 __device__ __forceinline__ void dma_table_init(uint16_t* tab, int wave, int lane) {
   const int l7 = lane & 7;
@@ -229,11 +230,6 @@ __device__ __forceinline__ void wave_pv(const char* vbuf, const char* pbuf, uint
     }
   }
 }
-
-template <bool V>
-struct BoolTag {
-  static constexpr bool value = V;
-};
 
 __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int n_mblocks,
                                                                int n_work) {

@@ -50,5 +50,31 @@ __device__ __forceinline__ size_t stream_row0(const DecodeParams& p, int b, int 
   return seq_kv_row0(p, b) + j0;
 }
 
+// A split item whose partition holds no visible key of any of its rows (a
+// partition past the end of a short sequence): its partial rows are the empty
+// ones, O = 0, m = -inf, l = 0, exactly what the whole item would store, without
+// its Q loads and its merge of the waves through LDS.  Rows numbered as in the
+// items' epilogues.  Called by all threads of the block.
+template <int D>
+__device__ __forceinline__ void stream_store_empty(const DecodeParams& p, int b, int g,
+                                                   int pidx, int rb) {
+  const int rps = 4 - p.hb_shift;  // log2 of the rows per head slot
+  const int nrows = seq_tokens(p, b) * p.group;
+  const size_t row0q = seq_row0(p, b);
+  for (int idx = threadIdx.x; idx < 16 * D; idx += blockDim.x) {
+    const int r = idx / D;
+    const int d = idx % D;
+    const int rrow = rb * 16 + (r & ((1 << rps) - 1));
+    if (rrow >= nrows) continue;
+    const int h = (g + (r >> rps)) * p.group + rrow % p.group;
+    const size_t row = (row0q + rrow / p.group) * p.num_q_heads + h;
+    const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
+    p.part_o[prow * D + d] = 0.f;
+    if (d == 0) {
+      p.part_m[prow] = kNegInf;
+      p.part_l[prow] = 0.f;
+    }
+  }
+}
 
 }  // namespace da

@@ -187,7 +187,7 @@ __device__ __forceinline__ void stream_tile(const char* st, const bf16x8_t (&qf)
 // over partition pidx.  With hb_shift > 0 (then rb = 0) the 16 rows are 2^hb_shift
 // slots of 16 >> hb_shift rows, slot s holding the token-major fold of KV head
 // g + s, and a score of a row against a stage row of another head is masked out.
-template <int D, int NS>
+template <int D, int NS, bool EMPTY_EXIT>
 __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, int b, int g,
                                             int pidx, int rb) {
   using C = StreamCfg<D, NS>;
@@ -218,6 +218,10 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
   }
   const int hmin = max(k_lo, __builtin_amdgcn_readfirstlane(hmin_l));
   const int hmax = max(k_lo, __builtin_amdgcn_readfirstlane(hmax_l));
+  if (EMPTY_EXIT && p.write_partials && hmax == k_lo) {  // no visible key (uniform)
+    stream_store_empty<D>(p, b, g, pidx, rb);
+    return;
+  }
 
   // Q^T operand: k-slot (g16, j) of depth step s <-> depth 32 s + 8 g16 + j.
   bf16x8_t qf[C::KS];
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
     if (work >= n_work) return;  // padding block: no barrier reached yet
     const int g = (work % n_hg) << p.hb_shift;
     work /= n_hg;
-    stream_item<D, NS>(p, smem, work % p.batch, g, work / p.batch, rb);
+    stream_item<D, NS, false>(p, smem, work % p.batch, g, work / p.batch, rb);
     return;
   }
   // s_next is double-buffered: slot it & 1 is written again two barriers after
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeParams p) {
     int w = item;
     const int g = (w % n_hg) << p.hb_shift;
     w /= n_hg;
-    stream_item<D, NS>(p, smem, w % p.batch, g, w / p.batch, 0);
+    stream_item<D, NS, true>(p, smem, w % p.batch, g, w / p.batch, 0);
     __syncthreads();  // the LDS is free again
   }
   if (threadIdx.x == 0) {

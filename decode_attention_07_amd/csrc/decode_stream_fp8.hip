@@ -189,6 +189,7 @@ __device__ __forceinline__ void fp8_tile(const char* st, const bf16x8_t (&qf)[Fp
 // over partition pidx; with hb_shift > 0 (then rb = 0) the 16 rows are 2^hb_shift
 // slots of 16 >> hb_shift rows, slot s holding the fold of KV head g + s, and a
 // score of a row against a stage row of another head is masked out.
+template <bool EMPTY_EXIT>
 __device__ __forceinline__ void fp8_item(const DecodeParams& p, char* smem, int b, int g,
                                          int pidx, int rb) {
   using C = Fp8Cfg;
@@ -218,6 +219,10 @@ __device__ __forceinline__ void fp8_item(const DecodeParams& p, char* smem, int 
   }
   const int hmin = max(k_lo, __builtin_amdgcn_readfirstlane(hmin_l));
   const int hmax = max(k_lo, __builtin_amdgcn_readfirstlane(hmax_l));
+  if (EMPTY_EXIT && p.write_partials && hmax == k_lo) {  // no visible key (uniform)
+    stream_store_empty<D>(p, b, g, pidx, rb);
+    return;
+  }
 
   // Q^T operand: k-slot (g16, j) of depth step s <-> depth 32 s + 8 g16 + j.
   bf16x8_t qf[C::KS];
@@ -383,7 +388,7 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p) 
     if (work >= n_work) return;  // padding block: no barrier reached yet
     const int g = (work % n_hg) << p.hb_shift;
     work /= n_hg;
-    fp8_item(p, smem, work % p.batch, g, work / p.batch, rb);
+    fp8_item<false>(p, smem, work % p.batch, g, work / p.batch, rb);
     return;
   }
   for (int it = 0;; ++it) {
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(256) void decode_stream_fp8_kernel(DecodeParams p) 
     int w = item;
     const int g = (w % n_hg) << p.hb_shift;
     w /= n_hg;
-    fp8_item(p, smem, w % p.batch, g, w / p.batch, 0);
+    fp8_item<true>(p, smem, w % p.batch, g, w / p.batch, 0);
     __syncthreads();  // the LDS is free again
   }
   if (threadIdx.x == 0) {

@@ -103,6 +103,46 @@ def test_partials_plus_reduce_equals_decode_attention():
     assert torch.equal(lse.view(-1), lse2)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_queue_partial_rows_match_oracle_partials(kv):
+    """The partial rows of a ragged paged call on the work queue, row by row against
+    the oracle's partials: the partitions past a short sequence's end are exactly
+    empty (O = 0, m = -inf, l = 0), the others agree to the partials' tolerance."""
+    from oracle import oracle as O
+    base = W.GQA if kv == "bf16" else W.GQA_FP8
+    wl = base.with_(name="queue_partials", seed=8640, batch=9, max_seq_len=1000, page_size=64,
+                    ragged=(1, 1000, 3))
+    inp = W.make_inputs(wl)
+    dev = device_inputs(inp)
+    P = 4
+    C = -(-wl.max_seq_len // P)
+    C = -(-C // 16) * 16  # partitions of the kernel: a whole number of 16-key steps
+    common = dict(group=wl.group, scale=wl.softmax_scale, num_partitions=P,
+                  page_table=dev["page_table"], valid_length=dev["valid_length"],
+                  max_seq_len=wl.max_seq_len)
+    if kv == "bf16":
+        ws = DA.decode_attention_partials(dev["q"], dev["k"], dev["v"], **common)
+    else:
+        ws = DA.decode_attention_fp8kv_partials(dev["q"], dev["k"], dev["v"], k_scale=wl.k_scale,
+                                                v_scale=wl.v_scale, **common)
+    po, pm, pl = DA.workspace_views(ws, P, wl.batch, 1, wl.num_heads, wl.depth)
+    torch.cuda.synchronize()
+    ro, rm, rl = O.partials(inp.q, inp.k, inp.v, scale=wl.softmax_scale, num_partitions=P,
+                            keys_per_partition=C, page_table=inp.page_table,
+                            valid_length=inp.valid_length, max_seq_len=wl.max_seq_len,
+                            k_scale=wl.k_scale, v_scale=wl.v_scale)
+    go, gm, gl = (x.double().cpu().numpy() for x in (po, pm, pl))
+    empty = rl == 0
+    assert empty.sum() >= 3 * (P - 1) * wl.num_heads, "too few empty partitions"
+    assert (go[empty] == 0).all() and (gl[empty] == 0).all() and np.isneginf(gm[empty]).all()
+    full = ~empty
+    oerr = np.abs(go[full] - ro[full]).max()
+    merr = np.abs(gm[full] - rm[full]).max()
+    lerr = (np.abs(gl[full] - rl[full]) / rl[full]).max()
+    say(f"  {kv}: {empty.sum()} empty rows; O err {oerr:.2e}, m err {merr:.2e}, l rel {lerr:.2e}")
+    assert oerr < 1e-2 and merr < 1e-3 and lerr < 1e-3
+
+
 @pytest.mark.parametrize("case", [
     # (P, C, batch, heads, kv heads, depth, S): partitions past a row's keys are empty
     (6, 16, 3, 4, 2, 64, 90),

@@ -52,7 +52,7 @@ COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
 
 def kernel_sources(wl: W.Workload):
     """Source files of the partition-pass kernel a workload runs."""
-    if wl.mla and wl.kv_type != "e4m3" and not wl.topk:
+    if wl.mla and not wl.topk:
         main = ["mla_wave8.hip"]
     elif wl.mla:
         main = ["mla_mfma.hip"]

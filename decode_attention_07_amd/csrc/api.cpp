@@ -30,9 +30,9 @@ int stream_step_keys();
 int stream_rows_per_block();
 hipError_t launch_decode_stream_fp8(const DecodeParams& p, hipStream_t s);
 int stream_fp8_step_keys();
-hipError_t launch_mla(const DecodeParams& p, hipStream_t s);
-hipError_t launch_mla_fp8(const DecodeParams& p, hipStream_t s);
+hipError_t launch_mla_sparse(const DecodeParams& p, hipStream_t s);
 hipError_t launch_mla_wave8(const DecodeParams& p, hipStream_t s);
+hipError_t launch_mla_wave8_fp8(const DecodeParams& p, hipStream_t s);
 int mla_step_keys(int q_len);
 int mla_rows_per_block(int q_len, int num_q_heads);
 bool splitk_reduce_supported(int depth_v, int P);
@@ -262,10 +262,11 @@ void* scratch_address() {
 // a memset: the call may be captured into a graph).  Each lane stores its own word.
 __global__ void clear_queue_section(unsigned long long* q) { q[threadIdx.x] = 0ull; }
 
-// The bf16 MLA problem over the contiguous, paged or ragged-KV cache runs on the
-// two-waves-per-SIMD matrix-core kernel; the sparse form on the one-wave kernel.
+// The MLA problem over the contiguous, paged or ragged-KV cache (bf16 or 8-bit)
+// runs on the two-waves-per-SIMD matrix-core kernel; the sparse form on the
+// one-wave kernel.
 bool uses_mla_wave8(const da::DecodeParams& p, Variant v) {
-  return v == kMla && !p.indices;
+  return (v == kMla || v == kMlaFp8) && !p.indices;
 }
 
 hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16,
@@ -274,10 +275,10 @@ hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16
     case kValu: return da::launch_decode_valu(p, s);
     case kStream: return da::launch_decode_stream(p, s);
     case kStreamFp8: return da::launch_decode_stream_fp8(p, s);
-    case kMlaFp8: return da::launch_mla_fp8(p, s);
+    case kMlaFp8: return da::launch_mla_wave8_fp8(p, s);
     default:
       if (uses_mla_wave8(p, v)) return da::launch_mla_wave8(p, s);
-      return da::launch_mla(p, s);
+      return da::launch_mla_sparse(p, s);
   }
 }
 

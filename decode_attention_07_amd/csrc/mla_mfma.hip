@@ -1,4 +1,5 @@
-// mla_mfma.hip -- matrix-core MLA decode for gfx950 ("flare_mla_decoding_dispatch").
+// mla_mfma.hip -- matrix-core sparse top-k MLA decode for gfx950 ("flare_mla_decoding_dispatch",
+// Parameters `sparse`).
 //
 // One KV head, depth 576 for q.K^T, and V = K[..., :512] taken from the same
 // cache rows (Args `k` and `kv_num_heads` of that page: V has no operand of its
@@ -37,10 +38,9 @@
 // With two tokens (256 rows) a sequence needs two blocks that read the same
 // tiles; their block ids differ by a multiple of 8 so that both land on the same
 // XCD and the second read of each tile is served by that XCD's L2.
-// Two more forms of the same kernel change only how a tile reaches its stage:
-// the sparse form gathers the tile's 32 keys from a list of pool rows (its row
-// indices reach LDS two tiles ahead), and the 8-bit form stages e4m3 rows in a
-// ring of its own and converts them into the bf16 stage layout.
+// The tile's 32 keys are gathered from a list of pool rows (their row indices
+// reach LDS ahead of the tile).  The dense MLA forms (bf16 and 8-bit caches) run
+// on the two-waves-per-SIMD kernel instead.
 #include "da_device.h"
 
 namespace da {
@@ -86,70 +86,9 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
-// Load instruction n (n = wave + 4 i) of a tile writes stage chunks 64 n + lane:
-// chunk position q = (64 n + lane) % 72 of key (64 n + lane) / 72, which holds the
-// key's chunk q ^ swz(key).  As 72 is a multiple of 8, q % 8 = lane % 8 and the
-// source offset is 16 (64 n + lane) + 16 (((lane % 8) ^ swz(key)) - lane % 8).
-// Each lane's 9 offsets are computed once and kept in LDS (registers are all in
-// use), packed as offset * 32 + key.
+// Each lane's load offsets are computed once and kept in LDS (registers are all
+// in use).
 constexpr int kTabPerLane = 12;  // 9 used; 48 bytes per lane keeps 16-byte reads aligned
-
-__device__ __forceinline__ void dma_table_init(uint32_t* tab, int wave, int lane) {
-  const int l7 = lane & 7;
-#pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const uint32_t c = 64u * (uint32_t)(wave + kWaves * i) + (uint32_t)lane;
-    const int key = (int)(c / 72u);
-    const uint32_t off = 16u * c + 16u * (uint32_t)((l7 ^ swz(key)) - l7);
-    tab[i] = off * 32u + (uint32_t)key;
-  }
-}
-
-// First cache row of the tile at key j0 (a tile never straddles a page).  The
-// page-table entry is read through the scalar cache (uniform index, table constant
-// during the call); its address is pinned to scalar registers first, or the
-// compiler, keeping it in vector registers under register pressure, would make the
-// read a vector load, whose wait would also wait for every tile load in flight.
-__device__ __forceinline__ size_t mla_row0(const DecodeParams& p, int b, int j0) {
-  if (p.page_table) {
-    const uint64_t a = pin_uniform_u64(
-        (uint64_t)(p.page_table + (size_t)b * p.max_pages + (size_t)(j0 >> p.page_shift)));
-    const uint32_t phys = *(const __attribute__((address_space(4))) uint32_t*)a;
-    return ((size_t)phys << p.page_shift) + (size_t)(j0 & ((1 << p.page_shift) - 1));
-  }
-  return seq_kv_row0(p, b) + j0;
-}
-
-// Requests the 32-key tile starting at key j0 into one LDS stage.  Keys at or
-// past `kend` fetch the same chunk of the tile's first key instead (finite data;
-// those keys are masked out of the softmax), so every wave issues exactly
-// kDmaPerWave instructions.
-__device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage, int b, int j0,
-                                          int kend, int wave, const uint32_t* tab) {
-  const size_t row0 = mla_row0(p, b, j0);
-  // Uniform by construction; pinned to scalar registers (the loads take a
-  // scalar base) even where it reaches here through a phi after a divergent branch.
-  const size_t off0 = row0 * kRowBytes;
-  const size_t off = pin_uniform_u64(off0);
-  const char* base = (const char*)p.k + off;
-  const int nvalid = kend - j0;
-  const uint4 t0 = *(const uint4*)tab;
-  const uint4 t1 = *(const uint4*)(tab + 4);
-  const uint32_t e[kDmaPerWave] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w, tab[8]};
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(stage + wave * 1024);
-  if (nvalid >= kBN) {  // whole tile (uniform branch)
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) dma16(base, e[i] >> 5, dst + i * kWaves * 1024);
-  } else {
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
-      uint32_t off = e[i] >> 5;
-      const int key = (int)(e[i] & 31u);
-      if (key >= nvalid) off -= (uint32_t)key * kRowBytes;
-      dma16(base, off, dst + i * kWaves * 1024);
-    }
-  }
-}
 
 // Sparse top-k lists ("flare_mla_decoding_dispatch", Parameters `sparse`, Args
 // `d_indices`, `indices_stride`, `topk_lengths`): the 32 keys of a tile are
@@ -228,84 +167,6 @@ __device__ __forceinline__ void mla_issue_sparse(const DecodeParams& p, uint32_t
     const int lo = sp_lo(i);
     const uint32_t row = (lo == 7 || lane < sp_split(i)) ? off[lo] : off[lo + 1];
     dma16(p.k, row + e[i], dst + i * 1024);
-  }
-}
-
-// 8-bit e4m3 cache with bf16 q ("flare_mla_decoding_dispatch", Parameters
-// `dtype`, Args `output`): a cache row is 576 bytes.  A tile's rows reach LDS in
-// a 2-slot staging ring of 18 KB, each wave loading its own 8 keys (18 loads of
-// 256 bytes); after its P.V each wave converts those same bytes into the bf16
-// stage layout above (a 3-slot ring here), so the scores, the softmax and P.V
-// run unchanged.  A wave converts only what it loaded itself, so its own vmcnt
-// wait orders the conversion after the loads, and the tile's barrier makes the
-// converted stage visible to the other waves.
-constexpr int kF8Row = kD;                           // bytes per cache row
-constexpr int kF8Tile = kF8Row * kBN;                // 18 KB
-constexpr int kF8WaveBytes = kF8Tile / kWaves;       // keys 8w .. 8w + 7 of a tile
-constexpr int kF8DmaPerWave = kF8WaveBytes / 256;    // 18
-constexpr int kF8Pieces = kF8WaveBytes / (64 * 8);   // 9 eight-byte pieces per lane
-constexpr int kBStagesF8 = 3;
-constexpr int kF8Ring0 = kBStagesF8 * kTileBytes;    // the staging ring follows the bf16 stages
-static_assert(kF8Ring0 + 2 * kF8Tile <= kStages * kTileBytes, "8-bit rings fit the stage array");
-static_assert(kF8Pieces <= kTabPerLane, "conversion table fits");
-
-// 4 bytes per lane from base + voff into LDS at lds_base + 4 * lane, non-temporal.
-// (No immediate offset: on these loads it would move the LDS destination too.)
-__device__ __forceinline__ void dma4_nt(const void* base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("global_load_lds_dword %0, %1 nt" : : "v"(voff), "s"(base), "{m0}"(lds_base)
-               : "memory");
-}
-
-// bf16-stage byte offset of the 8 elements that 8-byte piece j (byte 512 j + 8 lane
-// of the wave's 8 keys) converts to: chunk c of key k at position c ^ swz(k).
-__device__ __forceinline__ void f8_table_init(uint32_t* tab, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < kF8Pieces; ++j) {
-    const int o = 512 * j + 8 * lane;
-    const int key = 8 * wave + o / kF8Row;
-    const int c = (o % kF8Row) / 8;
-    tab[j] = (uint32_t)(key * kRowBytes + 16 * ((c & ~7) | ((c & 7) ^ swz(key))));
-  }
-}
-
-// Requests this wave's 8 keys of the 32-key tile at j0 into a staging slot.  Keys
-// at or past kend load the tile's first key instead (finite data, masked out of
-// the softmax), so every wave issues exactly kF8DmaPerWave loads.
-__device__ __forceinline__ void mla_issue_fp8(const DecodeParams& p, uint32_t fstage, int b,
-                                              int j0, int kend, int wave, int lane) {
-  const char* base = (const char*)p.k + pin_uniform_u64(mla_row0(p, b, j0) * kF8Row);
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(fstage + wave * kF8WaveBytes);
-  const uint32_t o0 = (uint32_t)(kF8WaveBytes * wave) + 4u * (uint32_t)lane;
-  const int nvalid = kend - j0;
-  if (nvalid >= kBN) {  // whole tile (uniform branch): one offset register, the base moves
-#pragma unroll
-    for (int i = 0; i < kF8DmaPerWave; ++i) dma4_nt(base + 256 * i, o0, dst + 256u * i);
-  } else {
-    // The lane's offsets are recomputed here from an opaque copy of o0, so that
-    // the compiler does not keep all 18 (and their keys) live across the loop.
-    uint32_t oq;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(oq) : "v"(o0));
-#pragma unroll
-    for (int i = 0; i < kF8DmaPerWave; ++i) {
-      uint32_t o = oq + 256u * i;
-      const uint32_t key = o / (uint32_t)kF8Row;
-      if ((int)key >= nvalid) o -= key * (uint32_t)kF8Row;
-      dma4_nt(base, o, dst + 256u * i);
-    }
-  }
-}
-
-// This wave's 8 keys of a staged 8-bit tile -> the bf16 stage (exact conversion).
-__device__ __forceinline__ void mla_convert_fp8(const char* fst, char* bst, int wave, int lane,
-                                                const uint32_t* tab) {
-  const char* src = fst + kF8WaveBytes * wave + 8 * lane;
-  const uint4 t0 = *(const uint4*)tab;
-  const uint4 t1 = *(const uint4*)(tab + 4);
-  const uint32_t e[kF8Pieces] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w, tab[8]};
-#pragma unroll
-  for (int j = 0; j < kF8Pieces; ++j) {
-    const uint2 w = *(const uint2*)(src + 512 * j);
-    *(bf16x8_t*)(bst + e[j]) = fp8x8_to_bf16(w.x, w.y);
   }
 }
 
@@ -598,16 +459,10 @@ struct BoolTag {
   static constexpr bool value = V;
 };
 
-// SPARSE: keys from a top-k list of pool rows (p.indices) instead of the
-// contiguous or paged cache.  FP8: the cache holds e4m3 elements (real value =
-// k_scale x stored; k_scale is folded into scale_log2, and v_scale, the same
-// factor for the value slice, multiplies the output).
-template <bool SPARSE, bool FP8>
+// Keys from a top-k list of pool rows (p.indices).
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
-  static_assert(!(SPARSE && FP8), "no sparse 8-bit form");
-  // loads per wave per tile request
-  constexpr int kIssue = FP8 ? kF8DmaPerWave : kDmaPerWave + (SPARSE ? 1 : 0);
+  constexpr int kIssue = kDmaPerWave + 1;  // loads per wave per tile request (the tile, its indices)
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
   // XCD-aware decode of the block id: blocks i and i + 8 share an XCD; the
   // n_mblocks row blocks of one (partition, sequence) get ids 8 apart.
@@ -683,85 +538,38 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   __shared__ __attribute__((aligned(16))) int votes[2][kWaves];
   __shared__ __attribute__((aligned(16))) uint32_t dma_tab[kThreads * kTabPerLane];
   const uint32_t* tab = dma_tab + threadIdx.x * kTabPerLane;  // this lane's own entries
-  if constexpr (SPARSE)
-    dma_table_init_sparse(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
-  else if constexpr (FP8)
-    f8_table_init(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
-  else
-    dma_table_init(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
-  // bf16 stage of tile t: a 4-slot ring, or 3 slots when the 8-bit staging ring
-  // takes the rest of the array.
-  // (The 3-slot index passes through an empty asm: left visible, the compiler
-  // keeps per-slot copies of the operand offsets live and spills the Q operand.)
-  auto bstage = [&](int t) __attribute__((always_inline)) {
-    if constexpr (FP8) {
-      int st = __builtin_amdgcn_readfirstlane(t % kBStagesF8);
-      asm volatile("" : "+s"(st));
-      return st;
-    } else {
-      return t & (kStages - 1);
-    }
-  };
+  dma_table_init_sparse(dma_tab + threadIdx.x * kTabPerLane, wave, lane);
+  auto bstage = [&](int t) __attribute__((always_inline)) { return t & (kStages - 1); };
   // Sparse lists: row indices of tiles t, t + 1, t + 2 sit in slots t % 4 ..
   // (t + 2) % 4 when tile t is requested.
   __shared__ __attribute__((aligned(16))) int32_t sp_slots[kSpSlots * kWaves * 8];
   auto issue = [&](int t) __attribute__((always_inline)) {
     const uint32_t stage = lds0 + (uint32_t)((t & (kStages - 1)) * kTileBytes);
-    if constexpr (FP8)
-      mla_issue_fp8(p, lds0 + (uint32_t)(kF8Ring0 + (t & 1) * kF8Tile), b, k_lo + t * kBN,
-                    hmax, wave, lane);
-    else if constexpr (SPARSE)
-      mla_issue_sparse(p, stage, b, t, k_lo, hmax, wave, lane, tab, sp_slots,
-                       (uint32_t)(uintptr_t)sp_slots);
-    else
-      mla_issue(p, stage, b, k_lo + t * kBN, hmax, wave, tab);
+    mla_issue_sparse(p, stage, b, t, k_lo, hmax, wave, lane, tab, sp_slots,
+                     (uint32_t)(uintptr_t)sp_slots);
   };
   // Sparse lists: the indices of tiles 0, 1 and 2, waited for before tile 0 is
   // requested.
   auto prime = [&]() __attribute__((always_inline)) {
-    if constexpr (SPARSE) {
-      for (int t = 0; t < 3; ++t)
-        sp_rows_issue(p, b, t, k_lo, hmax, wave, lane,
-                      (uint32_t)(uintptr_t)sp_slots + (uint32_t)((t * kWaves + wave) * 32));
-      wait_vm_lgkm0<0>();
-    }
-  };
-  // 8-bit cache: this wave's keys of staged tile t -> bf16 stage of tile t.
-  auto convert = [&](int t) __attribute__((always_inline)) {
-    if constexpr (FP8)
-      mla_convert_fp8(smem + kF8Ring0 + (t & 1) * kF8Tile, smem + bstage(t) * kTileBytes, wave,
-                      lane, tab);
+    for (int t = 0; t < 3; ++t)
+      sp_rows_issue(p, b, t, k_lo, hmax, wave, lane,
+                    (uint32_t)(uintptr_t)sp_slots + (uint32_t)((t * kWaves + wave) * 32));
+    wait_vm_lgkm0<0>();
   };
   // Start of a pass: tiles 0, 1 and 2 requested (those that exist) and tile 0
   // landed, with whatever was requested before it (the Q rows on the first pass).
-  // 8-bit: tile 0 is converted before tile 2 reuses its staging slot.
   auto start_pass = [&]() __attribute__((always_inline)) {
-    if constexpr (FP8) {
-      issue(0);
-      if (n_tot > 1) {
-        issue(1);
-        wait_vm_lgkm0<kIssue>();
-      } else {
-        wait_vm_lgkm0<0>();
-      }
-      convert(0);
-      if (n_tot > 2) {
-        wait_vm_lgkm0<63>();  // the conversion's reads of the slot are done
-        issue(2);
-      }
+    prime();
+    issue(0);
+    if (n_tot > 2) {
+      issue(1);
+      issue(2);
+      wait_vm_lgkm0<2 * kIssue>();
+    } else if (n_tot > 1) {
+      issue(1);
+      wait_vm_lgkm0<kIssue>();
     } else {
-      prime();
-      issue(0);
-      if (n_tot > 2) {
-        issue(1);
-        issue(2);
-        wait_vm_lgkm0<2 * kIssue>();
-      } else if (n_tot > 1) {
-        issue(1);
-        wait_vm_lgkm0<kIssue>();
-      } else {
-        wait_vm_lgkm0<0>();
-      }
+      wait_vm_lgkm0<0>();
     }
   };
   if (n_tot > 0) {
@@ -778,7 +586,7 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     }
     const float sl = fabsf(p.scale_log2);
     const int hi4 = hi - 4 * g;  // the row's key limit, less the lane half's key offset
-    // K fragments in flight: 4 (8-bit: 3, its staging needs registers of its own)
+    // K fragments in flight
     constexpr int kKPf = 3;
     for (;;) {  // one pass over the partition; repeated only after a restart
       __syncthreads();  // tile 0 is in LDS for every wave
@@ -789,13 +597,12 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) x[j] = s0[j] + s1[j];
       }
-      // tile 1 landed (8-bit: and converted); tile 2 may stay in flight
+      // tile 1 landed; tile 2 may stay in flight
       if (n_tot > 1) {
         if (n_tot > 2)
           wait_vm_lgkm0<kIssue>();
         else
           wait_vm_lgkm0<0>();
-        convert(1);
       }
       __syncthreads();
       // One tile: returns true when the votes of the tile before it ask for a
@@ -818,16 +625,11 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
                                      smem + bstage(i) * kTileBytes, qf, kofs, vofs0, vofs1, acc,
                                      m, lsum, lsr, hi4 - (k_lo + i * kBN), sl, need);
         if (lane == 0) votes[i & 1][wave] = __builtin_amdgcn_ballot_w64(need) != 0;
-        // tile i + 2 must have landed: tile i + 3 may stay in flight (8-bit: this
-        // wave's part of staged tile i + 2, converted into the bf16 stage tile
-        // i - 1 left, last read a barrier ago)
+        // tile i + 2 must have landed: tile i + 3 may stay in flight
         if (ahead)
           wait_vm_lgkm0<kIssue>();
         else
           wait_vm_lgkm0<0>();
-        if constexpr (FP8) {
-          if (i + 2 < n_tot) convert(i + 2);
-        }
         __syncthreads();
         return (prev.x | prev.y | prev.z | prev.w) != 0;  // same votes in every wave
       };
@@ -864,7 +666,6 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
     const bool any = lsum > 0.f;
     float inv = any ? 1.f / lsr : 0.f;
-    if constexpr (FP8) inv *= p.v_scale;
     float* dst = p.part_o + prow * kDv;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
@@ -890,7 +691,6 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     }
     const bool any = L > 0.f;
     float inv = any ? c / Lr : 0.f;
-    if constexpr (FP8) inv *= p.v_scale;
     uint16_t* dst = (uint16_t*)p.out + row * kDv;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
@@ -908,25 +708,12 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
 int mla_rows_per_block(int, int) { return kRows; }
 int mla_step_keys(int) { return kBN; }
 
-hipError_t launch_mla(const DecodeParams& p, hipStream_t s) {
+hipError_t launch_mla_sparse(const DecodeParams& p, hipStream_t s) {
+  if (!p.indices) return hipErrorInvalidValue;
   const int n_mblocks = p.row_blocks;
   const int n_work = p.num_partitions * p.batch;
   const int grid = ((n_work + 7) / 8) * 8 * n_mblocks;
-  if (p.indices)
-    hipLaunchKernelGGL((mla_decode_kernel<true, false>), dim3(grid), dim3(kThreads), 0, s, p,
-                       n_mblocks, n_work);
-  else
-    hipLaunchKernelGGL((mla_decode_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, p,
-                       n_mblocks, n_work);
-  return hipGetLastError();
-}
-
-hipError_t launch_mla_fp8(const DecodeParams& p, hipStream_t s) {
-  const int n_mblocks = p.row_blocks;
-  const int n_work = p.num_partitions * p.batch;
-  const int grid = ((n_work + 7) / 8) * 8 * n_mblocks;
-  hipLaunchKernelGGL((mla_decode_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, p,
-                     n_mblocks, n_work);
+  hipLaunchKernelGGL(mla_decode_kernel, dim3(grid), dim3(kThreads), 0, s, p, n_mblocks, n_work);
   return hipGetLastError();
 }
 

@@ -70,6 +70,30 @@ constexpr int kPBytes = kRows * kPRowBytes;  // 8 KB
 constexpr int kTabPerLane = 12;              // uint16 load offsets (9 used), 24 bytes
 constexpr float kHeadroom = 64.0f;           // largest exp2 argument (log2 units)
 
+// 8-bit e4m3 cache ("flare_mla_decoding_dispatch", Parameters `dtype`): a cache
+// row is 576 bytes.  Waves 0..3 load keys 8w .. 8w + 7 of a tile (4608
+// contiguous bytes each) into a 4-slot staging ring, tile t + 3 at the start of
+// half 2t + 1 as in the bf16 form.  At the end of that half (their P.V of tile
+// t) they convert tile t + 1 into the bf16 stage layout above, so that the
+// scores, the softmax and P.V run unchanged.  Two bf16 stages suffice: in half
+// 2t + 1 tile t's stage is being read and tile t - 1's, read last in half 2t, is
+// free.  A wave converts only what it loaded itself, so its own vmcnt wait orders
+// the conversion after the loads, and the next block barrier publishes the stage.
+constexpr int kF8Row = kD;                          // bytes per cache row
+constexpr int kF8Tile = kF8Row * kBN;               // 18 KB
+constexpr int kF8WaveBytes = kF8Tile / kDmaWaves;   // 4608
+constexpr int kF8Wide = 4;                          // 1 KB loads per wave and tile
+constexpr int kF8Narrow = 2;                        // then 256-byte loads for the last 512 bytes
+constexpr int kF8Issue = kF8Wide + kF8Narrow;
+constexpr int kF8Pieces = kF8WaveBytes / (64 * 8);  // 9 eight-byte pieces per lane
+constexpr int kBStagesF8 = 2;
+constexpr int kF8Slots = 4;
+constexpr int kF8Ring0 = kBStagesF8 * kTileBytes;   // the staging ring follows the bf16 stages
+static_assert(kF8Wide * 1024 + kF8Narrow * 256 == kF8WaveBytes, "a wave's keys split into loads");
+static_assert(kF8Ring0 + kF8Slots * kF8Tile <= kStages * kTileBytes,
+              "8-bit rings fit the stage array");
+static_assert(kF8Pieces <= kTabPerLane, "conversion table fits");
+
 // Chunk swizzle of a key row (XOR inside each 8-chunk line), from key bits 1 and
 // 2.  Fitted to gfx950's LDS: a ds_read_b128 is served in four cycles of 16
 // lanes (by the measured bank-conflict counts, the lanes of one cycle share lane
@@ -85,6 +109,13 @@ __device__ __forceinline__ constexpr int swz(int key) {
 // the cache is streamed once per block.  Completion is tracked with vmcnt waits.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
   asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(base), "{m0}"(lds_base)
+               : "memory");
+}
+
+// 4 bytes per lane from base + voff into LDS at lds_base + 4 * lane, non-temporal.
+// (No immediate offset: on these loads it would move the LDS destination too.)
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dword %0, %1 nt" : : "v"(voff), "s"(base), "{m0}"(lds_base)
                : "memory");
 }
 
@@ -162,6 +193,81 @@ __device__ __forceinline__ void mla_issue(const DecodeParams& p, uint32_t stage,
   }
 }
 
+// Waves 0..3, 8-bit cache: request keys 8w .. 8w + 7 of the tile at key j0 into
+// this wave's part of a staging slot (byte 4608 w on).  A 16-byte piece never
+// straddles two keys (576 = 36 x 16); pieces of keys at or past `kend` fetch the
+// tile's first key instead, so every issuing wave has kF8Issue loads per tile.
+__device__ __forceinline__ void mla_issue_fp8(const DecodeParams& p, uint32_t fslot, int b,
+                                              int j0, int kend, int wave, int lane) {
+  const char* base = (const char*)p.k + pin_uniform_u64(mla_row0(p, b, j0) * kF8Row);
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(fslot + wave * kF8WaveBytes);
+  const uint32_t w0 = (uint32_t)(kF8WaveBytes * wave);
+  uint32_t ow = w0 + 16u * (uint32_t)lane;                // 1 KB loads
+  uint32_t on = w0 + kF8Wide * 1024u + 4u * (uint32_t)lane;  // 256-byte loads
+  const int nvalid = kend - j0;
+  if (nvalid >= kBN) {  // whole tile (uniform branch)
+#pragma unroll
+    for (int i = 0; i < kF8Wide; ++i) dma16(base, ow + 1024u * i, dst + 1024u * i);
+#pragma unroll
+    for (int i = 0; i < kF8Narrow; ++i)
+      dma4(base, on + 256u * i, dst + kF8Wide * 1024u + 256u * i);
+  } else {
+    // Opaque copies: the per-load offsets and keys are computed here, not kept live.
+    asm volatile("" : "+v"(ow), "+v"(on));
+#pragma unroll
+    for (int i = 0; i < kF8Wide; ++i) {
+      uint32_t o = ow + 1024u * i;
+      const uint32_t key = o / (uint32_t)kF8Row;
+      if ((int)key >= nvalid) o -= key * (uint32_t)kF8Row;
+      dma16(base, o, dst + 1024u * i);
+    }
+#pragma unroll
+    for (int i = 0; i < kF8Narrow; ++i) {
+      uint32_t o = on + 256u * i;
+      const uint32_t key = o / (uint32_t)kF8Row;
+      if ((int)key >= nvalid) o -= key * (uint32_t)kF8Row;
+      dma4(base, o, dst + kF8Wide * 1024u + 256u * i);
+    }
+  }
+}
+
+// 8-bit cache: the bf16-stage byte offset (below 36 KB) of the 8 elements that
+// piece j of this lane converts, byte 512 j + 8 lane of the wave's 4608.
+__device__ __forceinline__ void f8_table_init(uint16_t* tab, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < kF8Pieces; ++j) {
+    const int o = 512 * j + 8 * lane;
+    const int key = 8 * wave + o / kF8Row;
+    const int c = (o % kF8Row) / 8;  // 16-byte chunk of the bf16 row
+    tab[j] = (uint16_t)(key * kRowBytes + 16 * ((c & ~7) | ((c & 7) ^ swz(key))));
+  }
+}
+
+// This wave's keys of a staged 8-bit tile -> the bf16 stage (exact conversion).
+// Software-pipelined three pieces deep: the compiler cannot tell a store into the
+// stage from a later read of the staging slot, so it keeps them in program
+// order; piece j + 3 is read right after piece j is stored, and three reads are
+// in flight at each store (all nine at once would need more registers than the
+// P.V wave has left).
+__device__ __forceinline__ void mla_convert_fp8(const char* fslot, char* bst, int wave, int lane,
+                                                const uint16_t* tab) {
+  constexpr int kDepth = 3;
+  const char* src = fslot + kF8WaveBytes * wave + 8 * lane;
+  const uint2 t01 = *(const uint2*)tab;
+  const uint2 t23 = *(const uint2*)(tab + 4);
+  const uint2 t45 = *(const uint2*)(tab + 8);
+  const uint32_t w[5] = {t01.x, t01.y, t23.x, t23.y, t45.x};
+  uint2 x[kDepth];
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j) x[j] = *(const uint2*)(src + 512 * j);
+#pragma unroll
+  for (int j = 0; j < kF8Pieces; ++j) {
+    const uint32_t e = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
+    *(bf16x8_t*)(bst + e) = fp8x8_to_bf16(x[j % kDepth].x, x[j % kDepth].y);
+    if (j + kDepth < kF8Pieces) x[j % kDepth] = *(const uint2*)(src + 512 * (j + kDepth));
+  }
+}
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Scores of one tile for this wave's 16 rows: s[kh] = S^T[16 keys (half kh) x 16
@@ -231,8 +337,13 @@ __device__ __forceinline__ void wave_pv(const char* vbuf, const char* pbuf, uint
   }
 }
 
+// FP8: the cache holds e4m3 elements (real value = k_scale x stored; k_scale is
+// folded into scale_log2, and v_scale, the same factor for the value slice,
+// multiplies the output).
+template <bool FP8>
 __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int n_mblocks,
                                                                int n_work) {
+  constexpr int kIssue = FP8 ? kF8Issue : kDmaPerWave;  // loads per issuing wave and tile
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) char pbuf[kPBytes];
   __shared__ __attribute__((aligned(16))) uint16_t dma_tab[kDmaWaves * 64 * kTabPerLane];
@@ -295,7 +406,12 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   uint16_t* tab = dma_tab + wq * 64 * kTabPerLane + lane * kTabPerLane;  // group 0's own entries
-  if (grp == 0) dma_table_init(tab, wave, lane);
+  if (grp == 0) {
+    if constexpr (FP8)
+      f8_table_init(tab, wave, lane);
+    else
+      dma_table_init(tab, wave, lane);
+  }
 
   // Per-lane LDS offsets of the operand reads.
   const uint32_t kofs = kRowBytes * l15 + ((16u * sg) ^ (16u * swz(l15)));
@@ -315,19 +431,34 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
     return kPRowBytes * srow + 16u * ((uint32_t)(2 * kh + (sg >> 1)) ^ pw_sw) + 8u * (sg & 1);
   };
 
-  // Group 0 requests the tiles.
+  // bf16 stage of tile t: a 4-slot ring, or 2 slots when the 8-bit staging ring
+  // takes the rest of the array.
+  auto bstage = [&](int t) __attribute__((always_inline)) {
+    return FP8 ? (t & (kBStagesF8 - 1)) : (t & (kStages - 1));
+  };
+  // Group 0 requests the tiles: into their bf16 stage, or into staging slot t % 4.
   auto issue = [&](int t) __attribute__((always_inline)) {
-    mla_issue(p, lds0 + (uint32_t)((t & (kStages - 1)) * kTileBytes), b, k_lo + t * kBN, hmax,
-              wave, lane, tab);
+    if constexpr (FP8)
+      mla_issue_fp8(p, lds0 + (uint32_t)(kF8Ring0 + (t & (kF8Slots - 1)) * kF8Tile), b,
+                    k_lo + t * kBN, hmax, wave, lane);
+    else
+      mla_issue(p, lds0 + (uint32_t)((t & (kStages - 1)) * kTileBytes), b, k_lo + t * kBN,
+                hmax, wave, lane, tab);
+  };
+  // 8-bit cache: this wave's keys of staged tile t -> bf16 stage of tile t.
+  auto convert = [&](int t) __attribute__((always_inline)) {
+    if constexpr (FP8)
+      mla_convert_fp8(smem + kF8Ring0 + (t & (kF8Slots - 1)) * kF8Tile,
+                      smem + bstage(t) * kTileBytes, wave, lane, tab);
   };
   // vmcnt for "the oldest requested tile landed" with `later` tiles requested after it.
   auto wait_tiles = [&](int later) __attribute__((always_inline)) {
     if (later >= 3)
-      wait_vm<3 * kDmaPerWave>();
+      wait_vm<3 * kIssue>();
     else if (later == 2)
-      wait_vm<2 * kDmaPerWave>();
+      wait_vm<2 * kIssue>();
     else if (later == 1)
-      wait_vm<kDmaPerWave>();
+      wait_vm<kIssue>();
     else
       wait_vm<0>();
   };
@@ -347,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
   auto score_tile = [&](int t) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     f32x4 sc[2];
-    wave_scores(smem + (t & (kStages - 1)) * kTileBytes, qf, kofs, sc);
+    wave_scores(smem + bstage(t) * kTileBytes, qf, kofs, sc);
     const int lim = hi4 - (k_lo + t * kBN);  // key 16 kh + 4 sg + v visible iff 16 kh + v < lim
     float x[8];
 #pragma unroll
@@ -392,9 +523,13 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
       // pass).  Every block starts at once and needs its Q and first tile before any
       // work: the fewer tile bytes in that first burst, the sooner it ends.  Tiles 2
       // and 3 follow at the start of half 1.
+      // 8-bit cache: tiles 0, 1 and 2 requested (54 KB, less than two bf16 tiles),
+      // and tile 0 converted; from then on one request per half 2t + 1.
       if (grp == 0) {
-        for (int t = 0; t < 2 && t < n_tot; ++t) issue(t);
-        wait_tiles(min(n_tot - 1, 1));
+        constexpr int kPre = FP8 ? 3 : 2;
+        for (int t = 0; t < kPre && t < n_tot; ++t) issue(t);
+        wait_tiles(min(n_tot - 1, kPre - 1));
+        convert(0);
       }
       if (pass == 0) {
 #pragma unroll
@@ -419,15 +554,19 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
         for (int t = 0; t < n_tot; ++t) {
           score_tile(t);
           __syncthreads();
-          // Tile t + 3 into the stage tile t - 1 left (tiles 2 and 3 in half 1).
-          if (t == 0) {
+          // Tile t + 3 into the stage (8-bit: the staging slot) tile t - 1 left
+          // (bf16: tiles 2 and 3 in half 1).
+          if (FP8 || t > 0) {
+            if (t + 3 < n_tot) issue(t + 3);
+          } else {
             if (2 < n_tot) issue(2);
             if (3 < n_tot) issue(3);
-          } else if (t + 3 < n_tot) {
-            issue(t + 3);
           }
-          wave_pv(smem + (t & (kStages - 1)) * kTileBytes, pgrp, vofs0, vofs1, pofs, wq, acc);
-          if (t + 1 < n_tot) wait_tiles(min(2, n_tot - 2 - t));  // tile t + 1 landed
+          wave_pv(smem + bstage(t) * kTileBytes, pgrp, vofs0, vofs1, pofs, wq, acc);
+          if (t + 1 < n_tot) {
+            wait_tiles(min(2, n_tot - 2 - t));  // tile t + 1 landed
+            convert(t + 1);  // 8-bit: into the bf16 stage tile t - 1 left
+          }
           __syncthreads();
         }
         __syncthreads();  // group 1's last P.V
@@ -436,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
         for (int t = 0; t < n_tot; ++t) {
           score_tile(t);
           __syncthreads();
-          wave_pv(smem + (t & (kStages - 1)) * kTileBytes, pgrp, vofs0, vofs1, pofs, wq, acc);
+          wave_pv(smem + bstage(t) * kTileBytes, pgrp, vofs0, vofs1, pofs, wq, acc);
           __syncthreads();
         }
       }
@@ -492,6 +631,7 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
       if (row_ok && p.lse)
         p.lse[(row0q + tok) * H + head] = L > 0.f ? (M + fast_log2(L)) * kLn2 : kNegInf;
     }
+    if constexpr (FP8) inv *= p.v_scale;
     rinv[srow] = inv;
   }
   __syncthreads();
@@ -535,7 +675,17 @@ hipError_t launch_mla_wave8(const DecodeParams& p, hipStream_t s) {
   const int n_mblocks = p.row_blocks;
   const int n_work = p.num_partitions * p.batch;
   const int grid = ((n_work + 7) / 8) * 8 * n_mblocks;
-  hipLaunchKernelGGL(mla_wave8_kernel, dim3(grid), dim3(kThreads), 0, s, p, n_mblocks, n_work);
+  hipLaunchKernelGGL(mla_wave8_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p, n_mblocks,
+                     n_work);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_wave8_fp8(const DecodeParams& p, hipStream_t s) {
+  const int n_mblocks = p.row_blocks;
+  const int n_work = p.num_partitions * p.batch;
+  const int grid = ((n_work + 7) / 8) * 8 * n_mblocks;
+  hipLaunchKernelGGL(mla_wave8_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p, n_mblocks,
+                     n_work);
   return hipGetLastError();
 }
 

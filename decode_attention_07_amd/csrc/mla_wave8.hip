@@ -501,20 +501,40 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
 #pragma unroll
       for (int v = 0; v < 4; ++v) x[4 * kh + v] = sc[kh][v];
     auto vis = [&](int j) { return (16 * (j >> 2) + (j & 3)) < lim; };
-    float mx = kNegInf;
+    // Exponents against the current reference; a key hidden from the row gets -inf
+    // (weight 0).  Every key of the tile is visible to every row of the wave on all
+    // but a partition's last tiles (uniform test; 19 is the largest key offset).
+    float nms = (m == kNegInf) ? 0.f : -m;
+    float y[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, vis(j) ? x[j] : kNegInf);
-    mx = max_xor32(max_xor16(mx));
-    mx = (mx == kNegInf) ? kNegInf : mx * sl;
-    const bool grow = mx > m + kHeadroom;
-    need = need || (grow && m != kNegInf);  // a row's first visible tile: nothing accumulated yet
-    m = grow ? mx : m;
-    const float nms = (m == kNegInf) ? 0.f : -m;
+    for (int j = 0; j < 8; ++j) y[j] = fmaf(x[j], sl, nms);
+    if (__builtin_amdgcn_ballot_w64(lim < 20) != 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = vis(j) ? y[j] : kNegInf;
+    }
+    const float ymax = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
+                             fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+    // The row max across its four lanes is needed only where the reference moves: a
+    // row's first visible tile sets it, and a score above it by more than kHeadroom
+    // raises it (and votes for a restart).  Otherwise the weights above stand.
+    if (__builtin_amdgcn_ballot_w64(ymax > kHeadroom || (m == kNegInf && ymax != kNegInf)) !=
+        0) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, vis(j) ? x[j] : kNegInf);
+      mx = max_xor32(max_xor16(mx));
+      mx = (mx == kNegInf) ? kNegInf : mx * sl;
+      const bool grow = mx > m + kHeadroom;
+      need = need || (grow && m != kNegInf);  // a row's first visible tile: nothing accumulated yet
+      m = grow ? mx : m;
+      nms = (m == kNegInf) ? 0.f : -m;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = vis(j) ? fmaf(x[j], sl, nms) : kNegInf;
+    }
     float ps = 0.f, pr = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float e = fast_exp2(fmaf(x[j], sl, nms));
-      x[j] = vis(j) ? e : 0.f;
+      x[j] = fast_exp2(y[j]);
       ps += x[j];
     }
 #pragma unroll

@@ -38,7 +38,7 @@
 // group 1 one half later.  A tile is read in halves 2t .. 2t + 2; the 4-stage
 // ring keeps two tiles in flight (tile t + 4 is requested, by group 0, at the
 // start of half 2t + 3, into the stage tile t left; tiles 0 and 1 before the
-// loop, 2 and 3 at the start of half 1).
+// loop, 2 and 3 at the start of half 1).  The 8-bit form's rings: below.
 // LDS stage layout: row-major, chunk c (16 bytes) of key k at position
 // (c & ~7) | ((c & 7) ^ swz(k)) of its 72-chunk row (swz below): the K reads and
 // the transposing V^T reads are conflict-free, and each 1 KB load instruction
@@ -354,7 +354,8 @@ __device__ __forceinline__ void wave_pv(const char* vbuf, const char* pbuf, uint
 
 // FP8: the cache holds e4m3 elements (real value = k_scale x stored; k_scale is
 // folded into scale_log2, and v_scale, the same factor for the value slice,
-// multiplies the output).
+// multiplies the output).  NT: the tile loads carry the non-temporal hint (one
+// row block per (sequence, partition); see dma16).
 template <bool FP8, bool NT>
 __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int n_mblocks,
                                                                int n_work) {

@@ -49,8 +49,9 @@ namespace {
 
 constexpr int kMlaDepth = 576;
 constexpr int kMlaDepthV = 512;
-// Shortest partition whose dense MLA partial rows go to the merge in bf16.
-constexpr int kMlaBf16PartialKeys = 1024;
+// Shortest partition (keys, or list positions of a sparse call) whose MLA partial
+// rows go to the merge in bf16.
+constexpr int kMlaBf16PartialKeys = 512;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -321,13 +322,13 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
   p.out = out;
   p.lse = lse;
   p.write_partials = split ? 1 : 0;
-  // The dense MLA kernel's own split over partitions of at least kMlaBf16PartialKeys
-  // keys hands its merge bf16 partial rows, as the pages' partition kernel writes
-  // its partial output in the output type: half the bytes of the write-back and of
-  // the merge's read.  Such a partial row averages values over many keys and its
+  // An MLA call's own split over partitions of at least kMlaBf16PartialKeys keys
+  // hands its merge bf16 partial rows, as the pages' partition kernel writes its
+  // partial output in the output type: half the bytes of the write-back and of the
+  // merge's read.  Such a partial row averages values over many keys and its
   // rounding adds at most one bf16 rounding of the same size to the output; short
   // partitions keep fp32 rows.
-  p.part_bf16 = (split && !partials_only && uses_mla_wave8(p, plan.variant) &&
+  p.part_bf16 = (split && !partials_only && (plan.variant == kMla || plan.variant == kMlaFp8) &&
                  p.keys_per_partition >= kMlaBf16PartialKeys)
                     ? 1
                     : 0;

@@ -662,10 +662,13 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   if (!row_ok) return;
   const size_t row = (row0q + tok) * H + head;
   // Lane holds O^T[d = 32*dt + 8*(j/4) + 4*g + j%4][row]: 4 consecutive d per j/4.
-  if (p.write_partials) {
-    const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
+  // Three row forms: fp32 partial rows, or one bf16 store loop for the bf16 output
+  // and the bf16 partial rows of a long split (a second bf16 loop made the
+  // allocator spill most of the accumulators).
+  const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
+  if (p.write_partials && !p.part_bf16) {
     const bool any = lsum > 0.f;
-    float inv = any ? 1.f / lsr : 0.f;
+    const float inv = any ? 1.f / lsr : 0.f;
     float* dst = p.part_o + prow * kDv;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
@@ -674,6 +677,18 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
         *(float4*)(dst + dt * 32 + q4 * 8 + g * 4) =
             make_float4(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv,
                         acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+    if (g == 0) {
+      p.part_m[prow] = any ? m * kLn2 : kNegInf;
+      p.part_l[prow] = lsum;
+    }
+    return;
+  }
+  float inv;
+  uint16_t* dst;
+  if (p.write_partials) {  // bf16 partial rows (long partitions of a full call)
+    const bool any = lsum > 0.f;
+    inv = any ? 1.f / lsr : 0.f;
+    dst = (uint16_t*)p.part_o + prow * kDv;
     if (g == 0) {
       p.part_m[prow] = any ? m * kLn2 : kNegInf;
       p.part_l[prow] = lsum;
@@ -690,17 +705,17 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
       M = M2;
     }
     const bool any = L > 0.f;
-    float inv = any ? c / Lr : 0.f;
-    uint16_t* dst = (uint16_t*)p.out + row * kDv;
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *(uint2*)(dst + dt * 32 + q4 * 8 + g * 4) =
-            make_uint2(pack_bf16(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv),
-                       pack_bf16(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv));
+    inv = any ? c / Lr : 0.f;
+    dst = (uint16_t*)p.out + row * kDv;
     if (g == 0 && p.lse) p.lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
   }
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *(uint2*)(dst + dt * 32 + q4 * 8 + g * 4) =
+          make_uint2(pack_bf16(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv),
+                     pack_bf16(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv));
 }
 
 }  // namespace

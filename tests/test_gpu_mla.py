@@ -21,6 +21,7 @@ SMALL = [
     (2, 3, 64, 150, 32, True, True),         # 3 tokens x 64 heads = 192 rows
     (1, 1, 160, 64, 0, False, False),        # 160 rows: second block 32 rows
     (2, 2, 128, 3000, 64, True, True),       # P = 3: 1024-key partitions, bf16 partial rows
+    (2, 1, 128, 1536, 0, False, True),       # P = 3: 512-key partitions, the shortest in bf16
 ]
 
 

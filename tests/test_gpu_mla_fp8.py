@@ -28,6 +28,7 @@ SMALL = [
     (2, 3, 64, 150, 32, True, True),         # 3 tokens x 64 heads = 192 rows
     (1, 1, 160, 64, 0, False, False),        # 160 rows: second block 32 rows
     (2, 1, 128, 33, 0, False, False),        # one whole tile and one key
+    (2, 1, 128, 1536, 64, False, True),      # P = 3: 512-key partitions, bf16 partial rows
 ]
 
 

@@ -30,6 +30,13 @@ SMALL = [
 ]
 
 
+def test_sparse_bf16_partial_rows():
+    """Long lists split in two (608 list positions per partition): the call's own
+    split hands its merge bf16 partial rows; ragged contexts, one of a single key."""
+    check(_wl("bf16_rows", 9961, 3, 1, 128, 2000, 1200, (1, 2000, 1), sink=True),
+          num_partitions=2)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 @pytest.mark.parametrize("P", [1, 2, 5])
 def test_sparse_small(case, P):

@@ -673,15 +673,15 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
   __syncthreads();
   // This wave's 128 columns of its group's rows: lane holds O^T[d = 128 wq + 32 ct +
   // 8 q + 4 hg + 0..3][row 64 grp + 32 rt + l31] in acc[ct][rt][4 q + 0..3].
+  if (p.write_partials && !p.part_bf16) {  // fp32 partial rows
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = grp * kGroupRows + 32 * rt + l31;
-    const int r2 = mb * kRows + row;
-    if (r2 >= nrows) continue;
-    const float inv = rinv[row];
-    const size_t orow = (row0q + r2 / H) * H + r2 % H;
-    const size_t prow = (size_t)pidx * (size_t)p.rows_total + orow;
-    if (p.write_partials && !p.part_bf16) {
+    for (int rt = 0; rt < 2; ++rt) {
+      const int row = grp * kGroupRows + 32 * rt + l31;
+      const int r2 = mb * kRows + row;
+      if (r2 >= nrows) continue;
+      const float inv = rinv[row];
+      const size_t prow =
+          (size_t)pidx * (size_t)p.rows_total + (row0q + r2 / H) * H + r2 % H;
       float* dst = p.part_o + prow * kDv + kCols * wq + 4 * hg;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
@@ -690,18 +690,42 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
           *(float4*)(dst + 32 * ct + 8 * q) =
               make_float4(acc[ct][rt][4 * q + 0] * inv, acc[ct][rt][4 * q + 1] * inv,
                           acc[ct][rt][4 * q + 2] * inv, acc[ct][rt][4 * q + 3] * inv);
-    } else {  // the bf16 output, or bf16 partials (row prow of part_o)
-      uint16_t* dst = (p.write_partials ? (uint16_t*)p.part_o + prow * kDv
-                                        : (uint16_t*)p.out + orow * kDv) +
-                      kCols * wq + 4 * hg;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *(uint2*)(dst + 32 * ct + 8 * q) =
-              make_uint2(pack_bf16(acc[ct][rt][4 * q + 0] * inv, acc[ct][rt][4 * q + 1] * inv),
-                         pack_bf16(acc[ct][rt][4 * q + 2] * inv, acc[ct][rt][4 * q + 3] * inv));
     }
+    return;
+  }
+  // bf16 rows (the output, or the partial rows of a long split) go through LDS, so
+  // that each store writes whole 256-byte pieces of four rows instead of 16 bytes
+  // of 32 rows.  Each wave stages its 64 rows x 128 columns in its own part of the
+  // idle tile ring (no tile load is in flight and every tile read ended a barrier
+  // ago), rows kStgRow bytes apart: the pad spreads the staging writes over the
+  // banks.  A wave reads back only what it wrote.
+  constexpr int kStgRow = kCols * 2 + 16;  // 272
+  static_assert(kWaves * kGroupRows * kStgRow <= kStages * kTileBytes, "staging fits the ring");
+  char* stg = smem + wave * (kGroupRows * kStgRow);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int rl = 32 * rt + l31;  // row within the group
+    const float inv = rinv[grp * kGroupRows + rl];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(uint2*)(stg + rl * kStgRow + 2 * (32 * ct + 8 * q + 4 * hg)) =
+            make_uint2(pack_bf16(acc[ct][rt][4 * q + 0] * inv, acc[ct][rt][4 * q + 1] * inv),
+                       pack_bf16(acc[ct][rt][4 * q + 2] * inv, acc[ct][rt][4 * q + 3] * inv));
+  }
+  const int chunk = lane & 15;  // 16-byte piece of the wave's 256 bytes of a row
+#pragma unroll 4
+  for (int i = 0; i < kGroupRows / 4; ++i) {
+    const int rl = 4 * i + (lane >> 4);
+    const int r2 = mb * kRows + grp * kGroupRows + rl;
+    if (r2 >= nrows) continue;
+    const size_t orow = (row0q + r2 / H) * H + r2 % H;
+    uint16_t* dst = (p.write_partials
+                         ? (uint16_t*)p.part_o + ((size_t)pidx * (size_t)p.rows_total + orow) * kDv
+                         : (uint16_t*)p.out + orow * kDv) +
+                    kCols * wq + 8 * chunk;
+    *(uint4*)dst = *(const uint4*)(stg + rl * kStgRow + 16 * chunk);
   }
 }
 

@@ -659,14 +659,11 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   mfma_settle(acc);
   lsum = sum_xor32(lsum);
   lsr = sum_xor32(lsr);
-  if (!row_ok) return;
   const size_t row = (row0q + tok) * H + head;
   // Lane holds O^T[d = 32*dt + 8*(j/4) + 4*g + j%4][row]: 4 consecutive d per j/4.
-  // Three row forms: fp32 partial rows, or one bf16 store loop for the bf16 output
-  // and the bf16 partial rows of a long split (a second bf16 loop made the
-  // allocator spill most of the accumulators).
   const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
-  if (p.write_partials && !p.part_bf16) {
+  if (p.write_partials && !p.part_bf16) {  // fp32 partial rows
+    if (!row_ok) return;
     const bool any = lsum > 0.f;
     const float inv = any ? 1.f / lsr : 0.f;
     float* dst = p.part_o + prow * kDv;
@@ -683,39 +680,58 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     }
     return;
   }
-  float inv;
-  uint16_t* dst;
-  if (p.write_partials) {  // bf16 partial rows (long partitions of a full call)
-    const bool any = lsum > 0.f;
-    inv = any ? 1.f / lsr : 0.f;
-    dst = (uint16_t*)p.part_o + prow * kDv;
-    if (g == 0) {
-      p.part_m[prow] = any ? m * kLn2 : kNegInf;
-      p.part_l[prow] = lsum;
+  // bf16 rows: the output, or the partial rows of a long split.
+  float inv = 0.f;
+  if (row_ok) {
+    if (p.write_partials) {
+      const bool any = lsum > 0.f;
+      inv = any ? 1.f / lsr : 0.f;
+      if (g == 0) {
+        p.part_m[prow] = any ? m * kLn2 : kNegInf;
+        p.part_l[prow] = lsum;
+      }
+    } else {
+      float M = m, L = lsum, Lr = lsr, c = 1.f;
+      if (p.sink) {
+        const float sig = p.sink[head] * kLog2e;
+        const float M2 = fmaxf(M, sig);
+        c = fast_exp2(M - M2);
+        const float e = fast_exp2(sig - M2);
+        L = L * c + e;
+        Lr = Lr * c + e;
+        M = M2;
+      }
+      const bool any = L > 0.f;
+      inv = any ? c / Lr : 0.f;
+      if (g == 0 && p.lse) p.lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
     }
-  } else {
-    float M = m, L = lsum, Lr = lsr, c = 1.f;
-    if (p.sink) {
-      const float sig = p.sink[head] * kLog2e;
-      const float M2 = fmaxf(M, sig);
-      c = fast_exp2(M - M2);
-      const float e = fast_exp2(sig - M2);
-      L = L * c + e;
-      Lr = Lr * c + e;
-      M = M2;
-    }
-    const bool any = L > 0.f;
-    inv = any ? c / Lr : 0.f;
-    dst = (uint16_t*)p.out + row * kDv;
-    if (g == 0 && p.lse) p.lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
   }
+  // The rows go through LDS, so that each store writes one whole 1 KB row instead
+  // of 16 bytes of 32 rows (and a single bf16 store loop: a second one made the
+  // allocator spill most of the accumulators).  Each wave stages its 32 rows in its
+  // own part of the idle tile ring (no load is in flight and every tile read ended
+  // a barrier ago), rows kStgRow bytes apart: the pad spreads the staging writes
+  // over the banks.  A wave reads back only what it wrote.
+  constexpr int kStgRow = kDv * 2 + 16;  // 1040
+  static_assert(kWaves * kWaveRows * kStgRow <= kStages * kTileBytes, "staging fits the ring");
+  char* stg = smem + wave * (kWaveRows * kStgRow);
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
-      *(uint2*)(dst + dt * 32 + q4 * 8 + g * 4) =
+      *(uint2*)(stg + c32 * kStgRow + 2 * (dt * 32 + q4 * 8 + g * 4)) =
           make_uint2(pack_bf16(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv),
                      pack_bf16(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv));
+  for (int i = 0; i < kWaveRows; ++i) {
+    const int r2 = mb * kRows + wave * kWaveRows + i;
+    if (r2 >= nrows) break;  // the wave's rows are consecutive
+    const size_t orow = (row0q + r2 / H) * H + r2 % H;
+    uint16_t* dst = (p.write_partials
+                         ? (uint16_t*)p.part_o + ((size_t)pidx * (size_t)p.rows_total + orow) * kDv
+                         : (uint16_t*)p.out + orow * kDv) +
+                    8 * lane;
+    *(uint4*)dst = *(const uint4*)(stg + i * kStgRow + 16 * lane);
+  }
 }
 
 }  // namespace

@@ -149,19 +149,27 @@ __device__ __forceinline__ void merge_factors(float mA, float mB, float& m, floa
 }
 
 // ---- per-row key limits ----------------------------------------------------------
-// Keys of sequence b visible to query token t.
+// Keys of sequence b visible to query token t.  b is uniform at every caller, and
+// the count is read through the scalar cache (the array is constant during the
+// call).  Read as an ordinary load inside a per-row branch it became a vector load
+// whose vmcnt(0) wait also waited for the block's stores still in flight: on the
+// work queue, the previous item's partial rows, at the start of every item.
 __device__ __forceinline__ int visible_keys(const DecodeParams& p, int b, int t) {
+  uint32_t raw = (uint32_t)p.max_seq_len;
+  if (p.valid_length) {
+    const uint64_t a = pin_uniform_u64((uint64_t)(p.valid_length + b));
+    raw = *(const __attribute__((address_space(4))) uint32_t*)a;
+  }
   int n;
   if (p.indices) {
     // sparse top-k counts (int32): a negative count is 0, one above the list
     // stride (max_seq_len here) is the stride
-    const int c = (int)p.valid_length[b];
+    const int c = (int)raw;
     n = c < 0 ? 0 : (c < p.max_seq_len ? c : p.max_seq_len);
   } else {
     // A length above max_seq_len counts as max_seq_len; compared as unsigned, so
     // that a length of 2^31 or more is a large count, not a negative one.
-    const uint32_t nv = p.valid_length ? p.valid_length[b] : (uint32_t)p.max_seq_len;
-    n = nv < (uint32_t)p.max_seq_len ? (int)nv : p.max_seq_len;
+    n = raw < (uint32_t)p.max_seq_len ? (int)raw : p.max_seq_len;
   }
   if (p.causal) {
     int lim = n - seq_tokens(p, b) + t + 1;

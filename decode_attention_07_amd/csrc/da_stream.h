@@ -50,6 +50,26 @@ __device__ __forceinline__ size_t stream_row0(const DecodeParams& p, int b, int 
   return seq_kv_row0(p, b) + j0;
 }
 
+// Block-uniform key range of a work item: [k_lo, hmin) is visible to every row of
+// its fold, [k_lo, hmax) to some.  The item's rows are rb * 16 + 0 .. 2^rps - 1 of
+// the token-major fold (each head slot repeats them), valid below nrows.  A row's
+// visible keys grow with its token, so the first row sets hmin and the last valid
+// one hmax: two scalar reads, where a reduction across the rows' lanes took eight
+// dependent lane swaps.  With no valid row both are k_lo (and nothing is streamed).
+__device__ __forceinline__ void item_key_range(const DecodeParams& p, int b, int rb, int rps,
+                                               int nrows, int k_lo, int& hmin, int& hmax) {
+  const int first = rb * 16;
+  const int last = min(nrows, first + (1 << rps)) - 1;
+  int lo = k_lo, hi = k_lo;
+  if (first <= last) {
+    const int k_hi = k_lo + p.keys_per_partition;
+    lo = max(k_lo, min(k_hi, visible_keys(p, b, first / p.group)));
+    hi = max(k_lo, min(k_hi, visible_keys(p, b, last / p.group)));
+  }
+  hmin = __builtin_amdgcn_readfirstlane(lo);
+  hmax = __builtin_amdgcn_readfirstlane(hi);
+}
+
 // A split item whose partition holds no visible key of any of its rows (a
 // partition past the end of a short sequence): its partial rows are the empty
 // ones, O = 0, m = -inf, l = 0, exactly what the whole item would store, without

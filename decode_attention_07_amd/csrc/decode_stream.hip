@@ -210,14 +210,8 @@ __device__ __forceinline__ void stream_item(const DecodeParams& p, char* smem, i
   const int lim = row_ok ? visible_keys(p, b, tok) : 0;
   const int hi = row_ok ? min(k_lo + p.keys_per_partition, lim) : k_lo;
   // Block-uniform key range: [k_lo, hmin) unmasked, [hmin, hmax) masked.
-  int hmin_l = row_ok ? hi : 0x7fffffff, hmax_l = hi;
-#pragma unroll
-  for (int x = 1; x < 16; x <<= 1) {
-    hmin_l = min(hmin_l, __shfl_xor(hmin_l, x, 64));
-    hmax_l = max(hmax_l, __shfl_xor(hmax_l, x, 64));
-  }
-  const int hmin = max(k_lo, __builtin_amdgcn_readfirstlane(hmin_l));
-  const int hmax = max(k_lo, __builtin_amdgcn_readfirstlane(hmax_l));
+  int hmin, hmax;
+  item_key_range(p, b, rb, rps, nrows, k_lo, hmin, hmax);
   if (EMPTY_EXIT && p.write_partials && hmax == k_lo) {  // no visible key (uniform)
     stream_store_empty<D>(p, b, g, pidx, rb);
     return;

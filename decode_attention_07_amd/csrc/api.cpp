@@ -39,7 +39,7 @@ bool splitk_reduce_supported(int depth_v, int P);
 hipError_t launch_splitk_reduce_bf16_partials(const uint16_t* po, const float* pm,
                                               const float* pl, int P, int rows, int H,
                                               const float* sink, void* out, float* lse,
-                                              hipStream_t s);
+                                              int batch, int seq_rows, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* po, const float* pm, const float* pl, int P,
                                 int rows, int H, int depth_v, const float* sink, void* out,
                                 bool bf16, float* lse, hipStream_t s);
@@ -376,9 +376,9 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
   if (launch_partition_pass(p, plan.variant, bf16, s) != hipSuccess) return DA_ERR_HIP;
   if (!partials_only && P > 1) {
     const hipError_t e =
-        p.part_bf16 ? da::launch_splitk_reduce_bf16_partials((const uint16_t*)po, pm, pl, P,
-                                                             (int)rows, c.num_q_heads, sink, out,
-                                                             lse, s)
+        p.part_bf16 ? da::launch_splitk_reduce_bf16_partials(
+                          (const uint16_t*)po, pm, pl, P, (int)rows, c.num_q_heads, sink, out, lse,
+                          c.batch, c.q_offsets ? 0 : c.q_len * c.num_q_heads, s)
                     : da::launch_splitk_reduce(po, pm, pl, P, (int)rows, c.num_q_heads,
                                                p.depth_v, sink, out, bf16, lse, s);
     if (e != hipSuccess) return DA_ERR_HIP;

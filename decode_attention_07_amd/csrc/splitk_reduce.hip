@@ -18,12 +18,21 @@ constexpr int kWaves = 4;          // rows per block
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxP = 1024;
 
+// seq_chunks > 0: the rows come in sequences of seq_chunks blocks' worth, and the
+// blocks of sequence b run on XCD b mod 8 (blocks i and i + 8 share an XCD), the
+// one whose L2 took that sequence's partial rows from its partition pass.
 template <int DV, bool BF16OUT, typename PO>
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(
     const PO* __restrict__ part_o, const float* __restrict__ part_m,
     const float* __restrict__ part_l, int P, int rows, int num_heads,
-    const float* __restrict__ sink, void* __restrict__ out, float* __restrict__ lse) {
-  const int row = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const float* __restrict__ sink, void* __restrict__ out, float* __restrict__ lse,
+    int seq_chunks = 0) {
+  int chunk = blockIdx.x;
+  if (seq_chunks > 0) {
+    const int k = blockIdx.x >> 3;
+    chunk = ((blockIdx.x & 7) + 8 * (k / seq_chunks)) * seq_chunks + k % seq_chunks;
+  }
+  const int row = chunk * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole wave; nothing below synchronises the block
   merge_row<DV, BF16OUT, PO>(part_o, part_m, part_l, P, rows, row, sink, num_heads, out, lse,
                              threadIdx.x & 63);
@@ -123,11 +132,16 @@ bool splitk_reduce_supported(int depth_v, int P) {
 hipError_t launch_splitk_reduce_bf16_partials(const uint16_t* po, const float* pm,
                                               const float* pl, int P, int rows, int H,
                                               const float* sink, void* out, float* lse,
-                                              hipStream_t s) {
-  // bf16 partial O of the 512-wide MLA rows, bf16 output
+                                              int batch, int seq_rows, hipStream_t s) {
+  // bf16 partial O of the 512-wide MLA rows, bf16 output.  The MLA partition pass
+  // runs sequence b's blocks on XCD b mod 8 when the batch is a multiple of 8; the
+  // merge of its rows is then mapped onto the same XCD (seq_rows = T * H rows per
+  // sequence, 0 when they vary).
   const int grid = (rows + kWaves - 1) / kWaves;
+  const bool xcd = batch > 0 && batch % 8 == 0 && seq_rows > 0 && seq_rows % kWaves == 0 &&
+                   (long)batch * seq_rows == rows;
   hipLaunchKernelGGL((splitk_reduce_kernel<512, true, uint16_t>), dim3(grid), dim3(kThreads), 0,
-                     s, po, pm, pl, P, rows, H, sink, out, lse);
+                     s, po, pm, pl, P, rows, H, sink, out, lse, xcd ? seq_rows / kWaves : 0);
   return hipGetLastError();
 }
 

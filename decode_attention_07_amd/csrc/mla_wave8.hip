@@ -307,11 +307,9 @@ __device__ __forceinline__ void wave_scores(const char* buf, const bf16x8_t (&qf
   for (int st = 0; st < kKS; ++st) {
     const int slot = st & 1;
     s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[slot], qf[st], st ? s[0] : f32x4{}, 0, 0, 0);
+    if (st + 2 < kKS) ra[slot] = kfrag(0, st + 2);
     s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rb[slot], qf[st], st ? s[1] : f32x4{}, 0, 0, 0);
-    if (st + 2 < kKS) {
-      ra[slot] = kfrag(0, st + 2);
-      rb[slot] = kfrag(1, st + 2);
-    }
+    if (st + 2 < kKS) rb[slot] = kfrag(1, st + 2);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -324,6 +322,15 @@ __device__ __forceinline__ void wave_scores(const char* buf, const bf16x8_t (&qf
 __device__ __forceinline__ void wave_pv(const char* vbuf, const char* pbuf, uint32_t vofs0,
                                         uint32_t vofs1, uint32_t pofs, int wq,
                                         f32x16_t (&acc)[4][2]) {
+  // V^T of column tile 4 wq + 2 cp + u for key half kh.
+  auto vfrag = [&](int kh, int cp, int u) {
+    const int dt = 4 * wq + 2 * cp + u;  // 32-column tile of the 512 value columns
+    const uint32_t x = 64u * (uint32_t)(dt & 1), y = 128u * (uint32_t)(dt >> 1) +
+                                                     16u * kRowBytes * kh;
+    return concat_bf16x8(lds_read_tr16(vbuf + ((vofs0 ^ x) + y)),
+                         lds_read_tr16(vbuf + ((vofs1 ^ x) + y)));
+  };
+  bf16x8_t a[2] = {vfrag(0, 0, 0), vfrag(0, 0, 1)};
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh) {
     bf16x8_t bq[2];  // P^T of both row tiles for this key half
@@ -332,21 +339,17 @@ __device__ __forceinline__ void wave_pv(const char* vbuf, const char* pbuf, uint
       bq[rt] = *(const bf16x8_t*)(pbuf + rt * 32 * kPRowBytes + (pofs ^ (32u * kh)));
 #pragma unroll
     for (int cp = 0; cp < 2; ++cp) {  // two column tiles at a time
-      bf16x8_t a[2];
+      const int step = 2 * kh + cp;
+      // Each V^T fragment is requested for the next step right after its second
+      // use, so that its read has the rest of this step to land.
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int dt = 4 * wq + 2 * cp + u;  // 32-column tile of the 512 value columns
-        const uint32_t x = 64u * (uint32_t)(dt & 1), y = 128u * (uint32_t)(dt >> 1) +
-                                                         16u * kRowBytes * kh;
-        a[u] = concat_bf16x8(lds_read_tr16(vbuf + ((vofs0 ^ x) + y)),
-                             lds_read_tr16(vbuf + ((vofs1 ^ x) + y)));
-      }
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int rt = 0; rt < 2; ++rt)
           acc[2 * cp + u][rt] =
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], bq[rt], acc[2 * cp + u][rt], 0, 0, 0);
+        if (step + 1 < 4) a[u] = vfrag((step + 1) >> 1, (step + 1) & 1, u);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -330,28 +330,27 @@ __device__ __forceinline__ void wave_pv(const char* vbuf, const char* pbuf, uint
     return concat_bf16x8(lds_read_tr16(vbuf + ((vofs0 ^ x) + y)),
                          lds_read_tr16(vbuf + ((vofs1 ^ x) + y)));
   };
+  auto pfrag = [&](int kh, int rt) {
+    return *(const bf16x8_t*)(pbuf + rt * 32 * kPRowBytes + (pofs ^ (32u * kh)));
+  };
   bf16x8_t a[2] = {vfrag(0, 0, 0), vfrag(0, 0, 1)};
+  bf16x8_t bq[2] = {pfrag(0, 0), pfrag(0, 1)};  // P^T of both row tiles, key half kh
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    bf16x8_t bq[2];  // P^T of both row tiles for this key half
+  for (int step = 0; step < 4; ++step) {  // (key half, pair of column tiles)
+    const int kh = step >> 1, cp = step & 1;
+    // Each fragment is requested for its next use right after its last use here,
+    // so that its read has the rest of this step to land.
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-      bq[rt] = *(const bf16x8_t*)(pbuf + rt * 32 * kPRowBytes + (pofs ^ (32u * kh)));
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-    for (int cp = 0; cp < 2; ++cp) {  // two column tiles at a time
-      const int step = 2 * kh + cp;
-      // Each V^T fragment is requested for the next step right after its second
-      // use, so that its read has the rest of this step to land.
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          acc[2 * cp + u][rt] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], bq[rt], acc[2 * cp + u][rt], 0, 0, 0);
-        if (step + 1 < 4) a[u] = vfrag((step + 1) >> 1, (step + 1) & 1, u);
+      for (int rt = 0; rt < 2; ++rt) {
+        acc[2 * cp + u][rt] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], bq[rt], acc[2 * cp + u][rt], 0, 0, 0);
+        if (step == 1 && u == 1) bq[rt] = pfrag(1, rt);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (step + 1 < 4) a[u] = vfrag((step + 1) >> 1, (step + 1) & 1, u);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 

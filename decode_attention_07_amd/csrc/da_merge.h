@@ -74,6 +74,24 @@ __device__ __forceinline__ MergeCols<EPL> merge_load_cols(const float* p) {
   return c;
 }
 
+// This lane's EPL columns of partition u's partial row.  fp32 partials: row
+// (u, row) of part_o [P, rows, DV].  Mixed partials (PO = uint16_t, the MLA
+// kernels' own long splits): partition 0's row is fp32 at (float*)part_o + row *
+// DV, partition u >= 1's is bf16 at part_o + ((u + 1) * rows + row) * DV.
+template <int DV, typename PO>
+__device__ __forceinline__ MergeCols<DV / 64> merge_part_cols(const PO* __restrict__ part_o,
+                                                              int rows, int row, int u,
+                                                              int lane) {
+  constexpr int EPL = DV / 64;
+  if constexpr (sizeof(PO) == 2) {
+    if (u == 0)
+      return merge_load_cols<EPL>((const float*)part_o + (size_t)row * DV + lane * EPL);
+    return merge_load_cols<EPL>(part_o + ((size_t)(u + 1) * rows + row) * DV + lane * EPL);
+  } else {
+    return merge_load_cols<EPL>(part_o + ((size_t)u * rows + row) * DV + lane * EPL);
+  }
+}
+
 // acc += w_u * O_u over a group of partial rows; a zero weight drops its row.
 template <int EPL, int N>
 __device__ __forceinline__ void merge_accumulate(float (&acc)[EPL], const float (&wj)[N],
@@ -87,10 +105,10 @@ __device__ __forceinline__ void merge_accumulate(float (&acc)[EPL], const float 
     }
 }
 
-// Merges row `row` (of `rows` per partition) of part_o [P, rows, DV] (fp32, or
-// bf16 with PO = uint16_t), part_m / part_l [P, rows]; writes out[row, :] (bf16
-// or fp32) and lse[row] (if lse).  Called by all 64 lanes of one wave; sink (or
-// nullptr) is indexed by row % num_heads.
+// Merges row `row` (of `rows` per partition) of the partial rows (fp32, or the
+// mixed fp32 / bf16 layout with PO = uint16_t: merge_part_cols), part_m / part_l
+// [P, rows]; writes out[row, :] (bf16 or fp32) and lse[row] (if lse).  Called by
+// all 64 lanes of one wave; sink (or nullptr) is indexed by row % num_heads.
 template <int DV, bool BF16OUT, typename PO = float>
 __device__ __forceinline__ void merge_row(const PO* __restrict__ part_o,
                                           const float* __restrict__ part_m,
@@ -102,8 +120,9 @@ __device__ __forceinline__ void merge_row(const PO* __restrict__ part_o,
   // Partial rows requested ahead: 64 values per lane in flight (8 rows at
   // DV = 512, 32 at DV <= 128, where a long split of few rows is latency bound).
   constexpr int kInFlight = (64 / EPL) < 32 ? (64 / EPL) : 32;
-  const PO* orow = part_o + (size_t)row * DV + lane * EPL;
-  const size_t pstride = (size_t)rows * DV;
+  // A slot past the partitions re-reads one already requested: partition 0, or for
+  // mixed partials the first bf16 one (P >= 2 there), so that slot u >= 1 is bf16.
+  constexpr int kSpare = sizeof(PO) == 2 ? 1 : 0;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
@@ -117,9 +136,10 @@ __device__ __forceinline__ void merge_row(const PO* __restrict__ part_o,
     const float lp_raw = part_l[(size_t)pc * rows + row];
     const float mp_raw = part_m[(size_t)pc * rows + row];
     MergeCols<EPL> c[kInFlight];
+    c[0] = merge_part_cols<DV>(part_o, rows, row, 0, lane);
 #pragma unroll
-    for (int u = 0; u < kInFlight; ++u)
-      c[u] = merge_load_cols<EPL>(orow + (size_t)(u < P ? u : 0) * pstride);
+    for (int u = 1; u < kInFlight; ++u)
+      c[u] = merge_part_cols<DV>(part_o, rows, row, u < P ? u : kSpare, lane);
     const float lp = lane < P ? lp_raw : 0.f;
     M = fmaxf(wave_max(lp > 0.f ? mp_raw * kLog2e : kNegInf), sig);
     const float Ms = (M == kNegInf) ? 0.f : M;
@@ -129,7 +149,7 @@ __device__ __forceinline__ void merge_row(const PO* __restrict__ part_o,
       if (j > 0) {  // more partitions than one group: the next group's rows
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u)
-          c[u] = merge_load_cols<EPL>(orow + (size_t)(j + u < P ? j + u : j) * pstride);
+          c[u] = merge_part_cols<DV>(part_o, rows, row, j + u < P ? j + u : j, lane);
       }
       float wj[kInFlight];
 #pragma unroll
@@ -169,7 +189,7 @@ __device__ __forceinline__ void merge_row(const PO* __restrict__ part_o,
                       ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u))
                       : 0.f;
           const int src = base + j + (wj[u] != 0.f ? u : 0);
-          c[u] = merge_load_cols<EPL>(orow + (size_t)src * pstride);
+          c[u] = merge_part_cols<DV>(part_o, rows, row, src, lane);
         }
         merge_accumulate(acc, wj, c);
       }

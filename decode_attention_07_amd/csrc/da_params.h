@@ -31,9 +31,14 @@ struct DecodeParams {
   // contiguous piece of each key row; 0 elsewhere.
   int hb_shift;
   int write_partials;           // 1: write part_*; 0: write out / lse directly
-  // 1: part_o holds bf16 values (same [P, rows, Dv] indexing, 2 bytes each).  Set
-  // only for the internal split of the dense MLA kernel with long partitions,
-  // whose merge pass reads them back; partials handed to the caller stay fp32.
+  // 1: mixed partial rows: partition 0's fp32 at part_o[row * Dv] (as with
+  // fp32 partials), partition p >= 1's bf16 at ((uint16_t*)part_o)[((p + 1) *
+  // rows + row) * Dv] (after partition 0's fp32 rows; the section is sized for
+  // P fp32 rows per row).  Set only for the internal split of the MLA kernels with
+  // long partitions, whose merge pass reads them back; partials handed to the
+  // caller stay fp32.  Partition 0 stays fp32 because a short sequence's keys all
+  // fall there: its partial row is then the whole result, of a few keys, and a
+  // bf16 rounding of it would add to the output's own rounding.
   int part_bf16;
   float scale_log2;             // scale * log2(e) (times k_scale for an 8-bit KV cache)
   float v_scale;                // 8-bit KV cache: real value = v_scale * stored value

@@ -662,7 +662,9 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
   const size_t row = (row0q + tok) * H + head;
   // Lane holds O^T[d = 32*dt + 8*(j/4) + 4*g + j%4][row]: 4 consecutive d per j/4.
   const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
-  if (p.write_partials && !p.part_bf16) {  // fp32 partial rows
+  // fp32 partial rows: every partition's of an fp32-partial split, and partition
+  // 0's of a bf16-partial one (layout in da_params.h)
+  if (p.write_partials && (!p.part_bf16 || pidx == 0)) {
     if (!row_ok) return;
     const bool any = lsum > 0.f;
     const float inv = any ? 1.f / lsr : 0.f;
@@ -727,7 +729,8 @@ void mla_decode_kernel(DecodeParams p, int n_mblocks, int n_work) {
     if (r2 >= nrows) break;  // the wave's rows are consecutive
     const size_t orow = (row0q + r2 / H) * H + r2 % H;
     uint16_t* dst = (p.write_partials
-                         ? (uint16_t*)p.part_o + ((size_t)pidx * (size_t)p.rows_total + orow) * kDv
+                         ? (uint16_t*)p.part_o +
+                               ((size_t)(pidx + 1) * (size_t)p.rows_total + orow) * kDv
                          : (uint16_t*)p.out + orow * kDv) +
                     8 * lane;
     *(uint4*)dst = *(const uint4*)(stg + i * kStgRow + 16 * lane);

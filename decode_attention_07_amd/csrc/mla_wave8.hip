@@ -675,7 +675,9 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
   __syncthreads();
   // This wave's 128 columns of its group's rows: lane holds O^T[d = 128 wq + 32 ct +
   // 8 q + 4 hg + 0..3][row 64 grp + 32 rt + l31] in acc[ct][rt][4 q + 0..3].
-  if (p.write_partials && !p.part_bf16) {  // fp32 partial rows
+  // fp32 partial rows: every partition's of an fp32-partial split, and partition
+  // 0's of a bf16-partial one (layout in da_params.h)
+  if (p.write_partials && (!p.part_bf16 || pidx == 0)) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int row = grp * kGroupRows + 32 * rt + l31;
@@ -724,7 +726,8 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
     if (r2 >= nrows) continue;
     const size_t orow = (row0q + r2 / H) * H + r2 % H;
     uint16_t* dst = (p.write_partials
-                         ? (uint16_t*)p.part_o + ((size_t)pidx * (size_t)p.rows_total + orow) * kDv
+                         ? (uint16_t*)p.part_o +
+                               ((size_t)(pidx + 1) * (size_t)p.rows_total + orow) * kDv
                          : (uint16_t*)p.out + orow * kDv) +
                     kCols * wq + 8 * chunk;
     *(uint4*)dst = *(const uint4*)(stg + rl * kStgRow + 16 * chunk);

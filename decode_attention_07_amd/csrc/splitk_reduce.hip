@@ -133,7 +133,8 @@ hipError_t launch_splitk_reduce_bf16_partials(const uint16_t* po, const float* p
                                               const float* pl, int P, int rows, int H,
                                               const float* sink, void* out, float* lse,
                                               int batch, int seq_rows, hipStream_t s) {
-  // bf16 partial O of the 512-wide MLA rows, bf16 output.  The MLA partition pass
+  // Mixed partial O of the 512-wide MLA rows (partition 0 fp32, the others bf16:
+  // da_params.h), bf16 output.  The MLA partition pass
   // runs sequence b's blocks on XCD b mod 8 when the batch is a multiple of 8; the
   // merge of its rows is then mapped onto the same XCD (seq_rows = T * H rows per
   // sequence, 0 when they vary).

@@ -68,6 +68,12 @@ CASES = [
                        max_seq_len=260, q_len=3, mla=True, causal=True, page_size=32,
                        ragged=(3, 260, 0), scale=1.0 / np.sqrt(192.0), sink=True),
      [1, 3, 0, 2]),
+    # P = 3: 576-key partitions (partial rows fp32 for partition 0, bf16 after it);
+    # 768 rows in blocks of 128 that start at each sequence's first token row
+    ("mla_long_split", dict(batch=3, num_heads=128, kv_heads=1, depth=576, depth_v=512,
+                              max_seq_len=1700, q_len=3, mla=True, causal=True,
+                              ragged=(3, 1700, 0), scale=1.0 / np.sqrt(192.0), sink=True),
+     [3, 1, 2]),
 ]
 
 

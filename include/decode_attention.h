@@ -114,6 +114,10 @@ int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_head
  *   part_max fp32 [P, rows]           partial max, natural-log units (-inf if empty)
  *   part_sum fp32 [P, rows]           partial exp-sum relative to part_max (0 if empty)
  * with rows = batch * q_len * num_q_heads.  Returns 0 for invalid arguments.
+ * The *_partials() passes leave their partials in this layout.  A full split call
+ * uses part_o as its own scratch: an MLA call over partitions of at least 512
+ * keys stores partition 0's rows there in fp32 and the others' in bf16, which its
+ * merge reads back; its contents are not part of the interface.
  *
  * Work queue.  A bf16 decode_attention() / decode_attention_partials() call
  * (or its 8-bit KV form) with valid_length, more than one partition and at most 16 query rows per KV

@@ -61,7 +61,7 @@ def kernel_sources(wl: W.Workload):
     elif wl.dtype == "bf16":
         main = ["decode_stream.hip", "da_stream.h"]
     else:
-        main = ["decode_valu.hip"]
+        main = ["decode_valu.hip", "da_merge.h"]
     return [os.path.join(CSRC, f) for f in (*main, "da_device.h", "da_params.h")]
 
 

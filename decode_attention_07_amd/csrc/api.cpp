@@ -22,7 +22,7 @@
 #include "da_params.h"
 
 namespace da {
-hipError_t launch_decode_valu(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeParams& p, unsigned* merge_count, hipStream_t s);
 int valu_step_keys(int rows_per_block);
 int valu_rows_per_block(int fold);
 hipError_t launch_decode_stream(const DecodeParams& p, hipStream_t s);
@@ -221,8 +221,11 @@ da::DecodeParams base_params(const Common& c, const void* q, const void* k, cons
 }
 
 // Workspace sections: the work-queue word (its own 256 bytes, at offset 0 so
-// that its place does not depend on P), part_o, part_max, part_sum.
+// that its place does not depend on P), part_o, part_max, part_sum.  The words of
+// the queue section after the 64-bit queue word are the merge counts of small fp32
+// split calls (kValuMergeGroups of them).
 constexpr size_t kQueueBytes = 256;
+constexpr long kValuMergeGroups = (long)(kQueueBytes - 8) / 4;
 
 void ws_sections(void* ws, int P, size_t rows, int depth_v, float** po, float** pm, float** pl,
                  unsigned long long** queue) {
@@ -271,9 +274,9 @@ bool uses_mla_wave8(const da::DecodeParams& p, Variant v) {
 }
 
 hipError_t launch_partition_pass(const da::DecodeParams& p, Variant v, bool bf16,
-                                 hipStream_t s) {
+                                 unsigned* merge_count, hipStream_t s) {
   switch (v) {
-    case kValu: return da::launch_decode_valu(p, s);
+    case kValu: return da::launch_decode_valu(p, merge_count, s);
     case kStream: return da::launch_decode_stream(p, s);
     case kStreamFp8: return da::launch_decode_stream_fp8(p, s);
     case kMlaFp8: return da::launch_mla_wave8_fp8(p, s);
@@ -359,22 +362,35 @@ int run(const Common& c, da::DecodeParams p, const Plan& plan, bool bf16, int nu
       (long)P * c.batch * (p.num_kv_heads / 2) * plan.row_blocks >= device_cus())
     p.hb_shift = 1;
 
+  // A small fp32 split call (at most kValuMergeGroups row groups, at most 8
+  // partitions, whose rows the merging block requests all at once) merges inside
+  // its partition pass: the last block of each row group merges the group's rows
+  // with the merge pass's operations, so the call is one launch instead of two
+  // (such calls are bound by launch latency).  Its count words are the spare words
+  // of the queue section, which no fp32 call uses for a queue.
+  unsigned* merge_count = nullptr;
+  if (plan.variant == kValu && split && !partials_only && P <= 8 &&
+      (long)c.batch * p.num_kv_heads * plan.row_blocks <= kValuMergeGroups)
+    merge_count = (unsigned*)queue + 2;
   hipStream_t s = (hipStream_t)stream;
   if (log_enabled())
     std::fprintf(stderr,
                  "[decode_attention] variant=%s B=%d T=%d H=%d KVH=%d D=%d Dv=%d S=%d P=%d C=%d "
-                 "rows/block=%d row_blocks=%d grid=%d paged=%d reduce=%d queue=%d heads/block=%d\n",
+                 "rows/block=%d row_blocks=%d grid=%d paged=%d merge=%s queue=%d heads/block=%d\n",
                  variant_name(plan.variant), c.batch, c.q_len, c.num_q_heads, p.num_kv_heads,
                  p.depth, p.depth_v, c.max_seq_len, P, p.keys_per_partition,
                  plan.rows_per_block, plan.row_blocks,
                  P * c.batch * (p.num_kv_heads >> p.hb_shift) * plan.row_blocks, c.page_table != nullptr,
-                 (!partials_only && P > 1) ? 1 : 0, p.queue != nullptr, 1 << p.hb_shift);
-  if (clear_queue && p.queue) {
-    hipLaunchKernelGGL(clear_queue_section, dim3(1), dim3(kQueueBytes / 8), 0, s, p.queue);
+                 (partials_only || P == 1) ? "none" : (merge_count ? "in-pass" : "launch"),
+                 p.queue != nullptr, 1 << p.hb_shift);
+  if (clear_queue && (p.queue || merge_count)) {  // the whole section: queue word and counts
+    hipLaunchKernelGGL(clear_queue_section, dim3(1), dim3(kQueueBytes / 8), 0, s,
+                       (unsigned long long*)queue);
     if (hipGetLastError() != hipSuccess) return DA_ERR_HIP;
   }
-  if (launch_partition_pass(p, plan.variant, bf16, s) != hipSuccess) return DA_ERR_HIP;
-  if (!partials_only && P > 1) {
+  if (launch_partition_pass(p, plan.variant, bf16, merge_count, s) != hipSuccess)
+    return DA_ERR_HIP;
+  if (!partials_only && P > 1 && !merge_count) {
     const hipError_t e =
         p.part_bf16 ? da::launch_splitk_reduce_bf16_partials(
                           (const uint16_t*)po, pm, pl, P, (int)rows, c.num_q_heads, sink, out, lse,

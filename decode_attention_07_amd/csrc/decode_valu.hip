@@ -24,9 +24,131 @@
 //
 // Software pipelining: the K/V rows of the next tile are requested before the
 // current tile is processed, so every lane keeps 2*U key rows in flight.
-#include "da_device.h"
+#include "da_merge.h"
 
 namespace da {
+
+namespace {
+
+// ---- merge inside the pass (small split calls) ----------------------------------
+// The P partition blocks of a row group may run on different XCDs, whose L2 caches
+// are not coherent with each other within a launch: the partial values are stored
+// and read back with device-scope (agent) relaxed atomic accesses, which go past
+// each XCD's L2 state, and a count word tells the last block that every other
+// block's stores have completed.  No release fence (an agent-scope release writes
+// back the XCD's whole L2).
+typedef __attribute__((address_space(1))) float global_f32;
+typedef __attribute__((address_space(1))) unsigned global_u32;
+__device__ __forceinline__ void st_agent(float* a, float v) {
+  __hip_atomic_store((global_f32*)a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* a) {
+  return __hip_atomic_load((global_f32*)a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct ValuMergeArgs {
+  const float* po;     // part_o [P, rows_total, D]
+  const float* pm;     // part_m [P, rows_total]
+  const float* pl;     // part_l [P, rows_total]
+  const float* sink;   // [num_q_heads] or nullptr
+  float* out;          // [rows_total, D]
+  float* lse;          // [rows_total] or nullptr
+  size_t rows_total;
+  size_t row0q;        // q / out token row of the sequence's first token
+  int num_q_heads, group, g, rb, R, nrows, P;
+};
+
+// After a block has stored its partial rows: every thread waits for its stores to
+// complete, one thread counts the block in its row group's word (an add that wraps
+// to zero on the P-th, so the word is zero again after the call), and the block
+// whose add completes the count merges the group's rows, one wave per row.  The
+// merge is the merge pass's one-wave row merge (at most 32 partitions here), the
+// same operations in the same order ("mha_decoding_single_batch_pipelined",
+// description: the mha_splitk_reduce pass): M = max(max_p m_p, sigma), w_p = l_p
+// exp(m_p - M), out = sum_p w_p O_p / (sum_p w_p + exp(sigma - M)), lse = M + ln L.
+// (A function of its own: inlined, its values would join the register allocation
+// of the kernel's key loop.)  `flag`: one int of LDS.
+// One row group's rows, one wave per row, with NP >= P slots: every slot's partial
+// row is requested at once (a slot past P re-reads partition 0 and gets weight 0),
+// so a row costs one memory round trip.
+template <int D, int NP>
+__device__ __forceinline__ void valu_merge_rows(const ValuMergeArgs& a, int wave, int lane) {
+  constexpr int EPL = D / 64;
+  for (int r = wave; r < a.R; r += 4) {
+    const int rr = a.rb * a.R + r;
+    if (rr >= a.nrows) break;  // uniform in the wave; later rows are past the fold too
+    const int h = a.g * a.group + rr % a.group;
+    const size_t row = (a.row0q + (size_t)(rr / a.group)) * a.num_q_heads + h;
+    const int pc = lane < a.P ? lane : 0;
+    const float lp_raw = ld_agent(a.pl + (size_t)pc * a.rows_total + row);
+    const float mp_raw = ld_agent(a.pm + (size_t)pc * a.rows_total + row);
+    float c[NP][EPL];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const float* src =
+          a.po + ((size_t)(u < a.P ? u : 0) * a.rows_total + row) * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) c[u][e] = ld_agent(src + e);
+    }
+    const float sig = a.sink ? a.sink[h] * kLog2e : kNegInf;
+    const float lp = lane < a.P ? lp_raw : 0.f;
+    const float M = fmaxf(wave_max(lp > 0.f ? mp_raw * kLog2e : kNegInf), sig);
+    const float Ms = (M == kNegInf) ? 0.f : M;
+    const float w = lp > 0.f ? lp * fast_exp2(mp_raw * kLog2e - Ms) : 0.f;
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const float wj =
+          u < a.P ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u)) : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float t = fmaf(wj, c[u][e], acc[e]);
+        acc[e] = (wj != 0.f) ? t : acc[e];
+      }
+    }
+    float L = wave_sum(w);
+    if (a.sink) L += fast_exp2(sig - Ms);
+    const bool any = L > 0.f;
+    const float inv = any ? 1.f / L : 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a.out[row * D + lane * EPL + e] = acc[e] * inv;
+    if (a.lse && lane == 0) a.lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
+  }
+}
+
+// After a block has stored its partial rows: every thread waits for its stores to
+// complete, one thread counts the block in its row group's word (an add that wraps
+// to zero on the P-th, so the word is zero again after the call), and the block
+// whose add completes the count merges the group's rows.  The merge is the merge
+// pass's one-wave row merge (at most 8 partitions here), the same operations in
+// the same order ("mha_decoding_single_batch_pipelined", description: the
+// mha_splitk_reduce pass): M = max(max_p m_p, sigma), w_p = l_p exp(m_p - M), out =
+// sum_p w_p O_p / (sum_p w_p + exp(sigma - M)), lse = M + ln L.  (A function of its
+// own: inlined, its values would join the register allocation of the kernel's key
+// loop.)  `flag`: one int of LDS.
+template <int D>
+__device__ __attribute__((noinline)) void valu_count_and_merge(const ValuMergeArgs a,
+                                                               unsigned* cnt, int* flag,
+                                                               int wave, int lane) {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t top = (uint32_t)a.P - 1u;
+    *flag = __builtin_amdgcn_atomic_inc32((global_u32*)cnt, top, __ATOMIC_RELAXED, "agent") == top
+                ? 1
+                : 0;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  if (a.P <= 4)
+    valu_merge_rows<D, 4>(a, wave, lane);
+  else
+    valu_merge_rows<D, 8>(a, wave, lane);
+}
+
+}  // namespace
 
 template <bool BF16, int D, int R, int U>
 struct ValuCfg {
@@ -182,8 +304,10 @@ __device__ __forceinline__ void valu_process(const ValuTile<BF16, D, R, U>& t,
   }
 }
 
+// merge_count: nullptr, or the count words of a split merged inside the pass (one
+// per (sequence, KV head, row block), zero between calls).
 template <bool BF16, int D, int R, int U>
-__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p, unsigned* merge_count) {
   using C = ValuCfg<BF16, D, R, U>;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id_uniform();
@@ -330,10 +454,19 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
     if (p.write_partials) {
       const size_t prow = (size_t)pidx * (size_t)p.rows_total + row;
       const bool any = Lsum > 0.f;
-      p.part_o[prow * D + d] = any ? O / Lsum : 0.f;
-      if (d == 0) {
-        p.part_m[prow] = any ? M * kLn2 : kNegInf;
-        p.part_l[prow] = Lsum;
+      const float pm = any ? M * kLn2 : kNegInf;
+      if (merge_count) {  // read back by another block of this launch
+        st_agent(p.part_o + prow * D + d, any ? O / Lsum : 0.f);
+        if (d == 0) {
+          st_agent(p.part_m + prow, pm);
+          st_agent(p.part_l + prow, Lsum);
+        }
+      } else {
+        p.part_o[prow * D + d] = any ? O / Lsum : 0.f;
+        if (d == 0) {
+          p.part_m[prow] = pm;
+          p.part_l[prow] = Lsum;
+        }
       }
     } else {
       if (p.sink) {
@@ -353,6 +486,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p) {
       if (d == 0 && p.lse) p.lse[row] = any ? (M + fast_log2(Lsum)) * kLn2 : kNegInf;
     }
   }
+  if (merge_count) {
+    __shared__ int sm_flag;
+    valu_count_and_merge<D>(
+        ValuMergeArgs{p.part_o, p.part_m, p.part_l, p.sink, (float*)p.out, p.lse,
+                      (size_t)p.rows_total, row0q, p.num_q_heads, p.group, g, rb, R, nrows,
+                      p.num_partitions},
+        merge_count + ((size_t)b * p.num_kv_heads + g) * p.row_blocks + rb, &sm_flag, wave,
+        lane);
+  }
 }
 
 // Rows per block the kernel is built for (rows are padded up to these).
@@ -364,19 +506,20 @@ static int valu_rows_bucket(int fold) {
 }
 
 template <bool BF16, int D, int R>
-static hipError_t launch_valu_r(const DecodeParams& p, int grid, hipStream_t s) {
+static hipError_t launch_valu_r(const DecodeParams& p, unsigned* mc, int grid, hipStream_t s) {
   constexpr int U = (R <= 4) ? 2 : 1;
-  hipLaunchKernelGGL((decode_valu_kernel<BF16, D, R, U>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((decode_valu_kernel<BF16, D, R, U>), dim3(grid), dim3(256), 0, s, p, mc);
   return hipGetLastError();
 }
 
 template <bool BF16, int D>
-static hipError_t launch_valu_d(const DecodeParams& p, int R, int grid, hipStream_t s) {
+static hipError_t launch_valu_d(const DecodeParams& p, unsigned* mc, int R, int grid,
+                                hipStream_t s) {
   switch (R) {
-    case 1: return launch_valu_r<BF16, D, 1>(p, grid, s);
-    case 2: return launch_valu_r<BF16, D, 2>(p, grid, s);
-    case 4: return launch_valu_r<BF16, D, 4>(p, grid, s);
-    default: return launch_valu_r<BF16, D, 8>(p, grid, s);
+    case 1: return launch_valu_r<BF16, D, 1>(p, mc, grid, s);
+    case 2: return launch_valu_r<BF16, D, 2>(p, mc, grid, s);
+    case 4: return launch_valu_r<BF16, D, 4>(p, mc, grid, s);
+    default: return launch_valu_r<BF16, D, 8>(p, mc, grid, s);
   }
 }
 
@@ -385,12 +528,13 @@ static hipError_t launch_valu_d(const DecodeParams& p, int R, int grid, hipStrea
 int valu_step_keys(int rows_per_block) { return 32 * ((rows_per_block <= 4) ? 2 : 1); }
 int valu_rows_per_block(int fold) { return valu_rows_bucket(fold); }
 
-// fp32 inputs (bf16 runs the streaming matrix-core kernel).
-hipError_t launch_decode_valu(const DecodeParams& p, hipStream_t s) {
+// fp32 inputs (bf16 runs the streaming matrix-core kernel).  merge_count: see the
+// kernel (the caller guarantees P <= 8 and one word per row group).
+hipError_t launch_decode_valu(const DecodeParams& p, unsigned* merge_count, hipStream_t s) {
   const int R = valu_rows_bucket(fold_rows(p));
   const int grid = p.num_partitions * p.batch * p.num_kv_heads * p.row_blocks;
-  if (p.depth == 64) return launch_valu_d<false, 64>(p, R, grid, s);
-  return launch_valu_d<false, 128>(p, R, grid, s);
+  if (p.depth == 64) return launch_valu_d<false, 64>(p, merge_count, R, grid, s);
+  return launch_valu_d<false, 128>(p, merge_count, R, grid, s);
 }
 
 }  // namespace da

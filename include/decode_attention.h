@@ -109,7 +109,8 @@ int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_head
  * decode_attention() / mla_decode() call that runs with one partition does not
  * touch the workspace (it may be NULL); the *_partials() passes always write it.
  * Workspace layout (each section 256-byte aligned):
- *   queue    uint64, 256 bytes        work queue of ragged calls (below), at offset 0
+ *   queue    256 bytes                at offset 0: the uint64 work-queue word of ragged
+ *                                     calls, then 62 uint32 merge counts (below)
  *   part_o   fp32 [P, rows, depth_v]  partial outputs, each normalised by its exp-sum
  *   part_max fp32 [P, rows]           partial max, natural-log units (-inf if empty)
  *   part_sum fp32 [P, rows]           partial exp-sum relative to part_max (0 if empty)
@@ -129,6 +130,15 @@ int decode_num_partitions(int batch, int q_len, int num_q_heads, int num_kv_head
  * zero again.  Its place does not depend on the partition count, so one
  * workspace sized for the largest P serves calls with any P.  Calls that share a
  * workspace must not run concurrently.
+ *
+ * Merge counts.  An fp32 decode_attention() / decode_attention_ragged() call with
+ * 2..8 partitions and at most 62 row groups (batch x KV heads x blocks of up to 8
+ * folded query rows) merges its partitions inside the partition pass: each row
+ * group counts its finished partitions in a word of the queue section, and the
+ * block that completes the count merges the group's rows, so the call is one
+ * launch (the same results as the merge pass, bit for bit).  Like the queue
+ * word, the counts must be zero when such a call starts (the same one-time zero
+ * fill covers them) and every completed call leaves them zero.
  */
 size_t decode_workspace_size(int num_partitions, int batch, int q_len, int num_q_heads,
                              int depth_v);
@@ -186,7 +196,8 @@ int decode_attention(const void* q, const void* k, const void* v, const uint32_t
  *   - Every call on a device shares that device's array, which keeps the last
  *     call's contents: calls that overlap on one device (other streams, other
  *     threads) race on it and must be serialised by the caller.  The work-queue
- *     word is cleared by a small kernel at the start of each call that uses it.
+ *     word and the merge counts are cleared by a small kernel at the start of
+ *     each call that uses them.
  */
 #define DA_NO_ALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 int decode_attention_no_alloc(const void* q, const void* k, const void* v,

@@ -52,6 +52,18 @@ def test_no_alloc_two_calls_in_a_row():
     _check(big.with_(name="no_alloc_big2", seed=9953, batch=5), 0, "ragged paged again")
 
 
+def test_no_alloc_fp32_splits_merged_in_the_pass():
+    """Small fp32 split calls merge inside their partition pass with count words in
+    the scratch's queue section: two in a row (the second smaller) both equal
+    decode_attention() bit for bit and the oracle within the bounds."""
+    a = W.Workload("no_alloc_f32_a", 9954, batch=2, num_heads=16, kv_heads=4, depth=128,
+                   max_seq_len=1500, ragged=(1, 1500, 1), sink=True, dtype="f32")
+    _check(a, 6, "fp32, merged in the pass")
+    b = W.Workload("no_alloc_f32_b", 9955, batch=1, num_heads=8, kv_heads=8, depth=64,
+                   max_seq_len=256, dtype="f32")
+    _check(b, 4, "smaller fp32, merged in the pass")
+
+
 def test_no_alloc_refuses_an_oversized_workspace():
     """A call whose workspace exceeds the scratch is refused before any launch; the
     next call still works."""

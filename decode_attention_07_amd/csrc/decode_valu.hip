@@ -323,6 +323,12 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeParams p, unsign
   const int pidx = id;
 
   const int nrows = seq_tokens(p, b) * p.group;  // this sequence's fold
+  // Ragged q: a block none of whose rows exists (a sequence without tokens, or a
+  // row block past a short sequence's rows) has nothing to do.  It must leave here:
+  // below, its key range would start from an empty minimum over its rows.  The
+  // whole block returns before any barrier; a merge inside the pass counts no
+  // such block, since every partition of the row group leaves alike.
+  if (rb * R >= nrows) return;
   const size_t row0q = seq_row0(p, b);
   const int k_lo = pidx * p.keys_per_partition;
   int hi[R];

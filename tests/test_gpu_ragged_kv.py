@@ -36,6 +36,12 @@ def test_ragged_kv_layout(name, kw, P):
     wl = W.Workload(f"ragged_kv_{name}", 9800 + len(name), **kw)
     if wl.mla:
         wl = wl.with_(scale=1.0 / np.sqrt(192.0))
+    run_ragged_kv(wl, P, name)
+
+
+def run_ragged_kv(wl, P, name):
+    """One problem in the ragged KV layout against the oracle, and bit for bit
+    against the same call on the dense layout."""
     say(f"[gpu] ragged KV layout {name}: B={wl.batch} T={wl.q_len} H={wl.num_heads} "
         f"KVH={wl.kv_heads} D={wl.depth} S={wl.max_seq_len} P={P}")
     inp = W.make_inputs(wl)

@@ -64,6 +64,11 @@ CASES = [
                                  q_len=3), [1, 3, 2]),
     ("f32_mha", dict(batch=3, num_heads=4, kv_heads=4, depth=64, max_seq_len=77, q_len=3,
                      dtype="f32", causal=True, ragged=(3, 77, 0)), [2, 1, 3]),
+    # fp32 blocks without a row: a sequence without tokens, and second row blocks
+    # (rows 8 .. 11 of the 12-row fold) past short sequences' rows
+    ("f32_empty_blocks", dict(batch=4, num_heads=16, kv_heads=4, depth=128, max_seq_len=600,
+                              q_len=3, dtype="f32", causal=True, ragged=(1, 600, 1),
+                              sink=True), [3, 0, 1, 2]),
     ("mla_paged", dict(batch=4, num_heads=128, kv_heads=1, depth=576, depth_v=512,
                        max_seq_len=260, q_len=3, mla=True, causal=True, page_size=32,
                        ragged=(3, 260, 0), scale=1.0 / np.sqrt(192.0), sink=True),

@@ -10,6 +10,8 @@ import pytest
 
 import workloads as W
 from gpu_util import check
+from test_gpu_ragged_kv import run_ragged_kv
+from test_gpu_ragged_q import _run as run_ragged_q
 
 pytestmark = pytest.mark.gpu
 
@@ -93,3 +95,29 @@ def test_random_mla_shapes(i):
 def test_random_sparse_shapes(i):
     wl, P = _sparse_case(i)
     check(wl, num_partitions=P, what=_describe(wl, P))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_ragged_kv(i):
+    """The dense draws (bf16 and fp32 GQA, bf16 MLA) in the ragged KV layout."""
+    if i % 4 == 3:
+        wl, P = _mla_case(2 * i)  # an even draw: the bf16 cache
+        wl = wl.with_(page_size=0)
+    else:
+        wl, P = _gqa_case(300 + 3 * i + (i % 2))  # bf16 and fp32 draws (index mod 3)
+        wl = wl.with_(page_size=0)
+    run_ragged_kv(wl, P, _describe(wl, P))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_ragged_q(i):
+    """Multi-token draws with per-sequence token counts (0 .. T) from offsets."""
+    rng = np.random.default_rng(50_000 + i)
+    if i % 4 == 3:
+        wl, P = _mla_case(2 * i)
+        wl = wl.with_(q_len=2, causal=True)
+    else:
+        wl, P = _gqa_case(600 + 3 * i + (i % 2))  # bf16 and fp32 draws (index mod 3)
+        wl = wl.with_(q_len=int(rng.integers(2, 5)), causal=bool(rng.random() < 0.7))
+    tokens = [int(t) for t in rng.integers(0, wl.q_len + 1, size=wl.batch)]
+    run_ragged_q(wl, tokens, P, _describe(wl, P) + f" tokens={tokens}")

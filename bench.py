@@ -333,9 +333,9 @@ def main():
 
     # A step is the call a user makes (one C call: the partition pass and, when split,
     # the merge).  The dominant kernel is timed on its own through the partials-only
-    # entry point; for the dense MLA kernel that call writes fp32 partial rows where
-    # the full call writes bf16 ones over long partitions, so its time is, if
-    # anything, the longer.
+    # entry point; for the MLA kernels that call writes fp32 partial rows where the
+    # full call writes bf16 ones for partitions 1 .. P-1 over long partitions, so its
+    # time is, if anything, the longer.
     steps = [full_call(d) for d in dev_sets]
     kernels = [partition_call(d) if split else steps[j] for j, d in enumerate(dev_sets)]
 

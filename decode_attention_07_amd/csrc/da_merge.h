@@ -109,7 +109,9 @@ __device__ __forceinline__ void merge_accumulate(float (&acc)[EPL], const float 
 // mixed fp32 / bf16 layout with PO = uint16_t: merge_part_cols), part_m / part_l
 // [P, rows]; writes out[row, :] (bf16 or fp32) and lse[row] (if lse).  Called by
 // all 64 lanes of one wave; sink (or nullptr) is indexed by row % num_heads.
-template <int DV, bool BF16OUT, typename PO = float>
+// SLOTS > 0: partial rows requested per group (at least 2 for mixed partials);
+// 0: 64 values per lane, at most 32 rows.
+template <int DV, bool BF16OUT, typename PO = float, int SLOTS = 0>
 __device__ __forceinline__ void merge_row(const PO* __restrict__ part_o,
                                           const float* __restrict__ part_m,
                                           const float* __restrict__ part_l, int P, int rows,
@@ -119,7 +121,8 @@ __device__ __forceinline__ void merge_row(const PO* __restrict__ part_o,
   constexpr int EPL = DV / 64;  // consecutive columns per lane
   // Partial rows requested ahead: 64 values per lane in flight (8 rows at
   // DV = 512, 32 at DV <= 128, where a long split of few rows is latency bound).
-  constexpr int kInFlight = (64 / EPL) < 32 ? (64 / EPL) : 32;
+  constexpr int kInFlight = SLOTS > 0 ? SLOTS : ((64 / EPL) < 32 ? (64 / EPL) : 32);
+  static_assert(sizeof(PO) == 4 || kInFlight >= 2, "mixed partials: slot 1 is the spare");
   // A slot past the partitions re-reads one already requested: partition 0, or for
   // mixed partials the first bf16 one (P >= 2 there), so that slot u >= 1 is bf16.
   constexpr int kSpare = sizeof(PO) == 2 ? 1 : 0;

@@ -21,7 +21,7 @@ constexpr int kMaxP = 1024;
 // seq_chunks > 0: the rows come in sequences of seq_chunks blocks' worth, and the
 // blocks of sequence b run on XCD b mod 8 (blocks i and i + 8 share an XCD), the
 // one whose L2 took that sequence's partial rows from its partition pass.
-template <int DV, bool BF16OUT, typename PO>
+template <int DV, bool BF16OUT, typename PO, int SLOTS = 0>
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(
     const PO* __restrict__ part_o, const float* __restrict__ part_m,
     const float* __restrict__ part_l, int P, int rows, int num_heads,
@@ -34,8 +34,8 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(
   }
   const int row = chunk * kWaves + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole wave; nothing below synchronises the block
-  merge_row<DV, BF16OUT, PO>(part_o, part_m, part_l, P, rows, row, sink, num_heads, out, lse,
-                             threadIdx.x & 63);
+  merge_row<DV, BF16OUT, PO, SLOTS>(part_o, part_m, part_l, P, rows, row, sink, num_heads, out,
+                                    lse, threadIdx.x & 63);
 }
 
 // Rows split into 33..64 partitions at DV <= 128 (a long sequence over few
@@ -141,8 +141,18 @@ hipError_t launch_splitk_reduce_bf16_partials(const uint16_t* po, const float* p
   const int grid = (rows + kWaves - 1) / kWaves;
   const bool xcd = batch > 0 && batch % 8 == 0 && seq_rows > 0 && seq_rows % kWaves == 0 &&
                    (long)batch * seq_rows == rows;
-  hipLaunchKernelGGL((splitk_reduce_kernel<512, true, uint16_t>), dim3(grid), dim3(kThreads), 0,
-                     s, po, pm, pl, P, rows, H, sink, out, lse, xcd ? seq_rows / kWaves : 0);
+  // Partial rows requested per group: as many as the partitions (2, 4 or 8), so
+  // that a short split does not re-read a row for every empty slot.
+  const int sc = xcd ? seq_rows / kWaves : 0;
+  if (P <= 2)
+    hipLaunchKernelGGL((splitk_reduce_kernel<512, true, uint16_t, 2>), dim3(grid),
+                       dim3(kThreads), 0, s, po, pm, pl, P, rows, H, sink, out, lse, sc);
+  else if (P <= 4)
+    hipLaunchKernelGGL((splitk_reduce_kernel<512, true, uint16_t, 4>), dim3(grid),
+                       dim3(kThreads), 0, s, po, pm, pl, P, rows, H, sink, out, lse, sc);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<512, true, uint16_t, 8>), dim3(grid),
+                       dim3(kThreads), 0, s, po, pm, pl, P, rows, H, sink, out, lse, sc);
   return hipGetLastError();
 }
 

@@ -95,6 +95,19 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_pair_kernel(
   if (lse && lane == 0) lse[row] = any ? (M + fast_log2(L)) * kLn2 : kNegInf;
 }
 
+template <int DV, int SLOTS>
+hipError_t launch_reduce_slots(const float* po, const float* pm, const float* pl, int P,
+                               int rows, int H, const float* sink, void* out, bool bf16,
+                               float* lse, int grid, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL((splitk_reduce_kernel<DV, true, float, SLOTS>), dim3(grid),
+                       dim3(kThreads), 0, s, po, pm, pl, P, rows, H, sink, out, lse, 0);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<DV, false, float, SLOTS>), dim3(grid),
+                       dim3(kThreads), 0, s, po, pm, pl, P, rows, H, sink, out, lse, 0);
+  return hipGetLastError();
+}
+
 template <int DV>
 hipError_t launch_reduce_dv(const float* po, const float* pm, const float* pl, int P, int rows,
                             int H, const float* sink, void* out, bool bf16, float* lse,
@@ -112,13 +125,19 @@ hipError_t launch_reduce_dv(const float* po, const float* pm, const float* pl, i
     }
   }
   const int grid = (rows + kWaves - 1) / kWaves;
-  if (bf16)
-    hipLaunchKernelGGL((splitk_reduce_kernel<DV, true, float>), dim3(grid), dim3(kThreads), 0, s,
-                       po, pm, pl, P, rows, H, sink, out, lse);
-  else
-    hipLaunchKernelGGL((splitk_reduce_kernel<DV, false, float>), dim3(grid), dim3(kThreads), 0,
-                       s, po, pm, pl, P, rows, H, sink, out, lse);
-  return hipGetLastError();
+  if constexpr (DV <= 128) {
+    // Partial rows requested per group: as many as the partitions need (4, 8 or 16),
+    // not 32 whatever P, so that a split into a few partitions does not re-read a
+    // row for every empty slot.  The same operations in the same order.
+    if (P <= 16) {
+      if (P <= 4) return launch_reduce_slots<DV, 4>(po, pm, pl, P, rows, H, sink, out, bf16, lse,
+                                                    grid, s);
+      if (P <= 8) return launch_reduce_slots<DV, 8>(po, pm, pl, P, rows, H, sink, out, bf16, lse,
+                                                    grid, s);
+      return launch_reduce_slots<DV, 16>(po, pm, pl, P, rows, H, sink, out, bf16, lse, grid, s);
+    }
+  }
+  return launch_reduce_slots<DV, 0>(po, pm, pl, P, rows, H, sink, out, bf16, lse, grid, s);
 }
 
 }  // namespace

@@ -676,24 +676,36 @@ __global__ __launch_bounds__(kThreads) void mla_wave8_kernel(DecodeParams p, int
   // This wave's 128 columns of its group's rows: lane holds O^T[d = 128 wq + 32 ct +
   // 8 q + 4 hg + 0..3][row 64 grp + 32 rt + l31] in acc[ct][rt][4 q + 0..3].
   // fp32 partial rows: every partition's of an fp32-partial split, and partition
-  // 0's of a bf16-partial one (layout in da_params.h)
+  // 0's of a bf16-partial one (layout in da_params.h).  They go through LDS like
+  // the bf16 rows below, 32 rows at a time (32 x 528 bytes per wave of the idle
+  // tile ring), so that each store writes the wave's 512 bytes of two rows instead
+  // of 16 bytes of 32 rows.  A wave reads back only what it wrote; its LDS
+  // operations stay in order, so the second half's writes follow the first half's
+  // reads.
   if (p.write_partials && (!p.part_bf16 || pidx == 0)) {
+    constexpr int kStgRowF = kCols * 4 + 16;  // 528
+    static_assert(kWaves * 32 * kStgRowF <= kStages * kTileBytes, "staging fits the ring");
+    char* stgf = smem + wave * (32 * kStgRowF);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      const int row = grp * kGroupRows + 32 * rt + l31;
-      const int r2 = mb * kRows + row;
-      if (r2 >= nrows) continue;
-      const float inv = rinv[row];
-      const size_t prow =
-          (size_t)pidx * (size_t)p.rows_total + (row0q + r2 / H) * H + r2 % H;
-      float* dst = p.part_o + prow * kDv + kCols * wq + 4 * hg;
+      const float inv = rinv[grp * kGroupRows + 32 * rt + l31];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *(float4*)(dst + 32 * ct + 8 * q) =
+          *(float4*)(stgf + l31 * kStgRowF + 4 * (32 * ct + 8 * q + 4 * hg)) =
               make_float4(acc[ct][rt][4 * q + 0] * inv, acc[ct][rt][4 * q + 1] * inv,
                           acc[ct][rt][4 * q + 2] * inv, acc[ct][rt][4 * q + 3] * inv);
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {
+        const int rl = 2 * i + (lane >> 5);  // row within the half
+        const int r2 = mb * kRows + grp * kGroupRows + 32 * rt + rl;
+        if (r2 >= nrows) continue;
+        const size_t prow =
+            (size_t)pidx * (size_t)p.rows_total + (row0q + r2 / H) * H + r2 % H;
+        *(float4*)(p.part_o + prow * kDv + kCols * wq + 4 * (lane & 31)) =
+            *(const float4*)(stgf + rl * kStgRowF + 16 * (lane & 31));
+      }
     }
     return;
   }
